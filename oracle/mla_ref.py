@@ -1,0 +1,199 @@
+"""Plain float64 MLA reference (TEST INFRASTRUCTURE ONLY).
+
+What it follows (pages on Multi-head Latent Attention):
+
+* [MLA explainer] disassemble-channel.com, "Multi-head Latent Attention（MLA）
+  とは？KVキャッシュを圧縮するDeepSeekの注意機構を完全解説":
+  low-rank section eqs.(2)-(3); matrix-absorption section eq.(8);
+  value-side absorption eqs.(9)-(10); "RoPE breaks absorption" section
+  (its rope() helper fixes the half-split pairing); decoupled-RoPE section
+  eqs.(14)-(16) and the 1/sqrt(d_h+d_R) softmax scale; trade-offs section
+  (RMSNorm on the cached latent; absorbed form = MQA with head dim 576).
+* [V2 summary] abeam.tech, DeepSeek-V2 / MLA KV-cache article: the
+  four-step inference flow.
+* [attention variants] youngju.dev: the extra RMSNorm after the compressed
+  latent (DeepSeek-V3).
+
+Conventions (row-major, one token per row):
+
+* W_dkv_kr [d_c + d_R, d_model]: rows 0..d_c-1 are W^DKV, the rest W^KR.
+  kv = h @ W_dkv_kr.T gives [W^DKV h ; W^KR h].
+* W_UK [n_h, d_h, d_c] stacks W^UK_i (d_h x d_c): k^C_{j,i} = W^UK_i c_j.
+* W_UV [n_h, d_v, d_c] stacks W^UV_i (d_v x d_c): v^C_{j,i} = W^UV_i c_j.
+* RoPE: half-split pairs (x_k, x_{k+d/2}), angle pos / base^(2k/d).
+* Query t of a request with T cached rows (the rows appended this step
+  included) sits at position T - q_len + t and sees keys 0..its position.
+
+Nothing is blocked, fused or reordered beyond the definitions; loops are
+per request and per head so a reader can check each line against the pages.
+"""
+
+import numpy as np
+
+
+# ------------------------------------------------------------------ pieces
+def rope_half(x, pos, base=10000.0):
+    """Rotary embedding with half-split pairing.
+
+    x: [..., d] (d even); pos: positions broadcastable to x.shape[:-1].
+    Pair k (k < d/2) is (x_k, x_{k+d/2}) rotated by theta_k = pos/base^(2k/d).
+    [MLA explainer, "RoPE breaks absorption" section: the rope() helper;
+    decoupled-RoPE section eq.(15)]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    inv = base ** (-(2.0 * np.arange(half)) / d)
+    theta = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(theta), np.sin(theta)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+def rmsnorm(x, gamma, eps):
+    """x / sqrt(mean(x^2) + eps) * gamma over the last axis.
+    [MLA explainer, trade-offs section (normalisation of the latent)];
+    [attention variants, trade-off section (RMSNorm after the latent)]."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * gamma
+
+
+def softmax_stats(s):
+    """Max-subtracted softmax over the last axis, with its log-sum-exp.
+    Entries equal to -inf are masked.  Rows with no visible entry get
+    weights 0 and lse = -inf (the empty sum)."""
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1, keepdims=True)
+    empty = ~np.isfinite(m)
+    m = np.where(empty, 0.0, m)
+    p = np.exp(s - m)
+    l = np.sum(p, axis=-1, keepdims=True)
+    a = np.where(empty, 0.0, p / np.where(empty, 1.0, l))
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m + np.log(np.where(empty, 1.0, l)))
+    return a, lse[..., 0]
+
+
+def query_positions(T, q_len):
+    """Positions of the q_len queries of a request with T cached rows."""
+    return np.arange(q_len) + (T - q_len)
+
+
+def causal_mask(q_pos, T):
+    """Boolean [q_len, T]: query at position p sees keys 0..p."""
+    return np.arange(T)[None, :] <= np.asarray(q_pos)[:, None]
+
+
+# ------------------------------------------------------------ append step
+def latent_rows(h, w_dkv_kr, gamma, pos, d_c, eps, base=10000.0):
+    """New cache rows from hidden states.
+
+    c = RMSNorm_gamma(W^DKV h)          [MLA explainer, low-rank eq.(2); norm]
+    k^R = RoPE(W^KR h, pos)             [MLA explainer, decoupled eq.(15)]
+    Returns (c [N, d_c], k^R [N, d_R])."""
+    kv = np.asarray(h, np.float64) @ np.asarray(w_dkv_kr, np.float64).T
+    c = rmsnorm(kv[:, :d_c], np.asarray(gamma, np.float64), eps)
+    kr = rope_half(kv[:, d_c:], pos, base)
+    return c, kr
+
+
+def append_from_projection(kv, gamma, pos, d_c, eps, base=10000.0):
+    """Same as latent_rows when the down-projection output kv [N, d_c+d_R]
+    is given instead of h."""
+    kv = np.asarray(kv, np.float64)
+    c = rmsnorm(kv[:, :d_c], np.asarray(gamma, np.float64), eps)
+    kr = rope_half(kv[:, d_c:], pos, base)
+    return c, kr
+
+
+# ---------------------------------------------- non-absorbed attention
+def attention_nonabsorbed(q_nope, q_pe, q_pos, C, KR, w_uk, w_uv, scale,
+                          base=10000.0, heads=None):
+    """Standard MLA attention for one request, keys and values expanded.
+
+    q_nope [Q, n_h, d_h]; q_pe [Q, n_h, d_R] (before RoPE); q_pos [Q];
+    C [T, d_c] latent rows; KR [T, d_R] RoPE'd shared keys.
+    For each head i:
+      k_{j,i} = [W^UK_i c_j ; k^R_j]     [MLA explainer eq.(3), eq.(14)]
+      v_{j,i} = W^UV_i c_j               [MLA explainer eq.(3)]
+      q_{t,i} = [q^C ; RoPE(q^R, pos_t)] [MLA explainer eq.(14)-(15)]
+      s = q.k * scale, causal            [eq.(16); scale 1/sqrt(d_h+d_R)]
+      o = softmax(s) @ v                 [MLA explainer eq.(9)]
+    Returns o [Q, len(heads), d_v]."""
+    q_nope = np.asarray(q_nope, np.float64)
+    q_pe = np.asarray(q_pe, np.float64)
+    C = np.asarray(C, np.float64)
+    KR = np.asarray(KR, np.float64)
+    n_h = q_nope.shape[1]
+    heads = range(n_h) if heads is None else heads
+    mask = causal_mask(q_pos, C.shape[0])
+    out = []
+    for i in heads:
+        k_c = C @ np.asarray(w_uk[i], np.float64).T          # [T, d_h]
+        v = C @ np.asarray(w_uv[i], np.float64).T            # [T, d_v]
+        k = np.concatenate([k_c, KR], axis=-1)               # [T, d_h+d_R]
+        q = np.concatenate([q_nope[:, i], rope_half(q_pe[:, i], q_pos, base)], axis=-1)
+        s = (q @ k.T) * scale
+        s = np.where(mask, s, -np.inf)
+        a, _ = softmax_stats(s)
+        out.append(a @ v)
+    return np.stack(out, axis=1)
+
+
+# --------------------------------------------------- absorbed pieces
+def absorb_q(q_nope, q_pe, q_pos, w_uk, base=10000.0):
+    """Latent query per head: q~ = W^UK_i^T q^C, then the RoPE'd q^R appended.
+    [MLA explainer, matrix absorption eq.(8); decoupled eq.(15)-(16)].
+    q_nope [N, n_h, d_h], q_pe [N, n_h, d_R], q_pos [N] -> [N, n_h, d_c+d_R]."""
+    q_nope = np.asarray(q_nope, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    n_h = q_nope.shape[1]
+    lat = np.stack([q_nope[:, i] @ w_uk[i] for i in range(n_h)], axis=1)
+    rot = rope_half(q_pe, np.asarray(q_pos)[:, None], base)
+    return np.concatenate([lat, rot], axis=-1)
+
+
+def decode_absorbed(q_lat, q_pos, C, KR, scale):
+    """Attention over the latent cache with the absorbed query.
+
+    q_lat [Q, n_h, d_c+d_R]; rows [C | KR] shared by every head (MQA with
+    head dim d_c+d_R whose value is the latent part).
+    s = q_lat . [c ; k^R] * scale (causal); o_lat = softmax(s) @ C.
+    [MLA explainer eq.(8), eq.(10), eq.(16); trade-offs section (MQA view)].
+    Returns (o_lat [Q, n_h, d_c], lse [Q, n_h]) with lse natural-log."""
+    q_lat = np.asarray(q_lat, np.float64)
+    C = np.asarray(C, np.float64)
+    rows = np.concatenate([C, np.asarray(KR, np.float64)], axis=-1)
+    mask = causal_mask(q_pos, C.shape[0])                     # [Q, T]
+    s = np.einsum("qhd,td->qht", q_lat, rows) * scale
+    s = np.where(mask[:, None, :], s, -np.inf)
+    a, lse = softmax_stats(s)
+    return np.einsum("qht,tc->qhc", a, C), lse
+
+
+def out_proj(o_lat, w_uv):
+    """Per-head output o = W^UV_i o_lat.  [MLA explainer eq.(10)].
+    o_lat [N, n_h, d_c], W_UV [n_h, d_v, d_c] -> [N, n_h, d_v]."""
+    o_lat = np.asarray(o_lat, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    return np.stack([o_lat[:, i] @ w_uv[i].T for i in range(o_lat.shape[1])], axis=1)
+
+
+def combine_partials(o_parts, lse_parts):
+    """Merge attention results over disjoint key sets (exact identity of
+    softmax): L = log sum_s exp(lse_s); o = sum_s exp(lse_s - L) o_s.
+    Used only to check split-context invariance."""
+    lse_parts = np.asarray(lse_parts, np.float64)
+    m = np.max(lse_parts, axis=0)
+    w = np.exp(lse_parts - m)
+    L = m + np.log(np.sum(w, axis=0))
+    o = np.sum(np.exp(lse_parts - L)[..., None] * np.asarray(o_parts, np.float64), axis=0)
+    return o, L
+
+
+# ------------------------------------------- paged cache (host indexing)
+def gather_rows(pool, block_table_row, T, block_size):
+    """Rows 0..T-1 of one request from a paged pool [blocks, block_size, D]
+    through its block table (plain indexing; no arithmetic on values)."""
+    idx = np.arange(T)
+    blocks = np.asarray(block_table_row)[idx // block_size]
+    return pool[blocks, idx % block_size]
