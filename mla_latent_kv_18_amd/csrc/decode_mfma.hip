@@ -1,0 +1,406 @@
+// Latent-cache decode for MI355X (gfx950): absorbed MLA attention as an
+// MQA with one shared 576-wide key row per token whose first 512 elements
+// are also the value ([MLA explainer, trade-offs section]).
+//
+// Work decomposition
+//   workgroup = (request b, context chunk, row group); rows of a request are
+//   (query t, head h) pairs, r = t * n_h + h.  Each 64-lane wave owns 32
+//   consecutive rows (one query position, 32 heads) for the whole chunk.
+//   A workgroup of WAVES waves owns 32*WAVES rows and streams its chunk of
+//   cache rows through LDS once; every wave reuses each staged tile.
+//
+// Per 32-token tile, per wave (bf16 MFMA 32x32x16, fp32 accumulate):
+//   S^T[t, h]  = sum_d K[t, d] Q[h, d]      A = K tile from LDS (ds_read_b128),
+//                                           B = Q^T, register resident (144 VGPR)
+//   online softmax over t (per lane: one head, 16 tokens; the other 16 tokens
+//   of that head sit in lane ^ 32)
+//   O^T[c, h] += sum_t V^T[c, t] P^T[t, h]  A = V^T read with ds_read_b64_tr_b16
+//                                           from the same LDS tile, B = P^T taken
+//                                           straight from the S^T registers
+// The token order inside each 16-token MFMA k-step is permuted identically on
+// both operands so P never leaves registers.
+//
+// LDS tile: 32 rows x 72 sixteen-byte chunks, chunk c of row t stored at
+// t*72 + (c ^ f(t)), f(t) = u ^ ((u & 1) << 2), u = (t >> 1) & 7; this keeps
+// both the 16-lane b128 key reads and the 32-lane transposed value reads free
+// of bank conflicts.  Tiles arrive by direct global->LDS 16-byte loads
+// (global_load_lds_dwordx4), NBUF tiles in flight.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int kDc = 512;
+constexpr int kD = 576;
+constexpr int kTileT = 32;
+constexpr int kChunks = kD * 2 / 16;                 // 72
+constexpr int kTileBytes = kTileT * kD * 2;          // 36864
+constexpr int kLoadsPerTile = kTileBytes / (64 * 16);  // 36 wave-wide 16-byte loads
+
+struct DecodeParams {
+  const __bf16* q_lat;
+  const __bf16* cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* o_part;
+  float* lse_part;
+  __bf16* o_lat;
+  float* lse;
+  int max_blocks, num_blocks, block_size, q_len, n_h, max_seq_len;
+  int split_tokens, num_splits, row_groups;
+  float scale_log2;
+};
+
+__device__ __forceinline__ int swz(int t) {
+  const int u = (t >> 1) & 7;
+  return u ^ ((u & 1) << 2);
+}
+
+// s_waitcnt with vmcnt <= n (lgkmcnt / expcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One wave-wide 16-byte-per-lane global->LDS copy: lane i's 16 bytes land at
+// lds_base + 16*i.  Issued from inline asm so that the compiler's wait-count
+// pass does not stall every later LDS read on it (it cannot tell which
+// buffer the copy targets); the kernel orders it with explicit vmcnt waits.
+// M0 carries the LDS base; nothing else in these kernels uses M0 (the asm
+// sets it before every copy), so listing the reserved register is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int WAVES>
+__device__ __forceinline__ void load_tile(const __bf16* rows, int valid_rows, uint32_t buf, int wave,
+                                          int lane) {
+#pragma unroll
+  for (int ii = 0; ii < kLoadsPerTile / WAVES; ++ii) {
+    const int i = wave + ii * WAVES;
+    const int slot = 64 * i + lane;
+    const int t = slot / kChunks;
+    const int c = (slot - t * kChunks) ^ swz(t);
+    const int tr = t < valid_rows ? t : valid_rows - 1;  // rows past the end: repeat a valid row
+    const char* g = reinterpret_cast<const char*>(rows) + static_cast<size_t>(tr) * (kD * 2) + c * 16;
+    dma16(g, buf + i * 1024);
+  }
+}
+
+template <int WAVES, int NBUF>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_bf16_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char tiles_raw[NBUF * kTileBytes];
+  __shared__ int second_pass;
+  MLA_LDS char* tiles = (MLA_LDS char*)tiles_raw;
+  const uint32_t tiles_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5;          // which 4-token half of each 8-token group
+  const int b = blockIdx.y;
+  const int rg = blockIdx.x % p.row_groups;
+  const int split = blockIdx.x / p.row_groups;
+
+  // block table and lengths are read through the scalar path (uniform per workgroup)
+  const MLA_CONST int32_t* block_table = (const MLA_CONST int32_t*)(p.block_table);
+  int T = ((const MLA_CONST int32_t*)(p.seq_lens))[b];
+  T = T < 0 ? 0 : (T > p.max_seq_len ? p.max_seq_len : T);
+  const int j0 = split * p.split_tokens;
+  const bool direct = p.num_splits == 1;
+  if (!direct && j0 >= T) return;  // empty chunk: the combine step skips it
+  const int j1 = min(j0 + p.split_tokens, T);
+  const int n_tiles = j1 > j0 ? (j1 - j0 + kTileT - 1) / kTileT : 0;
+
+  const int rows_per_req = p.q_len * p.n_h;
+  const int row0 = rg * (32 * WAVES) + wave * 32;  // first row of this wave
+  const int t_q = row0 / p.n_h;                     // query index of this wave
+  const int h0 = row0 % p.n_h;
+  const int n_tok = b * p.q_len + t_q;
+  const int vis_end = T - p.q_len + t_q + 1;         // keys < vis_end are visible
+  const int my_h = h0 + (lane & 31);
+  if (threadIdx.x == 0) second_pass = 0;
+
+  // latent query rows of this wave's heads, register resident: Q[h, 16s + 8hf .. +8]
+  bf16x8_t qf[36];
+  {
+    const __bf16* qrow = p.q_lat + (static_cast<int64_t>(n_tok) * p.n_h + my_h) * kD + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 36; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s);
+    wait_vmcnt<0>();  // complete before the tile copies start counting
+  }
+
+  // per-lane LDS byte offsets (tile independent)
+  const int tq = lane & 31;
+  const int fq = swz(tq);
+  int qk_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) qk_off[q] = (tq * kChunks + (((2 * q) | hf) ^ fq)) * 16;
+  const int L = lane & 15, cg = (lane >> 4) & 1;
+  int pv_off[2][2][2];  // [ks][h2][ct parity]
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int row = 16 * ks + 8 * h2 + 4 * hf + (L >> 2);
+      const int f = swz(row);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int x = 4 * par + 2 * cg + ((L & 3) >> 1);
+        pv_off[ks][h2][par] = (row * kChunks + (x ^ f)) * 16 + 8 * (L & 1);
+      }
+    }
+
+  const int64_t bt_row = static_cast<int64_t>(b) * p.max_blocks;
+  auto issue_tile = [&](int k, int bi) {
+    const int tok0 = j0 + k * kTileT;
+    const int valid = min(kTileT, T - tok0);
+    int blk = block_table[bt_row + tok0 / p.block_size];
+    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+    const __bf16* rows = p.cache + (static_cast<int64_t>(blk) * p.block_size + tok0 % p.block_size) * kD;
+    load_tile<WAVES>(rows, valid, tiles_addr + bi * kTileBytes, wave, lane);
+  };
+
+  // Softmax reference point m_ref (log2 domain, per lane = per head).  It is
+  // fixed at the first tile with a visible key and never moved inside the
+  // loop, so the accumulators are only ever touched by MFMA there: P =
+  // 2^(s - m_ref) may grow up to 2^kSlack (exact in fp32/bf16).  If some tile
+  // exceeds m_ref + kSlack, the chunk is processed again with m_ref = the
+  // exact chunk maximum found by the first pass (no third pass is needed).
+  constexpr float kSlack = 64.f;
+  f32x16_t oacc[16];
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+
+  auto run_pass = [&]() -> bool {
+    bool flagged = false;
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) oacc[ct] = f32x16_t{};
+    l_run = 0.f;
+    // prologue: tiles 0 .. NBUF-2 in flight
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < n_tiles) issue_tile(k, k);
+    int bcur = 0;
+    for (int k = 0; k < n_tiles; ++k) {
+      if constexpr (NBUF >= 3) {
+        if (k + 1 < n_tiles) wait_vmcnt<kLoadsPerTile / WAVES>();
+        else wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_s_barrier();  // tile k visible to all; tile k-1 released by all
+      if (k + NBUF - 1 < n_tiles) issue_tile(k + NBUF - 1, bcur == 0 ? NBUF - 1 : bcur - 1);
+      MLA_LDS char* buf = tiles + bcur * kTileBytes;
+      bcur = bcur == NBUF - 1 ? 0 : bcur + 1;
+
+      // scores S^T for 32 tokens x 32 heads, key fragments prefetched 4 ahead
+      f32x16_t sacc = f32x16_t{};
+      bf16x8_t kf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[s] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(buf + qk_off[s & 3] + (2 * s & ~7) * 16);
+#pragma unroll
+      for (int s = 0; s < 36; ++s) {
+        const bf16x8_t cur = kf[s & 3];
+        if (s + 4 < 36)
+          kf[s & 3] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(buf + qk_off[(s + 4) & 3] + (2 * (s + 4) & ~7) * 16);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sacc, 0, 0, 0);
+      }
+
+      // softmax numerators; register r holds token 8(r/4) + 4hf + r%4
+      const int tok_base = j0 + k * kTileT + 4 * hf;
+      float sv[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = tok_base + 8 * (r >> 2) + (r & 3);
+        sv[r] = tok < vis_end ? sacc[r] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_seen = fmaxf(m_seen, mx);
+      if (m_ref == -INFINITY) m_ref = mx;  // nothing accumulated yet for this head
+      flagged |= mx > m_ref + kSlack;
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      bf16x8_t pf[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(sv[r] - m_use);
+        psum += pr;
+        pf[r >> 3][r & 7] = f32_to_bf16(pr);
+      }
+      l_run += psum;
+
+      // O^T += V^T P^T over the tile's two 16-token k-steps
+      i16x4_t vlo[2], vhi[2];
+      auto vread = [&](int ks, int ct, int slot) {
+        const int hi_off = (ct >> 1) * 128;
+        vlo[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<MLA_LDS i16x4_t*>(buf + pv_off[ks][0][ct & 1] + hi_off));
+        vhi[slot] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<MLA_LDS i16x4_t*>(buf + pv_off[ks][1][ct & 1] + hi_off));
+      };
+      vread(0, 0, 0);
+#pragma unroll
+      for (int it = 0; it < 32; ++it) {
+        const int ks = it >> 4, ct = it & 15;
+        if (it + 1 < 32) vread((it + 1) >> 4, (it + 1) & 15, (it + 1) & 1);
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(vlo[it & 1], vhi[it & 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[ct], 0, 0, 0);
+      }
+    }
+    return flagged;
+  };
+
+  const bool flagged = run_pass();
+  // workgroup-wide decision on the second pass
+  if (__builtin_amdgcn_ballot_w64(flagged) != 0 && lane == 0) second_pass = 1;
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  if (second_pass) {
+    __builtin_amdgcn_s_barrier();
+    m_ref = m_seen;
+    run_pass();
+  }
+
+  // epilogue: normalise, write o (rows of this wave) and lse
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+  const int my_row = row0 + (lane & 31);
+  if (direct) {
+    __bf16* orow = p.o_lat + (static_cast<int64_t>(n_tok) * p.n_h + my_h) * kDc;
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4_t v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[ct][4 * j + i] * inv);
+        *reinterpret_cast<bf16x4_t*>(orow + 32 * ct + 8 * j + 4 * hf) = v;
+      }
+    if (p.lse != nullptr && hf == 0) p.lse[static_cast<int64_t>(n_tok) * p.n_h + my_h] = lse_v;
+  } else {
+    const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
+    float* orow = p.o_part + pr * kDc;
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4_t v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = oacc[ct][4 * j + i] * inv;
+        *reinterpret_cast<f32x4_t*>(orow + 32 * ct + 8 * j + 4 * hf) = v;
+      }
+    if (hf == 0) p.lse_part[pr] = lse_v;
+  }
+}
+
+// Merge the chunk partials of one row: L = log sum_s exp(lse_s),
+// o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).
+template <typename OutT>
+__global__ void __launch_bounds__(64) combine_kernel(const float* __restrict__ o_part,
+                                                     const float* __restrict__ lse_part,
+                                                     const int32_t* __restrict__ seq_lens,
+                                                     int num_splits, int split_tokens, int q_len,
+                                                     int n_h, int max_seq_len, OutT* __restrict__ o_lat,
+                                                     float* __restrict__ lse) {
+  const int row = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int rows = q_len * n_h;
+  int T = seq_lens[b];
+  T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
+  const int ns = (T + split_tokens - 1) / split_tokens;
+  const int64_t base = static_cast<int64_t>(b) * num_splits * rows + row;
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lse_part[base + static_cast<int64_t>(s) * rows]);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  float L = -INFINITY;
+  if (mx != -INFINITY) {
+    float sum = 0.f;
+    for (int s = 0; s < ns; ++s) sum += __expf(lse_part[base + static_cast<int64_t>(s) * rows] - mx);
+    L = mx + __logf(sum);
+    for (int s = 0; s < ns; ++s) {
+      const int64_t pr = base + static_cast<int64_t>(s) * rows;
+      const float w = __expf(lse_part[pr] - L);
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(o_part + pr * kDc + lane * 8);
+      const f32x4_t x0 = src[0], x1 = src[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] = fmaf(w, x0[i], acc[i]);
+        acc[4 + i] = fmaf(w, x1[i], acc[4 + i]);
+      }
+    }
+  }
+  const int n = b * q_len + row / n_h, h = row % n_h;
+  OutT* dst = o_lat + (static_cast<int64_t>(n) * n_h + h) * kDc + lane * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if constexpr (sizeof(OutT) == 2) dst[i] = f32_to_bf16(acc[i]);
+    else dst[i] = acc[i];
+  }
+  if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(n) * n_h + h] = L;
+}
+
+}  // namespace
+
+int decode_waves_per_group(int n_h, int q_len) {
+  const int rows = n_h * q_len;
+  return rows % 128 == 0 ? 4 : 2;
+}
+
+size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits) {
+  if (num_splits <= 1) return 0;
+  const size_t rows = static_cast<size_t>(batch) * num_splits * q_len * n_h;
+  return rows * kDc * sizeof(float) + rows * sizeof(float);
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+  DecodeParams p;
+  p.q_lat = static_cast<const __bf16*>(a.q_lat);
+  p.cache = static_cast<const __bf16*>(a.cache);
+  p.block_table = a.block_table;
+  p.seq_lens = a.seq_lens;
+  const size_t rows = static_cast<size_t>(a.batch) * a.num_splits * a.q_len * a.n_h;
+  p.o_part = static_cast<float*>(a.workspace);
+  p.lse_part = a.num_splits > 1 ? p.o_part + rows * kDc : nullptr;
+  p.o_lat = static_cast<__bf16*>(a.o_lat);
+  p.lse = a.lse;
+  p.max_blocks = a.max_blocks;
+  p.num_blocks = a.num_blocks;
+  p.block_size = a.block_size;
+  p.q_len = a.q_len;
+  p.n_h = a.n_h;
+  p.max_seq_len = a.max_seq_len;
+  p.split_tokens = a.split_tokens;
+  p.num_splits = a.num_splits;
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  const int waves = decode_waves_per_group(a.n_h, a.q_len);
+  p.row_groups = a.q_len * a.n_h / (32 * waves);
+  const dim3 grid(a.num_splits * p.row_groups, a.batch);
+  if (waves == 4)
+    hipLaunchKernelGGL((decode_bf16_kernel<4, 3>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<2, 2>), grid, dim3(128), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.num_splits == 1) return e;
+  const dim3 cgrid(a.q_len * a.n_h, a.batch);
+  hipLaunchKernelGGL((combine_kernel<__bf16>), cgrid, dim3(64), 0, st, p.o_part, p.lse_part,
+                     a.seq_lens, a.num_splits, a.split_tokens, a.q_len, a.n_h, a.max_seq_len,
+                     static_cast<__bf16*>(a.o_lat), a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

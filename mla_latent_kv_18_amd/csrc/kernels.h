@@ -1,0 +1,80 @@
+// Launch interfaces between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct AppendArgs {
+  const void* hidden;
+  const void* w;  // null: hidden holds the projection [n, d_c + d_r] fp32
+  const float* gamma;
+  const int32_t* positions;
+  const int64_t* slots;
+  int n_tokens, d_model, d_c, d_r;
+  int64_t cache_slots;
+  float eps, theta;
+  void* cache;
+  float* cache_scale;
+  void* workspace;
+  int cache_dtype;
+};
+
+struct AbsorbArgs {
+  const void* q_nope;
+  const void* q_pe;
+  const void* w_uk;
+  const int32_t* positions;
+  int n_tokens, n_h, d_h, d_c, d_r;
+  float theta;
+  void* q_lat;
+  float* q_scale;
+  void* workspace;
+  int cache_dtype;
+};
+
+struct DecodeArgs {
+  const void* q_lat;
+  const float* q_scale;
+  const void* cache;
+  const float* cache_scale;
+  const int32_t* block_table;
+  int max_blocks, num_blocks;
+  const int32_t* seq_lens;
+  int batch, q_len, n_h, d_c, d_r, block_size, max_seq_len;
+  int split_tokens, num_splits;
+  float scale;
+  void* workspace;
+  void* o_lat;
+  float* lse;
+  int cache_dtype;
+};
+
+struct OutProjArgs {
+  const void* o_lat;
+  const void* w_uv;
+  int n_tokens, n_h, d_c, d_v;
+  void* out;
+};
+
+// fp32, any dims
+hipError_t launch_append_f32(const AppendArgs&, hipStream_t);
+hipError_t launch_absorb_q_f32(const AbsorbArgs&, hipStream_t);
+hipError_t launch_decode_f32(const DecodeArgs&, hipStream_t);
+hipError_t launch_out_proj_f32(const OutProjArgs&, hipStream_t);
+
+// bf16 activations, d_c = 512, d_r = 64, d_h = d_v = 128 (MFMA)
+size_t append_mfma_workspace(int n_tokens);
+hipError_t launch_append_mfma(const AppendArgs&, hipStream_t);
+size_t absorb_mfma_workspace(int n_tokens, int n_h, int cache_dtype);
+hipError_t launch_absorb_q_mfma(const AbsorbArgs&, hipStream_t);
+hipError_t launch_out_proj_mfma(const OutProjArgs&, hipStream_t);
+
+// latent decode, bf16 or fp8 cache (d_c = 512, d_r = 64)
+int decode_waves_per_group(int n_h, int q_len);
+size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits);
+hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
+
+}  // namespace mla

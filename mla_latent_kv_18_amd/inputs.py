@@ -1,0 +1,215 @@
+"""Seeded synthetic inputs for MLA latent-cache decode.
+
+Shared by the GPU tests, the benchmark and the smoke check; holds only
+random draws, storage-format conversion and integer indexing (block tables,
+slots, positions) -- none of the method's arithmetic.  Both the HIP path and
+the CPU oracle consume the arrays produced here.
+
+Workloads (dims from the attention-variants page's DeepSeek-V3 / Kimi-K2
+hyper-parameters; shapes and lengths as the workload list states):
+
+  tiny_f32          fp32, 1 layer: B=1, n_h=4, d_model=64, d_c=32, d_h=16,
+                    d_R=8, d_v=16, 64 cached tokens (all built by the append
+                    call from hidden states), 1 query token
+  v3_bs64_ctx4k     DeepSeek-V3 attention dims, bf16: B=64, 4096 tokens each
+  v3_paged_bs16_ctx32k  same dims, B=16, 32768 tokens each, 64-token blocks
+                    with a seed-shuffled block table (split context + combine)
+  kimi_k2_ragged_bs32   n_h=64, B=32, lengths uniform in [1024, 131072]
+  v3_fp8_bs4_ctx128k_q2 fp8 e4m3 cache with one fp32 scale per token, B=4,
+                    131072 tokens each, 2 causal queries per request
+
+Value recipe: weights N(0,1)/sqrt(fan_in) (fan_in = d_model for the
+down-projection, d_c for W^UK and W^UV); RMSNorm gain U[0.5, 1.5]; hidden
+states, q_nope, q_pe and pre-filled latent rows N(0,1).  Rows T-q_len..T-1
+of each request are left empty in the pool: the append call writes them.
+
+Draw order for numpy.random.default_rng(seed): sequence lengths (ragged
+workload only), W_dkv_kr, W_UK, W_UV, gamma, pre-filled rows (request by
+request), hidden states, q_nope, q_pe, block permutation (shuffled tables).
+"""
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    n_h: int
+    d_c: int
+    d_h: int
+    d_r: int
+    d_v: int
+    d_model: int
+    batch: int
+    seq_len: int            # tokens per request (upper bound when ragged)
+    q_len: int
+    dtype: str              # "f32" | "bf16" | "fp8" (cache); activations f32 or bf16
+    block_size: int = 64
+    shuffle: bool = False
+    ragged_min: int = 0     # >0: lengths uniform in [ragged_min, seq_len]
+    seed: int = 0
+    all_rows_appended: bool = False
+    lens: tuple = ()        # explicit per-request lengths (overrides seq_len / ragged)
+
+    @property
+    def act_dtype(self):
+        return "f32" if self.dtype == "f32" else "bf16"
+
+    @property
+    def row_dim(self):
+        return self.d_c + self.d_r
+
+    @property
+    def softmax_scale(self):
+        return 1.0 / float(np.sqrt(self.d_h + self.d_r))
+
+    def scaled(self, **kw):
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", n_h=4, d_c=32, d_h=16, d_r=8, d_v=16, d_model=64,
+                         batch=1, seq_len=64, q_len=1, dtype="f32", seed=1, all_rows_appended=True),
+    "v3_bs64_ctx4k": Workload("v3_bs64_ctx4k", n_h=128, d_c=512, d_h=128, d_r=64, d_v=128,
+                              d_model=7168, batch=64, seq_len=4096, q_len=1, dtype="bf16", seed=2),
+    "v3_paged_bs16_ctx32k": Workload("v3_paged_bs16_ctx32k", n_h=128, d_c=512, d_h=128, d_r=64,
+                                     d_v=128, d_model=7168, batch=16, seq_len=32768, q_len=1,
+                                     dtype="bf16", shuffle=True, seed=3),
+    "kimi_k2_ragged_bs32": Workload("kimi_k2_ragged_bs32", n_h=64, d_c=512, d_h=128, d_r=64,
+                                    d_v=128, d_model=7168, batch=32, seq_len=131072, q_len=1,
+                                    dtype="bf16", shuffle=True, ragged_min=1024, seed=4),
+    "v3_fp8_bs4_ctx128k_q2": Workload("v3_fp8_bs4_ctx128k_q2", n_h=128, d_c=512, d_h=128, d_r=64,
+                                      d_v=128, d_model=7168, batch=4, seq_len=131072, q_len=2,
+                                      dtype="fp8", seed=5),
+}
+
+
+# ------------------------------------------------------------ storage formats
+def to_bf16_bits(x):
+    """float32 array -> uint16 bfloat16 bit patterns (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def to_fp8_rows(x):
+    """float32 rows -> (uint8 e4m3 codes, float32 scale per row), one scale
+    per row = max|row|/448 (1 for a zero row)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = torch.from_numpy(x / scale[..., None]).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), scale
+
+
+def _store(x, fmt):
+    if fmt == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if fmt == "bf16":
+        return to_bf16_bits(x)
+    raise ValueError(fmt)
+
+
+# ------------------------------------------------------------------ generate
+def seq_lens_of(w, rng=None):
+    if w.lens:
+        assert len(w.lens) == w.batch
+        return np.asarray(w.lens, dtype=np.int32)
+    if w.ragged_min > 0:
+        rng = np.random.default_rng(w.seed) if rng is None else rng
+        return rng.integers(w.ragged_min, w.seq_len, size=w.batch, endpoint=True).astype(np.int32)
+    return np.full(w.batch, w.seq_len, dtype=np.int32)
+
+
+def generate(w: Workload):
+    """All inputs of one decode step of `w`, as numpy arrays in storage form.
+
+    Returns a dict with:
+      seq_lens [B] int32, block_table [B, max_blocks] int32, pool
+      [num_blocks, block_size, d_c+d_R] (f32 / uint16 bf16 bits / uint8 e4m3
+      codes), pool_scale [num_blocks, block_size] float32 (fp8 only),
+      w_dkv_kr [d_c+d_R, d_model], w_uk [n_h, d_h, d_c], w_uv [n_h, d_v, d_c]
+      (f32 or bf16 bits), gamma [d_c] float32, h [N_new, d_model],
+      new_positions [N_new] int32, slot_mapping [N_new] int64,
+      q_nope [N, n_h, d_h], q_pe [N, n_h, d_R], q_positions [N] int32
+      (N = B*q_len), with N_new = N (or every row for all_rows_appended)."""
+    rng = np.random.default_rng(w.seed)
+    B, D, bs = w.batch, w.row_dim, w.block_size
+    seq = seq_lens_of(w, rng)
+    act = w.act_dtype
+    out = {"workload": w, "seq_lens": seq}
+    out["w_dkv_kr"] = _store(rng.standard_normal((D, w.d_model)) / np.sqrt(w.d_model), act)
+    out["w_uk"] = _store(rng.standard_normal((w.n_h, w.d_h, w.d_c)) / np.sqrt(w.d_c), act)
+    out["w_uv"] = _store(rng.standard_normal((w.n_h, w.d_v, w.d_c)) / np.sqrt(w.d_c), act)
+    out["gamma"] = rng.uniform(0.5, 1.5, size=w.d_c).astype(np.float32)
+
+    nblk = (seq + bs - 1) // bs
+    total_blocks = int(nblk.sum())
+    max_blocks = int(nblk.max())
+    # logical block i of request b -> physical block (identity before shuffling)
+    offsets = np.concatenate([[0], np.cumsum(nblk)[:-1]]).astype(np.int64)
+    pool_shape = (total_blocks, bs, D)
+    if w.dtype == "f32":
+        pool = np.zeros(pool_shape, dtype=np.float32)
+    elif w.dtype == "bf16":
+        pool = np.zeros(pool_shape, dtype=np.uint16)
+    else:
+        pool = np.zeros(pool_shape, dtype=np.uint8)
+    pool_scale = np.ones((total_blocks, bs), dtype=np.float32) if w.dtype == "fp8" else None
+
+    # pre-filled rows, request by request, written in logical order; the
+    # physical placement is applied after the permutation is drawn
+    prefill = []
+    for b in range(B):
+        n_pre = 0 if w.all_rows_appended else max(0, int(seq[b]) - w.q_len)
+        rows = rng.standard_normal((n_pre, D), dtype=np.float32)
+        prefill.append(rows)
+
+    n_new = int(seq[0]) if w.all_rows_appended else B * w.q_len
+    out["h"] = _store(rng.standard_normal((n_new, w.d_model)), act)
+    N = B * w.q_len
+    out["q_nope"] = _store(rng.standard_normal((N, w.n_h, w.d_h)), act)
+    out["q_pe"] = _store(rng.standard_normal((N, w.n_h, w.d_r)), act)
+
+    phys = np.arange(total_blocks, dtype=np.int64)
+    if w.shuffle:
+        phys = rng.permutation(total_blocks).astype(np.int64)
+    table = np.zeros((B, max_blocks), dtype=np.int32)
+    for b in range(B):
+        table[b, :nblk[b]] = phys[offsets[b]:offsets[b] + nblk[b]]
+    out["block_table"] = table
+
+    for b in range(B):
+        rows = prefill[b]
+        n_pre = rows.shape[0]
+        if n_pre == 0:
+            continue
+        idx = np.arange(n_pre)
+        blk = table[b, idx // bs]
+        if w.dtype == "f32":
+            pool[blk, idx % bs] = rows
+        elif w.dtype == "bf16":
+            pool[blk, idx % bs] = to_bf16_bits(rows)
+        else:
+            codes, scale = to_fp8_rows(rows)
+            pool[blk, idx % bs] = codes
+            pool_scale[blk, idx % bs] = scale
+        prefill[b] = None
+    out["pool"] = pool
+    out["pool_scale"] = pool_scale
+
+    if w.all_rows_appended:
+        pos = np.arange(n_new, dtype=np.int32)
+        req = np.zeros(n_new, dtype=np.int64)
+    else:
+        pos = np.concatenate([np.arange(w.q_len) + seq[b] - w.q_len for b in range(B)]).astype(np.int32)
+        req = np.repeat(np.arange(B), w.q_len)
+    valid = pos >= 0                       # a request shorter than q_len has nothing to append there
+    posc = np.where(valid, pos, 0)
+    out["new_positions"] = posc.astype(np.int32)
+    out["slot_mapping"] = np.where(valid, table[req, posc // bs].astype(np.int64) * bs + posc % bs, -1).astype(np.int64)
+    out["q_positions"] = np.concatenate(
+        [np.arange(w.q_len) + seq[b] - w.q_len for b in range(B)]).astype(np.int32)
+    return out

@@ -1,0 +1,78 @@
+"""One MLA decode step on the GPU: upload a generated workload and run the
+four libmla calls (append -> absorb q -> decode -> out proj).  Plumbing
+only: torch allocates device memory, libmla does every computation."""
+
+import numpy as np
+import torch
+
+from . import absorb_q, append_latent, decode, decode_workspace_size, make_dims, out_proj
+
+
+def _dev(a, device, fmt):
+    a = np.ascontiguousarray(a)
+    if fmt == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceStep:
+    def __init__(self, gen, device="cuda:0", split_tokens=0):
+        w = gen["workload"]
+        self.w = w
+        self.device = device
+        act = w.act_dtype
+        self.dims = make_dims(w.n_h, w.d_c, w.d_h, w.d_r, w.d_v, w.d_model, w.block_size,
+                              w.dtype, act)
+        self.w_dkv_kr = _dev(gen["w_dkv_kr"], device, act)
+        self.w_uk = _dev(gen["w_uk"], device, act)
+        self.w_uv = _dev(gen["w_uv"], device, act)
+        self.gamma = _dev(gen["gamma"], device, "f32")
+        self.h = _dev(gen["h"], device, act)
+        self.q_nope = _dev(gen["q_nope"], device, act)
+        self.q_pe = _dev(gen["q_pe"], device, act)
+        self.cache = _dev(gen["pool"], device, w.dtype if w.dtype != "fp8" else "u8")
+        self.cache_scale = _dev(gen["pool_scale"], device, "f32") if w.dtype == "fp8" else None
+        self.block_table = _dev(gen["block_table"], device, "i32")
+        self.seq_lens = _dev(gen["seq_lens"], device, "i32")
+        self.max_seq_len = int(gen["seq_lens"].max())
+        self.new_pos = _dev(gen["new_positions"], device, "i32")
+        self.slots = _dev(gen["slot_mapping"], device, "i64")
+        self.q_pos = _dev(gen["q_positions"], device, "i32")
+        N = w.batch * w.q_len
+        D = w.d_c + w.d_r
+        lat_dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.dtype]
+        out_dtype = torch.float32 if act == "f32" else torch.bfloat16
+        self.q_lat = torch.empty(N, w.n_h, D, dtype=lat_dtype, device=device)
+        self.q_scale = torch.empty(N, w.n_h, dtype=torch.float32, device=device) if w.dtype == "fp8" else None
+        self.o_lat = torch.empty(N, w.n_h, w.d_c, dtype=out_dtype, device=device)
+        self.lse = torch.empty(N, w.n_h, dtype=torch.float32, device=device)
+        self.out = torch.empty(N, w.n_h, w.d_v, dtype=out_dtype, device=device)
+        self.split_tokens = split_tokens
+        nws = decode_workspace_size(self.dims, w.batch, w.q_len, self.max_seq_len, split_tokens)
+        self.decode_ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
+
+    def append(self):
+        append_latent(self.dims, self.h, self.w_dkv_kr, self.gamma, self.new_pos, self.slots,
+                      self.cache, self.cache_scale)
+
+    def absorb(self):
+        absorb_q(self.dims, self.q_nope, self.q_pe, self.w_uk, self.q_pos, self.q_lat, self.q_scale)
+
+    def decode(self, split_tokens=None):
+        st = self.split_tokens if split_tokens is None else split_tokens
+        ws = self.decode_ws
+        need = decode_workspace_size(self.dims, self.w.batch, self.w.q_len, self.max_seq_len, st)
+        if need > ws.numel():
+            ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        decode(self.dims, self.q_lat, self.cache, self.block_table, self.seq_lens, self.max_seq_len,
+               self.o_lat, self.lse, q_scale=self.q_scale, cache_scale=self.cache_scale,
+               q_len=self.w.q_len, split_tokens=st, workspace=ws)
+
+    def out_proj(self):
+        out_proj(self.dims, self.o_lat, self.w_uv, self.out)
+
+    def run(self):
+        self.append()
+        self.absorb()
+        self.decode()
+        self.out_proj()

@@ -1,0 +1,108 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/mla.h declares, and rejects bad arguments before any launch (these
+calls never reach the GPU).  CPU only."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_kv_18_amd as mla
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = mla.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(mla.EXPORTS) == names
+
+
+def v3_dims(**kw):
+    a = dict(n_h=128, d_c=512, d_h=128, d_r=64, d_v=128, d_model=7168, block_size=64,
+             cache_dtype="bf16", act_dtype="bf16")
+    a.update(kw)
+    return mla.make_dims(**a)
+
+
+def test_sizes_and_status_strings():
+    lib = mla.lib()
+    d = v3_dims()
+    assert lib.mla_cache_row_bytes(ctypes.byref(d)) == 576 * 2
+    assert lib.mla_cache_row_bytes(ctypes.byref(v3_dims(cache_dtype="fp8"))) == 576
+    f32 = mla.make_dims(4, 32, 16, 8, 16, 64, 64, "f32", "f32")
+    assert lib.mla_cache_row_bytes(ctypes.byref(f32)) == 40 * 4
+    assert lib.mla_status_string(0) == b"MLA_OK"
+    assert lib.mla_version() >= 100
+    # default split: one resident wave of workgroups for the 64 x 4096 decode
+    assert mla.default_split(d, 64, 1, 4096) == 1024
+    assert mla.decode_workspace_size(d, 64, 1, 4096) == 64 * 4 * 128 * (512 + 1) * 4
+    assert mla.decode_workspace_size(d, 64, 1, 256) == 0          # one chunk: no partials
+
+
+def call_decode(d, **over):
+    lib = mla.lib()
+    a = dict(q_lat=1, q_scale=None, cache=1, cache_scale=None, block_table=1, max_blocks=64,
+             num_blocks=64, seq_lens=1, batch=64, q_len=1, max_seq_len=4096, split=0, ws=1,
+             ws_bytes=1 << 30, o_lat=1, lse=None, stream=None)
+    a.update(over)
+    return lib.mla_decode(ctypes.byref(d), a["q_lat"], a["q_scale"], a["cache"], a["cache_scale"],
+                          a["block_table"], a["max_blocks"], a["num_blocks"], a["seq_lens"], a["batch"],
+                          a["q_len"], a["max_seq_len"], a["split"], a["ws"], a["ws_bytes"], a["o_lat"],
+                          a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q_lat=None), 1),
+    (dict(q_len=3), 2),
+    (dict(max_seq_len=4097), 1),
+    (dict(split=100), 1),
+    (dict(ws_bytes=10), 3),
+    (dict(num_blocks=0), 1),
+])
+def test_decode_rejects_bad_arguments_on_host(over, status):
+    assert call_decode(v3_dims(), **over) == status
+    assert mla.lib().mla_last_error_message()
+
+
+def test_unsupported_dims_and_dtypes():
+    lib = mla.lib()
+    bad = v3_dims(d_c=256)
+    assert lib.mla_cache_row_bytes(ctypes.byref(bad)) == (256 + 64) * 2   # defined for any dims
+    assert call_decode(bad) == 2
+    assert call_decode(v3_dims(n_h=96)) == 2
+    assert call_decode(v3_dims(block_size=32)) == 2
+    mixed = v3_dims(cache_dtype="bf16", act_dtype="f32")
+    assert call_decode(mixed) == 2
+    odd = v3_dims(d_r=63)
+    assert call_decode(odd) == 1
+
+
+def test_zero_work_calls_succeed_without_launch():
+    lib = mla.lib()
+    d = v3_dims()
+    assert lib.mla_append_latent(ctypes.byref(d), None, None, None, None, None, 0, 64, None, None,
+                                 None, 0, None) == 0
+    assert lib.mla_absorb_q(ctypes.byref(d), None, None, None, None, 0, None, None, None, 0, None) == 0
+    assert lib.mla_out_proj(ctypes.byref(d), None, None, 0, None, None) == 0
+    assert call_decode(d, batch=0) == 0
+
+
+def test_missing_workspace_and_scales_are_reported():
+    lib = mla.lib()
+    d = v3_dims()
+    assert lib.mla_append_latent(ctypes.byref(d), 1, 1, 1, 1, 1, 64, 4096, 1, None, None, 0, None) == 3
+    d8 = v3_dims(cache_dtype="fp8")
+    assert lib.mla_append_latent(ctypes.byref(d8), 1, 1, 1, 1, 1, 64, 4096, 1, None, 1, 1 << 30, None) == 1
+    assert lib.mla_absorb_q(ctypes.byref(d8), 1, 1, 1, 1, 64, 1, None, 1, 1 << 30, None) == 1
+    assert call_decode(d8) == 1
