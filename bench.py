@@ -1,0 +1,169 @@
+"""Benchmark one MLA decode step (append -> absorb q -> decode -> out proj)
+on the DeepSeek-V3 attention shape: batch 64, 4096 cached tokens per
+request, bf16 latent cache, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints one JSON line.  `value` is latent-cache GB/s of the whole step
+(cache bytes read per step / step time, inputs resident in HBM); the
+`roofline` object covers the decode call (its algorithmic cache bytes per
+launch / its average launch time from HIP events on the launch stream);
+`cpu_baseline` times the float64 CPU oracle on a bounded sample of the
+same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+WORKLOAD = "v3_bs64_ctx4k"
+COUNTERS = os.path.join(ROOT, "profiles", "decode_v3_bs64_ctx4k_counters.json")
+DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_18_amd", "csrc", "decode_mfma.hip")
+
+
+def decode_source_hash():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, or
+    None when absent or taken on a different decode kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("decode_source_sha256_16") != decode_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(gen, min_seconds=10.0, max_requests=64):
+    """The float64 oracle, as it stands, on whole requests of the workload
+    (all heads, non-absorbed) until at least `min_seconds` of CPU work."""
+    from threadpoolctl import threadpool_info
+
+    from tests import oracle_views as ov
+
+    w = gen["workload"]
+    t0 = time.perf_counter()
+    n = 0
+    while n < max_requests:
+        ov.reference_output(gen, n)
+        n += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cache_bytes = int(sum(int(gen["seq_lens"][b]) for b in range(n))) * w.row_dim * 2
+    return {"value": round(cache_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} of {w.batch} requests of {w.name} (all {w.n_h} heads, 4096 tokens each), "
+                      f"non-absorbed float64 MLA, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "libmla runs on one GPU; multi-GPU sharding is described in "
+                                   "DESIGN.md and not built, so --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from mla_latent_kv_18_amd.inputs import WORKLOADS, generate
+    from mla_latent_kv_18_amd.step import DeviceStep
+
+    w = WORKLOADS[WORKLOAD]
+    gen = generate(w)
+    step = DeviceStep(gen, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    cache_bytes = int(gen["seq_lens"].sum()) * w.row_dim * 2                    # bf16 rows read
+    flops = int(gen["seq_lens"].sum()) * w.q_len * 2 * w.n_h * (w.row_dim + w.d_c)
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.append()
+        step.absorb()
+        ev[i][0].record(stream)
+        step.decode()
+        ev[i][1].record(stream)
+        step.out_proj()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    decode_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+
+    # decode alone with the last-level caches flushed before each launch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    cold = []
+    for _ in range(10):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step.decode()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del scratch
+    cold_ms = sorted(cold)[len(cold) // 2]
+
+    achieved = cache_bytes / (decode_ms * 1e-3) / 1e9
+    out = {
+        "metric": "MLA decode latent-cache GB/s + TFLOP/s, % roofline (V3 shape, bs64, ctx 4k)",
+        "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latent rows, N(0,1)/sqrt(fan_in) weights)",
+        "config": {"workload": WORKLOAD, "num_heads": w.n_h, "kv_lora_rank": w.d_c,
+                   "qk_rope_head_dim": w.d_r, "qk_nope_head_dim": w.d_h, "v_head_dim": w.d_v,
+                   "hidden_size": w.d_model, "batch": w.batch, "cached_tokens": w.seq_len,
+                   "q_len": w.q_len, "block_size": w.block_size,
+                   "split_tokens": step.split_tokens or None},
+        "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
+        "decode_ms": round(decode_ms, 5),
+        "decode_cold_ms": round(cold_ms, 5),
+        "decode_tflops": round(flops / (decode_ms * 1e-3) / 1e12, 2),
+        "decode_mfma_frac": round(flops / (decode_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "mla_decode (chunk partials + combine)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "bytes_per_launch": cache_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(gen)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
