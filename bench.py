@@ -116,11 +116,12 @@ def main():
     ms_step = wall * 1e3 / args.steps
     decode_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
-    # decode alone with the last-level caches flushed before each launch
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    # decode alone with the last-level caches flushed before each launch: a
+    # 1 GiB read (a write would leave dirty lines whose write-back competes)
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
     cold = []
     for _ in range(10):
-        scratch.fill_(1)
+        scratch.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         step.decode()

@@ -62,7 +62,7 @@ mla_status_t resolve(const mla_dims_t* d, Resolved* r) {
                   r->d_c, r->d_r, r->d_h, r->d_v);
     if (r->n_h % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "bf16/fp8 kernels need num_heads %% 64 == 0");
     if (r->bs % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "bf16/fp8 kernels need block_size %% 64 == 0");
-    if (r->d_model % 16 != 0) return fail(MLA_ERR_UNSUPPORTED, "hidden_size must be a multiple of 16");
+    if (r->d_model % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "hidden_size must be a multiple of 64");
     r->mfma = true;
     return MLA_OK;
   }

@@ -45,7 +45,7 @@ struct DecodeParams {
   const __bf16* cache;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* o_part;
+  __bf16* o_part;
   float* lse_part;
   __bf16* o_lat;
   float* lse;
@@ -293,15 +293,15 @@ decode_bf16_kernel(DecodeParams p) {
     if (p.lse != nullptr && hf == 0) p.lse[static_cast<int64_t>(n_tok) * p.n_h + my_h] = lse_v;
   } else {
     const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
-    float* orow = p.o_part + pr * kDc;
+    __bf16* orow = p.o_part + pr * kDc;
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f32x4_t v;
+        bf16x4_t v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = oacc[ct][4 * j + i] * inv;
-        *reinterpret_cast<f32x4_t*>(orow + 32 * ct + 8 * j + 4 * hf) = v;
+        for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[ct][4 * j + i] * inv);
+        *reinterpret_cast<bf16x4_t*>(orow + 32 * ct + 8 * j + 4 * hf) = v;
       }
     if (hf == 0) p.lse_part[pr] = lse_v;
   }
@@ -310,7 +310,7 @@ decode_bf16_kernel(DecodeParams p) {
 // Merge the chunk partials of one row: L = log sum_s exp(lse_s),
 // o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).
 template <typename OutT>
-__global__ void __launch_bounds__(64) combine_kernel(const float* __restrict__ o_part,
+__global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ o_part,
                                                      const float* __restrict__ lse_part,
                                                      const int32_t* __restrict__ seq_lens,
                                                      int num_splits, int split_tokens, int q_len,
@@ -335,13 +335,9 @@ __global__ void __launch_bounds__(64) combine_kernel(const float* __restrict__ o
     for (int s = 0; s < ns; ++s) {
       const int64_t pr = base + static_cast<int64_t>(s) * rows;
       const float w = __expf(lse_part[pr] - L);
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(o_part + pr * kDc + lane * 8);
-      const f32x4_t x0 = src[0], x1 = src[1];
+      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(o_part + pr * kDc + lane * 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] = fmaf(w, x0[i], acc[i]);
-        acc[4 + i] = fmaf(w, x1[i], acc[4 + i]);
-      }
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, static_cast<float>(x[i]), acc[i]);
     }
   }
   const int n = b * q_len + row / n_h, h = row % n_h;
@@ -364,7 +360,7 @@ int decode_waves_per_group(int n_h, int q_len) {
 size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits) {
   if (num_splits <= 1) return 0;
   const size_t rows = static_cast<size_t>(batch) * num_splits * q_len * n_h;
-  return rows * kDc * sizeof(float) + rows * sizeof(float);
+  return rows * kDc * sizeof(__bf16) + rows * sizeof(float);  // bf16 partials, fp32 lse
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
@@ -374,8 +370,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   p.block_table = a.block_table;
   p.seq_lens = a.seq_lens;
   const size_t rows = static_cast<size_t>(a.batch) * a.num_splits * a.q_len * a.n_h;
-  p.o_part = static_cast<float*>(a.workspace);
-  p.lse_part = a.num_splits > 1 ? p.o_part + rows * kDc : nullptr;
+  p.o_part = static_cast<__bf16*>(a.workspace);
+  p.lse_part = a.num_splits > 1 ? reinterpret_cast<float*>(p.o_part + rows * kDc) : nullptr;
   p.o_lat = static_cast<__bf16*>(a.o_lat);
   p.lse = a.lse;
   p.max_blocks = a.max_blocks;

@@ -61,18 +61,26 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   return s ? -v : v;
 }
 
-// Rotary-embedding angle for pair k of a d_r-wide vector at `pos`, in
-// double: pos / theta^(2k/d_r).  Double keeps the phase accurate at the
-// 131072-token positions (a float angle would be off by ~1e-2 rad there).
+// Rotary embedding: pair k of a d_r-wide vector at `pos` turns by
+// pos / theta^(2k/d_r).  The angle and its reduction to [-pi, pi] are done in
+// double (at the 131072-token positions a float angle would be off by ~1e-2
+// rad); the reduced angle then goes through float sin/cos.
+__device__ __forceinline__ void rope_cos_sin_inv(int pos, double inv_freq, float* c, float* s) {
+  const double ang = static_cast<double>(pos) * inv_freq;
+  const double red = ang - 6.283185307179586477 * rint(ang * 0.15915494309189533577);
+  sincosf(static_cast<float>(red), s, c);
+}
+
 __device__ __forceinline__ void rope_cos_sin(int pos, int k, int d_r, float theta, float* c,
                                              float* s) {
-  double inv = exp2(-(2.0 * k / d_r) * log2(static_cast<double>(theta)));
-  double ang = static_cast<double>(pos) * inv;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  *c = static_cast<float>(cd);
-  *s = static_cast<float>(sd);
+  rope_cos_sin_inv(pos, exp2(-(2.0 * k / d_r) * log2(static_cast<double>(theta))), c, s);
 }
+
+// Inverse frequencies theta^(-2k/64) of a 64-wide rotary part, computed on
+// the host in double and passed by value to the kernels that need them.
+struct RopeTable64 {
+  double inv[32];
+};
 
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {

@@ -46,7 +46,7 @@ def test_sizes_and_status_strings():
     assert lib.mla_version() >= 100
     # default split: one resident wave of workgroups for the 64 x 4096 decode
     assert mla.default_split(d, 64, 1, 4096) == 1024
-    assert mla.decode_workspace_size(d, 64, 1, 4096) == 64 * 4 * 128 * (512 + 1) * 4
+    assert mla.decode_workspace_size(d, 64, 1, 4096) == 64 * 4 * 128 * (512 * 2 + 4)   # bf16 partials + fp32 lse
     assert mla.decode_workspace_size(d, 64, 1, 256) == 0          # one chunk: no partials
 
 
