@@ -98,6 +98,12 @@ typedef struct {
  * variants, MLA section: per-token elements = d_c + d_R per layer.] */
 size_t mla_cache_row_bytes(const mla_dims_t* dims);
 
+/* Bytes of one latent-query row q_lat[n, i] as mla_absorb_q writes it and
+ * mla_decode reads it: (d_c + d_R) * element size for fp32 / bf16; for an
+ * fp8 cache two e4m3 planes of d_c + d_R codes each (see mla_absorb_q).
+ * Returns 0 for invalid dims. */
+size_t mla_q_lat_row_bytes(const mla_dims_t* dims);
+
 /* ---------------------------------------------------------------- append
  * New cache rows [MLA explainer: low-rank section eq.(2), decoupled RoPE
  * section eq.(15), trade-offs section (normalisation of the latent);
@@ -130,7 +136,11 @@ mla_status_t mla_append_latent(const mla_dims_t* dims, const void* hidden,
  *                                                  W^UK_i is d_h x d_c)
  *   q_lat[n, i, d_c:] = RoPE(q_pe[n, i], positions[n])
  * q_nope: [n_tokens, n_h, d_h], q_pe: [n_tokens, n_h, d_R] act_dtype.
- * q_lat: [n_tokens, n_h, d_c + d_R] in cache_dtype (fp32 / bf16 / e4m3).
+ * q_lat: [n_tokens, n_h, d_c + d_R] in cache_dtype for fp32 / bf16.  For an
+ *          fp8 cache each row is two e4m3 planes [hi (d_c + d_R) | lo (d_c +
+ *          d_R)] with x = row / q_scale, hi = e4m3(x), lo = e4m3((x - hi) * 16),
+ *          so row ~= q_scale * (hi + lo / 16) to about 8 significant bits
+ *          (mla_q_lat_row_bytes() gives the row size).
  * q_scale: [n_tokens, n_h] fp32 for fp8 (scale = max|q_lat row| / 448),
  *          else NULL.
  * workspace: at least mla_absorb_workspace_size() bytes (0 unless fp8: the
@@ -153,7 +163,8 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void
  * merges them; with one chunk per request the partial step writes o_lat
  * directly.  split_tokens = 0 picks a size from the shapes; otherwise it
  * must be a positive multiple of 64 (bf16/fp8) and only changes rounding.
- * q_lat: [batch*q_len, n_h, d_c + d_R] cache_dtype; q_scale as above.
+ * q_lat: [batch*q_len, n_h] rows as mla_absorb_q writes them; q_scale as
+ *   above.
  * cache: pool [num_blocks, block_size, d_c + d_R]; cache_scale [num_blocks,
  *   block_size] for fp8 else NULL.
  * block_table: [batch, max_blocks_per_seq] int32 physical block ids, each

@@ -21,7 +21,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
           3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_HIP"}
 
 # every entry point declared in include/mla.h
-EXPORTS = ("mla_cache_row_bytes", "mla_append_workspace_size", "mla_append_latent",
+EXPORTS = ("mla_cache_row_bytes", "mla_q_lat_row_bytes", "mla_append_workspace_size", "mla_append_latent",
            "mla_absorb_workspace_size", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_decode", "mla_decode_default_split", "mla_out_proj", "mla_status_string",
            "mla_last_error_message", "mla_version")
@@ -62,6 +62,7 @@ def lib():
     P, I32, I64, SZ, DP = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.POINTER(Dims)
     sig = {
         "mla_cache_row_bytes": (SZ, [DP]),
+        "mla_q_lat_row_bytes": (SZ, [DP]),
         "mla_append_workspace_size": (SZ, [DP, I32]),
         "mla_append_latent": (I32, [DP, P, P, P, P, P, I32, I64, P, P, P, SZ, P]),
         "mla_absorb_workspace_size": (SZ, [DP, I32]),
@@ -124,7 +125,8 @@ def append_latent(dims, hidden, w_dkv_kr, gamma, positions, slot_mapping, cache,
 
 
 def absorb_q(dims, q_nope, q_pe, w_uk, positions, q_lat, q_scale=None, workspace=None):
-    """mla_absorb_q: q_lat [N, n_h, d_c+d_R] (and q_scale [N, n_h] for fp8)."""
+    """mla_absorb_q: q_lat [N, n_h, row] with row = mla_q_lat_row_bytes (and q_scale
+    [N, n_h] for fp8: two e4m3 planes per row)."""
     n = q_nope.shape[0]
     need = lib().mla_absorb_workspace_size(ctypes.byref(dims), n)
     if workspace is None:

@@ -94,6 +94,11 @@ size_t mla_cache_row_bytes(const mla_dims_t* dims) {
   return static_cast<size_t>(dims->kv_lora_rank + dims->qk_rope_head_dim) * elem_size(dims->cache_dtype);
 }
 
+size_t mla_q_lat_row_bytes(const mla_dims_t* dims) {
+  const size_t row = mla_cache_row_bytes(dims);
+  return dims != nullptr && dims->cache_dtype == MLA_FP8_E4M3 ? 2 * row : row;
+}
+
 size_t mla_append_workspace_size(const mla_dims_t* dims, int32_t n_tokens) {
   Resolved r;
   if (resolve(dims, &r) != MLA_OK || n_tokens <= 0) return 0;
@@ -211,14 +216,14 @@ mla_status_t mla_decode(const mla_dims_t* dims, const void* q_lat, const float* 
   a.lse = lse;
   a.cache_dtype = r.cache_dtype;
   if (!r.mfma) return hip_status(mla::launch_decode_f32(a, s), "mla_decode");
-  if (r.cache_dtype == MLA_FP8_E4M3) return fail(MLA_ERR_UNSUPPORTED, "fp8 decode not built yet");
   a.split_tokens = split_tokens > 0 ? split_tokens : default_split(r, batch, q_len, max_seq_len);
   a.num_splits = max_seq_len > 0 ? (max_seq_len + a.split_tokens - 1) / a.split_tokens : 1;
   const size_t need = mla::decode_mfma_workspace(batch, q_len, r.n_h, a.num_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
   a.workspace = workspace;
-  return hip_status(mla::launch_decode_mfma(a, s), "mla_decode");
+  return hip_status(r.cache_dtype == MLA_FP8_E4M3 ? mla::launch_decode_fp8(a, s) : mla::launch_decode_mfma(a, s),
+                    "mla_decode");
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv,

@@ -29,6 +29,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace mla {
 namespace {
@@ -58,28 +59,6 @@ __device__ __forceinline__ int swz(int t) {
   const int u = (t >> 1) & 7;
   return u ^ ((u & 1) << 2);
 }
-
-// s_waitcnt with vmcnt <= n (lgkmcnt / expcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// One wave-wide 16-byte-per-lane global->LDS copy: lane i's 16 bytes land at
-// lds_base + 16*i.  Issued from inline asm so that the compiler's wait-count
-// pass does not stall every later LDS read on it (it cannot tell which
-// buffer the copy targets); the kernel orders it with explicit vmcnt waits.
-// M0 carries the LDS base; nothing else in these kernels uses M0 (the asm
-// sets it before every copy), so listing the reserved register is safe.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
-               "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 template <int WAVES>
 __device__ __forceinline__ void load_tile(const __bf16* rows, int valid_rows, uint32_t buf, int wave,
@@ -392,9 +371,16 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_bf16_kernel<2, 2>), grid, dim3(128), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
+  return launch_combine(a, st);
+}
+
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
+  const size_t rows = static_cast<size_t>(a.batch) * a.num_splits * a.q_len * a.n_h;
+  const __bf16* o_part = static_cast<const __bf16*>(a.workspace);
+  const float* lse_part = reinterpret_cast<const float*>(o_part + rows * kDc);
   const dim3 cgrid(a.q_len * a.n_h, a.batch);
-  hipLaunchKernelGGL((combine_kernel<__bf16>), cgrid, dim3(64), 0, st, p.o_part, p.lse_part,
-                     a.seq_lens, a.num_splits, a.split_tokens, a.q_len, a.n_h, a.max_seq_len,
+  hipLaunchKernelGGL((combine_kernel<__bf16>), cgrid, dim3(64), 0, st, o_part, lse_part, a.seq_lens,
+                     a.num_splits, a.split_tokens, a.q_len, a.n_h, a.max_seq_len,
                      static_cast<__bf16*>(a.o_lat), a.lse);
   return hipGetLastError();
 }

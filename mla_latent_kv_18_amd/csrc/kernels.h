@@ -76,5 +76,8 @@ hipError_t launch_out_proj_mfma(const OutProjArgs&, hipStream_t);
 int decode_waves_per_group(int n_h, int q_len);
 size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits);
 hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
+hipError_t launch_decode_fp8(const DecodeArgs&, hipStream_t);
+// merge of the chunk partials that a split decode left in the workspace
+hipError_t launch_combine(const DecodeArgs&, hipStream_t);
 
 }  // namespace mla

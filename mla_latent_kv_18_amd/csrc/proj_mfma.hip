@@ -238,7 +238,10 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
   }
 }
 
-// fp32 latent query rows -> e4m3 codes + one fp32 scale per (token, head).
+// fp32 latent query rows -> two e4m3 planes + one fp32 scale per (token, head):
+// x = row / scale (scale = max|row| / 448), hi = e4m3(x), lo = e4m3((x - hi) * 16),
+// so row ~= scale * (hi + lo / 16) to about 8 significant bits.  The output
+// row is [hi (576 codes) | lo (576 codes)].
 __global__ void __launch_bounds__(64) quantize_rows_fp8_kernel(const float* __restrict__ src,
                                                                uint8_t* __restrict__ dst,
                                                                float* __restrict__ scale_out) {
@@ -253,8 +256,15 @@ __global__ void __launch_bounds__(64) quantize_rows_fp8_kernel(const float* __re
   }
   am = wave_max(am);
   const float scale = am > 0.f ? am / 448.f : 1.f;
+  uint8_t* d = dst + static_cast<int64_t>(row) * (2 * kD);
 #pragma unroll
-  for (int i = 0; i < 9; ++i) dst[static_cast<int64_t>(row) * kD + lane + 64 * i] = static_cast<uint8_t>(f32_to_e4m3(v[i] / scale));
+  for (int i = 0; i < 9; ++i) {
+    const float x = v[i] / scale;
+    const uint32_t hi = f32_to_e4m3(x);
+    const uint32_t lo = f32_to_e4m3((x - e4m3_to_f32(hi)) * 16.f);
+    d[lane + 64 * i] = static_cast<uint8_t>(hi);
+    d[kD + lane + 64 * i] = static_cast<uint8_t>(lo);
+  }
   if (lane == 0) scale_out[row] = scale;
 }
 

@@ -42,7 +42,7 @@ class DeviceStep:
         D = w.d_c + w.d_r
         lat_dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.dtype]
         out_dtype = torch.float32 if act == "f32" else torch.bfloat16
-        self.q_lat = torch.empty(N, w.n_h, D, dtype=lat_dtype, device=device)
+        self.q_lat = torch.empty(N, w.n_h, 2 * D if w.dtype == "fp8" else D, dtype=lat_dtype, device=device)
         self.q_scale = torch.empty(N, w.n_h, dtype=torch.float32, device=device) if w.dtype == "fp8" else None
         self.o_lat = torch.empty(N, w.n_h, w.d_c, dtype=out_dtype, device=device)
         self.lse = torch.empty(N, w.n_h, dtype=torch.float32, device=device)

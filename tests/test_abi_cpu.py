@@ -40,6 +40,8 @@ def test_sizes_and_status_strings():
     d = v3_dims()
     assert lib.mla_cache_row_bytes(ctypes.byref(d)) == 576 * 2
     assert lib.mla_cache_row_bytes(ctypes.byref(v3_dims(cache_dtype="fp8"))) == 576
+    assert lib.mla_q_lat_row_bytes(ctypes.byref(d)) == 576 * 2
+    assert lib.mla_q_lat_row_bytes(ctypes.byref(v3_dims(cache_dtype="fp8"))) == 2 * 576   # hi + lo planes
     f32 = mla.make_dims(4, 32, 16, 8, 16, 64, 64, "f32", "f32")
     assert lib.mla_cache_row_bytes(ctypes.byref(f32)) == 40 * 4
     assert lib.mla_status_string(0) == b"MLA_OK"

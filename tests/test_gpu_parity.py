@@ -65,9 +65,13 @@ def check_request(step, gen, b, heads, tol, lse_tol):
     q_pe = ov.f64(gen["q_pe"], act)[sl]
     q_pos = gen["q_positions"][sl]
     q_lat_ref = ref.absorb_q(q_nope, q_pe, q_pos, wuk)
-    q_lat = _host(step.q_lat[sl], w.dtype)
-    if w.dtype == "fp8":
-        q_lat = q_lat * step.q_scale[sl].cpu().numpy().astype(np.float64)[..., None]
+    if w.dtype == "fp8":   # two planes: row = scale * (hi + lo / 16)
+        planes = _host(step.q_lat[sl], "fp8")
+        D = w.row_dim
+        q_lat = (planes[..., :D] + planes[..., D:] / 16.0) * \
+            step.q_scale[sl].cpu().numpy().astype(np.float64)[..., None]
+    else:
+        q_lat = _host(step.q_lat[sl], w.dtype)
     assert ov.rel_err(q_lat[:, heads], q_lat_ref[:, heads]) <= tol, "absorb q"
     # decode, fed the GPU's q_lat and cache rows
     o_ref, lse_ref = ref.decode_absorbed(q_lat[:, heads], q_pos, rows[:, :w.d_c], rows[:, w.d_c:],
@@ -150,7 +154,25 @@ def test_empty_request_gives_zero_and_neg_inf():
         check_request(step, gen, 1, list(range(w.n_h)), ov.TOL["bf16"], 2e-2)
 
 
-FULL = ["v3_bs64_ctx4k", "v3_paged_bs16_ctx32k", "kimi_k2_ragged_bs32"]
+SMALL_FP8 = {
+    "fp8_q2_ragged": dict(batch=3, lens=(1, 100, 257), shuffle=True),
+    "fp8_q2_tiles": dict(batch=2, lens=(64, 130)),
+    "fp8_q1": dict(batch=2, lens=(65, 300), q_len=1),
+    "fp8_heads64_q2": dict(n_h=64, batch=2, lens=(2, 200), shuffle=True),
+    "fp8_heads64_q1": dict(n_h=64, batch=2, lens=(129, 33), q_len=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_FP8))
+@pytest.mark.parametrize("split_tokens", [0, 64, 128])
+def test_small_fp8_all_heads(name, split_tokens):
+    w = WORKLOADS["v3_fp8_bs4_ctx128k_q2"].scaled(name=name, seed=11, **SMALL_FP8[name])
+    gen, step = _run(w, split_tokens)
+    for b in range(w.batch):
+        check_request(step, gen, b, list(range(w.n_h)), ov.TOL["fp8"], 2e-2)
+
+
+FULL = ["v3_bs64_ctx4k", "v3_paged_bs16_ctx32k", "kimi_k2_ragged_bs32", "v3_fp8_bs4_ctx128k_q2"]
 
 
 @pytest.mark.parametrize("name", FULL)
