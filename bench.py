@@ -2,7 +2,10 @@
 on the DeepSeek-V3 attention shape: batch 64, 4096 cached tokens per
 request, bf16 latent cache, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+--workload picks another workload of mla_latent_kv_18_amd.inputs.WORKLOADS
+(the paged, ragged and fp8 shapes); the default is the one above.
 
 Prints one JSON line.  `value` is latent-cache GB/s of the whole step
 (cache bytes read per step / step time, inputs resident in HBM); the
@@ -23,8 +26,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense, TFLOP/s
 WORKLOAD = "v3_bs64_ctx4k"
+METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % roofline (V3 shape, bs64, ctx 4k)"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_v3_bs64_ctx4k_counters.json")
 DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_18_amd", "csrc", "decode_mfma.hip")
 
@@ -47,28 +51,40 @@ def measured_traffic():
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(gen, min_seconds=10.0, max_requests=64):
-    """The float64 oracle, as it stands, on whole requests of the workload
-    (all heads, non-absorbed) until at least `min_seconds` of CPU work."""
+def cpu_baseline(gen, min_seconds=10.0, max_units=64):
+    """The float64 oracle, as it stands (non-absorbed MLA), on whole requests
+    of the workload (all heads) until at least `min_seconds` of CPU work; for
+    workloads whose single request takes longer, on head subsets of one
+    request.  Reported as cache GB/s-equivalent: rows x row bytes x fraction
+    of heads done, per second."""
     from threadpoolctl import threadpool_info
 
     from tests import oracle_views as ov
 
     w = gen["workload"]
+    row_bytes = w.row_dim * (1 if w.dtype == "fp8" else 2) + (4 if w.dtype == "fp8" else 0)
+    T0 = int(gen["seq_lens"][0])
+    whole = T0 * w.q_len * w.n_h <= 4096 * 128
     t0 = time.perf_counter()
-    n = 0
-    while n < max_requests:
-        ov.reference_output(gen, n)
+    done_bytes, n = 0.0, 0
+    while n < max_units:
+        if whole:
+            b = n % w.batch
+            ov.reference_output(gen, b)
+            done_bytes += int(gen["seq_lens"][b]) * row_bytes
+        else:
+            heads = [(8 * n + k) % w.n_h for k in range(8)]
+            ov.reference_output(gen, 0, heads=heads)
+            done_bytes += T0 * row_bytes * len(heads) / w.n_h
         n += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    cache_bytes = int(sum(int(gen["seq_lens"][b]) for b in range(n))) * w.row_dim * 2
-    return {"value": round(cache_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} of {w.batch} requests of {w.name} (all {w.n_h} heads, 4096 tokens each), "
-                      f"non-absorbed float64 MLA, {dt:.1f} s"}
+    what = (f"{n} of {w.batch} requests of {w.name} (all {w.n_h} heads)" if whole else
+            f"{8 * n} head evaluations of request 0 of {w.name} ({T0} tokens, q_len {w.q_len})")
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": f"{what}, non-absorbed float64 MLA, {dt:.1f} s"}
 
 
 def main():
@@ -77,6 +93,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="workload name from mla_latent_kv_18_amd.inputs.WORKLOADS (default: the "
+                         "V3 shape, batch 64, 4096 cached tokens, bf16)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "libmla runs on one GPU; multi-GPU sharding is described in "
@@ -88,13 +107,17 @@ def main():
     from mla_latent_kv_18_amd.inputs import WORKLOADS, generate
     from mla_latent_kv_18_amd.step import DeviceStep
 
-    w = WORKLOADS[WORKLOAD]
+    w = WORKLOADS[args.workload]
     gen = generate(w)
     step = DeviceStep(gen, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    cache_bytes = int(gen["seq_lens"].sum()) * w.row_dim * 2                    # bf16 rows read
-    flops = int(gen["seq_lens"].sum()) * w.q_len * 2 * w.n_h * (w.row_dim + w.d_c)
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    n_rows = int(gen["seq_lens"].sum())
+    cache_bytes = n_rows * (w.row_dim * elem + (4 if w.dtype == "fp8" else 0))   # rows (+ fp8 scales) read
+    flops = n_rows * w.q_len * 2 * w.n_h * (w.row_dim + w.d_c)                 # scores + weighted sum
+    mfma_peak = MFMA_PEAK_TFLOPS[w.dtype]
+    bound = "mfma" if flops / (mfma_peak * 1e12) > cache_bytes / (HBM_PEAK_GBS * 1e9) else "hbm"
 
     for _ in range(args.warmup):
         step.run()
@@ -131,9 +154,19 @@ def main():
     del scratch
     cold_ms = sorted(cold)[len(cold) // 2]
 
-    achieved = cache_bytes / (decode_ms * 1e-3) / 1e9
+    gbs = cache_bytes / (decode_ms * 1e-3) / 1e9
+    tflops = flops / (decode_ms * 1e-3) / 1e12
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic() if args.workload == WORKLOAD else None,
+                "bytes_per_launch": cache_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(tflops / mfma_peak, 4), "traffic": None, "flops_per_launch": flops}
+    roof["kernel"] = "mla_decode (chunk partials + combine)"
     out = {
-        "metric": "MLA decode latent-cache GB/s + TFLOP/s, % roofline (V3 shape, bs64, ctx 4k)",
+        "metric": METRIC if args.workload == WORKLOAD else f"MLA decode latent-cache GB/s ({args.workload})",
         "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -143,23 +176,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) latent rows, N(0,1)/sqrt(fan_in) weights)",
-        "config": {"workload": WORKLOAD, "num_heads": w.n_h, "kv_lora_rank": w.d_c,
+        "config": {"workload": args.workload, "num_heads": w.n_h, "kv_lora_rank": w.d_c,
                    "qk_rope_head_dim": w.d_r, "qk_nope_head_dim": w.d_h, "v_head_dim": w.d_v,
-                   "hidden_size": w.d_model, "batch": w.batch, "cached_tokens": w.seq_len,
+                   "hidden_size": w.d_model, "batch": w.batch, "cached_tokens_total": n_rows,
+                   "max_cached_tokens": int(gen["seq_lens"].max()),
                    "q_len": w.q_len, "block_size": w.block_size,
                    "split_tokens": step.split_tokens or None},
         "step_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
         "decode_ms": round(decode_ms, 5),
         "decode_cold_ms": round(cold_ms, 5),
-        "decode_tflops": round(flops / (decode_ms * 1e-3) / 1e12, 2),
-        "decode_mfma_frac": round(flops / (decode_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "mla_decode (chunk partials + combine)",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "bytes_per_launch": cache_bytes},
+        "decode_gbs": round(gbs, 2),
+        "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "decode_tflops": round(tflops, 2),
+        "decode_mfma_frac": round(tflops / mfma_peak, 4),
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(gen)

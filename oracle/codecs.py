@@ -12,6 +12,10 @@ Written from the public format definitions, not from any library:
 
 All arithmetic is float64; every quantisation step below is exact in float64
 (scaling by powers of two), so the only rounding is the intended one.
+
+Parity unpinned: the per-row fp8 scale recipe of e4m3_quantize_rows (one
+fp32 scale per cache row, max|x| / 448) is a reading; the pages give no fp8
+storage recipe.  The codecs themselves are pinned exhaustively.
 """
 
 import numpy as np

@@ -26,6 +26,10 @@ Conventions (row-major, one token per row):
 
 Nothing is blocked, fused or reordered beyond the definitions; loops are
 per request and per head so a reader can check each line against the pages.
+
+Parity unpinned: the RMSNorm eps constant (the pages name the norm but no
+eps; 1e-6 is a reading).  The norm's form is pinned by closed forms, the
+constant is not.
 """
 
 import numpy as np

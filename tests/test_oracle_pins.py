@@ -423,6 +423,24 @@ def test_rmsnorm_gain_folds_into_up_projections():
     assert np.max(np.abs(a - c)) > 1e-3
 
 
+def test_rmsnorm_closed_forms():
+    """RMSNorm's own definition: with gain 1 and eps 0 the output has unit
+    root-mean-square, it is invariant to a positive rescaling of its input,
+    a constant vector maps to its sign times the gain, and eps only matters
+    against mean(x^2).  (The eps constant itself is a reading, not pinned.)"""
+    rng = np.random.default_rng(12)
+    x = rng.normal(size=(5, 16)) * rng.uniform(0.1, 10, size=(5, 1))
+    y = ref.rmsnorm(x, np.ones(16), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, atol=1e-14)
+    assert np.allclose(ref.rmsnorm(3.7 * x, np.ones(16), 0.0), y, atol=1e-14)
+    gamma = rng.uniform(0.5, 1.5, size=16)
+    assert np.allclose(ref.rmsnorm(np.full(16, -2.5), gamma, 0.0), -gamma, atol=1e-15)
+    assert np.allclose(ref.rmsnorm(x, gamma, 0.0), y * gamma, atol=1e-14)
+    small = np.full(16, 1e-4)      # mean(x^2) = 1e-8: eps = 1e-6 dominates
+    assert abs(ref.rmsnorm(small, np.ones(16), 1e-6)[0] - 1e-4 / math.sqrt(1e-8 + 1e-6)) < 1e-15
+    assert np.all(ref.rmsnorm(np.zeros(16), gamma, 1e-6) == 0)
+
+
 def test_softmax_special_cases():
     rng = np.random.default_rng(11)
     T, n_h, d_c, d_r = 10, 3, 8, 4
