@@ -123,21 +123,25 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # whole steps, nothing else on the stream: this is `value`
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step.append()
-        step.absorb()
-        ev[i][0].record(stream)
-        step.decode()
-        ev[i][1].record(stream)
-        step.out_proj()
+    for _ in range(args.steps):
+        step.run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    decode_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+
+    # the decode call alone, K launches back to back between two HIP events
+    # recorded on the launch stream: the average launch duration
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(args.steps):
+        step.decode()
+    b.record(stream)
+    torch.cuda.synchronize()
+    decode_ms = a.elapsed_time(b) / args.steps
 
     # decode alone with the last-level caches flushed before each launch: a
     # 1 GiB read (a write would leave dirty lines whose write-back competes)

@@ -88,6 +88,8 @@ __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restri
   }
 }
 
+constexpr int kMaxChunks = 16;  // contraction slices of the append GEMM
+
 // One workgroup (256 threads) per token: reduce the partials, RMSNorm the
 // latent, rotate the key part, convert, write the cache row.
 template <bool FP8>
@@ -100,10 +102,24 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
   const int n = blockIdx.x, tid = threadIdx.x;
   const int64_t slot = slots[n];
   if (slot < 0 || slot >= cache_slots) return;
-  for (int c = tid; c < kD; c += 256) {
-    float s = 0.f;
-    for (int kc = 0; kc < n_chunks; ++kc) s += partial[(static_cast<int64_t>(kc) * n_tokens + n) * kD + c];
-    kv[c] = s;
+  // all chunk partials of this thread's columns are requested before any is summed
+  {
+    float v[kMaxChunks][3];
+#pragma unroll
+    for (int kc = 0; kc < kMaxChunks; ++kc)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int c = tid + 256 * j;
+        v[kc][j] = (kc < n_chunks && c < kD) ? partial[(static_cast<int64_t>(kc) * n_tokens + n) * kD + c] : 0.f;
+      }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int c = tid + 256 * j;
+      float s = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < kMaxChunks; ++kc) s += v[kc][j];
+      if (c < kD) kv[c] = s;
+    }
   }
   __syncthreads();
   float ss = 0.f;
@@ -218,21 +234,39 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
     }
   }
   if (n_tokens <= 0) __syncthreads();
-  if (ct == 0) {  // RoPE part of the latent query
-    for (int i = threadIdx.x; i < n_tokens * 32; i += 256) {
-      const int n = i >> 5, k = i & 31;
-      float cs, sn;
-      rope_cos_sin_inv(positions[n], rope.inv[k], &cs, &sn);
-      const __bf16* qr = q_pe + (static_cast<int64_t>(n) * n_h + head) * kDr;
-      const float x1 = static_cast<float>(qr[k]), x2 = static_cast<float>(qr[32 + k]);
-      const int64_t base = (static_cast<int64_t>(n) * n_h + head) * kD + kDc;
-      const float y1 = x1 * cs - x2 * sn, y2 = x1 * sn + x2 * cs;
+  if (ct == 0) {  // RoPE part of the latent query: thread = (token, 8 of the 32 pairs)
+    for (int i = threadIdx.x; i < n_tokens * 4; i += 256) {
+      const int n = i >> 2, k0 = 8 * (i & 3);
+      const __bf16* qr = q_pe + (static_cast<int64_t>(n) * n_h + head) * kDr + k0;
+      const bf16x8_t x1 = load8(qr), x2 = load8(qr + 32);
+      const int pos = positions[n];
+      const int64_t base = (static_cast<int64_t>(n) * n_h + head) * kD + kDc + k0;
+      float y1[8], y2[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float cs, sn;
+        rope_cos_sin_inv(pos, rope.inv[k0 + k], &cs, &sn);
+        const float a = static_cast<float>(x1[k]), b = static_cast<float>(x2[k]);
+        y1[k] = a * cs - b * sn;
+        y2[k] = a * sn + b * cs;
+      }
       if constexpr (OUT_F32) {
-        static_cast<float*>(q_out)[base + k] = y1;
-        static_cast<float*>(q_out)[base + 32 + k] = y2;
+        float* o = static_cast<float*>(q_out) + base;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          o[k] = y1[k];
+          o[32 + k] = y2[k];
+        }
       } else {
-        static_cast<__bf16*>(q_out)[base + k] = f32_to_bf16(y1);
-        static_cast<__bf16*>(q_out)[base + 32 + k] = f32_to_bf16(y2);
+        bf16x8_t o1, o2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          o1[k] = f32_to_bf16(y1[k]);
+          o2[k] = f32_to_bf16(y2[k]);
+        }
+        __bf16* o = static_cast<__bf16*>(q_out) + base;
+        *reinterpret_cast<bf16x8_t*>(o) = o1;
+        *reinterpret_cast<bf16x8_t*>(o + 32) = o2;
       }
     }
   }
