@@ -124,7 +124,6 @@ def main():
     torch.cuda.synchronize()
 
     # whole steps, nothing else on the stream: this is `value`
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step.run()

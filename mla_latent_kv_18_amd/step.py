@@ -1,11 +1,15 @@
 """One MLA decode step on the GPU: upload a generated workload and run the
 four libmla calls (append -> absorb q -> decode -> out proj).  Plumbing
-only: torch allocates device memory, libmla does every computation."""
+only: torch allocates device memory and streams, libmla does every
+computation.  capture() records a whole step (or the decode call alone)
+into a HIP graph for callers that replay steps from a graph."""
+
+import ctypes
 
 import numpy as np
 import torch
 
-from . import absorb_q, append_latent, decode, decode_workspace_size, make_dims, out_proj
+from . import absorb_q, append_latent, decode, decode_workspace_size, lib, make_dims, out_proj
 
 
 def _dev(a, device, fmt):
@@ -50,13 +54,19 @@ class DeviceStep:
         self.split_tokens = split_tokens
         nws = decode_workspace_size(self.dims, w.batch, w.q_len, self.max_seq_len, split_tokens)
         self.decode_ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
+        n_new = len(gen["new_positions"])
+        self.append_ws = torch.empty(max(lib().mla_append_workspace_size(ctypes.byref(self.dims), n_new), 1),
+                                     dtype=torch.uint8, device=device)
+        self.absorb_ws = torch.empty(max(lib().mla_absorb_workspace_size(ctypes.byref(self.dims), N), 1),
+                                     dtype=torch.uint8, device=device)
 
     def append(self):
         append_latent(self.dims, self.h, self.w_dkv_kr, self.gamma, self.new_pos, self.slots,
-                      self.cache, self.cache_scale)
+                      self.cache, self.cache_scale, workspace=self.append_ws)
 
     def absorb(self):
-        absorb_q(self.dims, self.q_nope, self.q_pe, self.w_uk, self.q_pos, self.q_lat, self.q_scale)
+        absorb_q(self.dims, self.q_nope, self.q_pe, self.w_uk, self.q_pos, self.q_lat, self.q_scale,
+                 workspace=self.absorb_ws)
 
     def decode(self, split_tokens=None):
         st = self.split_tokens if split_tokens is None else split_tokens
@@ -76,3 +86,16 @@ class DeviceStep:
         self.absorb()
         self.decode()
         self.out_proj()
+
+    def capture(self, decode_only=False):
+        """HIP graph of one step (or of the decode call).  Every buffer the
+        kernels touch is allocated beforehand; the step is run eagerly once
+        first so that all kernels are loaded before capture."""
+        fn = self.decode if decode_only else self.run
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g

@@ -186,3 +186,29 @@ def test_full_size_sampled(name):
     for b in reqs:
         heads = sorted(set([0, w.n_h - 1] + [int(x) for x in rng.integers(w.n_h, size=2)]))
         check_request(step, gen, b, heads, ov.TOL[w.dtype], 2e-2)
+
+
+def test_graph_replay_matches_eager():
+    """A captured step replays the same kernels: every replay, with eager
+    work and synchronisations between replays, equals the eager step
+    bitwise (the path is deterministic)."""
+    w = WORKLOADS["v3_bs64_ctx4k"].scaled(name="graph", batch=3, lens=(300, 77, 1000), shuffle=True, seed=12)
+    gen, step = _run(w, 256)
+    ref = [step.out.clone(), step.o_lat.clone(), step.lse.clone()]
+    g = step.capture()
+    for _ in range(3):
+        step.out.zero_()
+        step.o_lat.zero_()
+        step.lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((step.out, step.o_lat, step.lse), ref):
+            assert torch.equal(got, want)
+        step.decode(split_tokens=64)   # eager work between replays
+        torch.cuda.synchronize()
+    gd = step.capture(decode_only=True)
+    step.o_lat.zero_()
+    gd.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(step.o_lat, ref[1])
