@@ -131,16 +131,17 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    # the decode call alone, K launches back to back between two HIP events
-    # recorded on the launch stream: the average launch duration
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record(stream)
-    for _ in range(args.steps):
+    # the decode call alone: K calls, each between two HIP events recorded on
+    # the launch stream (partial kernel + combine), averaged; launches back to
+    # back would add the host's launch gaps to the GPU time
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
         step.decode()
-    b.record(stream)
-    torch.cuda.synchronize()
-    decode_ms = a.elapsed_time(b) / args.steps
+        b.record(stream)
+        torch.cuda.synchronize()
+    decode_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
     # decode alone with the last-level caches flushed before each launch: a
     # 1 GiB read (a write would leave dirty lines whose write-back competes)
