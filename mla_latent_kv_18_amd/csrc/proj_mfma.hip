@@ -35,7 +35,7 @@ __device__ __forceinline__ bf16x8_t load8(const __bf16* p) { return *reinterpret
 // issued before its MFMAs; the 4 wave partials are summed through LDS.
 // partial[kc][n][r] = sum_{k in slice kc} h[n][k] * W[r][k]
 constexpr int kProjWaves = 4;
-constexpr int kMaxMTiles = 2;  // tokens per pass: 64
+constexpr int kMaxMTiles = 1;  // 32-token tiles per pass; blockIdx.z picks the tile
 
 __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restrict__ h,
                                                           const __bf16* __restrict__ w, int n_tokens,
@@ -47,9 +47,11 @@ __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restri
   const int ksteps = chunk_len / 16 / kProjWaves;  // per wave
   const int k_begin = kc * chunk_len + wave * ksteps * 16;
   const __bf16* wrow = w + static_cast<int64_t>(r0 + l32) * d_model + k_begin + 8 * hf;
-  for (int m0 = 0; m0 < n_tokens; m0 += 32 * kMaxMTiles) {
+  for (int m0 = blockIdx.z * 32 * kMaxMTiles; m0 < n_tokens; m0 += gridDim.z * 32 * kMaxMTiles) {
     const int mts = min(kMaxMTiles, (n_tokens - m0 + 31) / 32);
-    f32x16_t acc[kMaxMTiles] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t acc[kMaxMTiles];
+#pragma unroll
+    for (int mt = 0; mt < kMaxMTiles; ++mt) acc[mt] = f32x16_t{};
     for (int kb = 0; kb < ksteps; kb += 8) {
       bf16x8_t bw[8], ha[kMaxMTiles][8];
 #pragma unroll
@@ -201,14 +203,18 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
     }
   }
   const int L = lane & 15, cg = (lane >> 4) & 1;
-  for (int m0 = 0; m0 < n_tokens; m0 += 32) {
+  bool staged = false;  // W slice visible to every wave
+  for (int m0 = blockIdx.z * 32; m0 < n_tokens; m0 += gridDim.z * 32) {
     const int n_a = m0 + l32;
     bf16x8_t a[kDh / 16];
 #pragma unroll
     for (int ks = 0; ks < kDh / 16; ++ks)
       a[ks] = n_a < n_tokens ? load8(q_nope + (static_cast<int64_t>(n_a) * n_h + head) * kDh + 16 * ks + 8 * hf)
                              : bf16x8_t{};
-    if (m0 == 0) __syncthreads();  // W slice staged
+    if (!staged) {
+      __syncthreads();
+      staged = true;
+    }
     f32x16_t acc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < kDh / 16; ++ks) {
@@ -233,10 +239,11 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
       }
     }
   }
-  if (n_tokens <= 0) __syncthreads();
-  if (ct == 0) {  // RoPE part of the latent query: thread = (token, 8 of the 32 pairs)
+  if (!staged) __syncthreads();
+  if (ct == 0) {  // RoPE part of the latent query: thread = (token, 8 of the 32 pairs), own token tiles
     for (int i = threadIdx.x; i < n_tokens * 4; i += 256) {
       const int n = i >> 2, k0 = 8 * (i & 3);
+      if (static_cast<int>((n >> 5) % gridDim.z) != static_cast<int>(blockIdx.z)) continue;
       const __bf16* qr = q_pe + (static_cast<int64_t>(n) * n_h + head) * kDr + k0;
       const bf16x8_t x1 = load8(qr), x2 = load8(qr + 32);
       const int pos = positions[n];
@@ -317,7 +324,7 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
   bf16x8_t bw[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) bw[j] = load8(wrow + 16 * j);
-  for (int m0 = 0; m0 < n_tokens; m0 += 32 * kMaxMTiles) {
+  for (int m0 = blockIdx.z * 32 * kMaxMTiles; m0 < n_tokens; m0 += gridDim.z * 32 * kMaxMTiles) {
     const int mts = min(kMaxMTiles, (n_tokens - m0 + 31) / 32);
     bf16x8_t oa[kMaxMTiles][8];
 #pragma unroll
@@ -329,7 +336,9 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
                         ? load8(o_lat + (static_cast<int64_t>(n) * n_h + head) * kDc + c_begin + 16 * j + 8 * hf)
                         : bf16x8_t{};
     }
-    f32x16_t acc[kMaxMTiles] = {f32x16_t{}, f32x16_t{}};
+    f32x16_t acc[kMaxMTiles];
+#pragma unroll
+    for (int mt = 0; mt < kMaxMTiles; ++mt) acc[mt] = f32x16_t{};
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -363,6 +372,17 @@ int append_chunks(int d_model) {
   return best;
 }
 
+// 32-token tiles of the append GEMM run by separate workgroups (grid z), so
+// that the latency chain of one workgroup (operand loads, MFMA, reduction,
+// stores) covers one tile; beyond kMaxZ tiles a workgroup loops over several.
+// (For absorb and out proj a second tile workgroup re-reads the same weight
+// slice, which costs more than it saves: they keep one workgroup per slice.)
+constexpr int kMaxZ = 16;
+int token_tiles(int n_tokens) {
+  const int t = (n_tokens + 32 * kMaxMTiles - 1) / (32 * kMaxMTiles);
+  return t < 1 ? 1 : (t > kMaxZ ? kMaxZ : t);
+}
+
 RopeTable64 rope_table(float theta) {
   RopeTable64 t;
   for (int k = 0; k < 32; ++k) t.inv[k] = std::pow(static_cast<double>(theta), -2.0 * k / kDr);
@@ -381,7 +401,7 @@ hipError_t launch_append_mfma(const AppendArgs& a, hipStream_t st) {
   if (a.w != nullptr) {
     n_chunks = append_chunks(a.d_model);
     float* ws = static_cast<float*>(a.workspace);
-    hipLaunchKernelGGL(append_proj_kernel, dim3(kD / 32, n_chunks), dim3(256), 0, st,
+    hipLaunchKernelGGL(append_proj_kernel, dim3(kD / 32, n_chunks, token_tiles(a.n_tokens)), dim3(256), 0, st,
                        static_cast<const __bf16*>(a.hidden), static_cast<const __bf16*>(a.w),
                        a.n_tokens, a.d_model, a.d_model / n_chunks, ws);
     hipError_t e = hipGetLastError();
@@ -407,7 +427,7 @@ size_t absorb_mfma_workspace(int n_tokens, int n_h, int cache_dtype) {
 }
 
 hipError_t launch_absorb_q_mfma(const AbsorbArgs& a, hipStream_t st) {
-  const dim3 grid(a.n_h, kDc / 128);
+  const dim3 grid(a.n_h, kDc / 128);  // one workgroup per W slice: staging it twice costs more than it saves
   if (a.cache_dtype == 2) {
     hipLaunchKernelGGL(absorb_q_kernel<true>, grid, dim3(256), 0, st,
                        static_cast<const __bf16*>(a.q_nope), static_cast<const __bf16*>(a.q_pe),
