@@ -287,7 +287,10 @@ decode_bf16_kernel(DecodeParams p) {
 }
 
 // Merge the chunk partials of one row: L = log sum_s exp(lse_s),
-// o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).
+// o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).  The lse of up
+// to 64 splits is read lane-parallel, and the partial rows of each batch of 8
+// splits are requested before any of them is weighted, so the merge costs a
+// few memory round trips rather than one per split.
 template <typename OutT>
 __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ o_part,
                                                      const float* __restrict__ lse_part,
@@ -301,30 +304,48 @@ __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ 
   T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
   const int ns = (T + split_tokens - 1) / split_tokens;
   const int64_t base = static_cast<int64_t>(b) * num_splits * rows + row;
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, lse_part[base + static_cast<int64_t>(s) * rows]);
+  auto lse_of = [&](int s) { return lse_part[base + static_cast<int64_t>(s) * rows]; };
+  const float v0 = lane < ns ? lse_of(lane) : -INFINITY;  // splits 0..63
+  float mx = v0;
+  for (int s = 64 + lane; s < ns; s += 64) mx = fmaxf(mx, lse_of(s));
+  mx = wave_max(mx);
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float L = -INFINITY;
   if (mx != -INFINITY) {
-    float sum = 0.f;
-    for (int s = 0; s < ns; ++s) sum += __expf(lse_part[base + static_cast<int64_t>(s) * rows] - mx);
-    L = mx + __logf(sum);
-    for (int s = 0; s < ns; ++s) {
-      const int64_t pr = base + static_cast<int64_t>(s) * rows;
-      const float w = __expf(lse_part[pr] - L);
-      const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(o_part + pr * kDc + lane * 8);
+    float sum = v0 == -INFINITY ? 0.f : __expf(v0 - mx);
+    for (int s = 64 + lane; s < ns; s += 64) {
+      const float v = lse_of(s);
+      sum += v == -INFINITY ? 0.f : __expf(v - mx);
+    }
+    L = mx + __logf(wave_sum(sum));
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      bf16x8_t x[8];
+      float w[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, static_cast<float>(x[i]), acc[i]);
+      for (int j = 0; j < 8; ++j) {
+        const int s = s0 + j;
+        x[j] = s < ns ? *reinterpret_cast<const bf16x8_t*>(o_part + (base + static_cast<int64_t>(s) * rows) * kDc + lane * 8)
+                      : bf16x8_t{};
+        w[j] = s < ns ? __expf(lse_of(s) - L) : 0.f;  // uniform address: one line per wave
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], static_cast<float>(x[j][i]), acc[i]);
     }
   }
   const int n = b * q_len + row / n_h, h = row % n_h;
   OutT* dst = o_lat + (static_cast<int64_t>(n) * n_h + h) * kDc + lane * 8;
+  if constexpr (sizeof(OutT) == 2) {
+    bf16x8_t v;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if constexpr (sizeof(OutT) == 2) dst[i] = f32_to_bf16(acc[i]);
-    else dst[i] = acc[i];
+    for (int i = 0; i < 8; ++i) v[i] = f32_to_bf16(acc[i]);
+    *reinterpret_cast<bf16x8_t*>(dst) = v;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = acc[i];
   }
   if (lse != nullptr && lane == 0) lse[static_cast<int64_t>(n) * n_h + h] = L;
 }
