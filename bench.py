@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # dense, TFLOP/s
+SPIN_CYCLES = 400_000               # GPU-side wait queued before each timed decode call (~0.2 ms)
 WORKLOAD = "v3_bs64_ctx4k"
 METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % roofline (V3 shape, bs64, ctx 4k)"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_v3_bs64_ctx4k_counters.json")
@@ -132,11 +133,14 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     # the decode call alone: K calls, each between two HIP events recorded on
-    # the launch stream (partial kernel + combine), averaged; launches back to
-    # back would add the host's launch gaps to the GPU time
+    # the launch stream (partial kernel + combine), averaged.  A GPU-side spin
+    # (no memory traffic) is queued first, so that both events and the call
+    # are on the queue before the GPU reaches them and the host's launch
+    # latency is not timed.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for a, b in ev:
+        torch.cuda._sleep(SPIN_CYCLES)
         a.record(stream)
         step.decode()
         b.record(stream)

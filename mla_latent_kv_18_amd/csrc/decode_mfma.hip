@@ -52,6 +52,7 @@ struct DecodeParams {
   float* lse;
   int max_blocks, num_blocks, block_size, q_len, n_h, max_seq_len;
   int split_tokens, num_splits, row_groups;
+  int xcd_group;  // 1: the workgroups of one request share an XCD (see xcd_slot)
   float scale_log2;
 };
 
@@ -286,6 +287,323 @@ decode_bf16_kernel(DecodeParams p) {
   }
 }
 
+// Software-pipelined form of the kernel above for workgroups of four waves
+// (128 rows, one query position).  Step k scores tile k+1, turns the scores
+// into softmax numerators and adds tile k's weighted value rows, as one
+// instruction stream per wave: two independent score chains and the
+// weighted-sum MFMAs alternate so the matrix pipe never waits on a chain,
+// the softmax VALU work runs between the last weighted-sum MFMAs, and the
+// wave's nine tile copies are spread over the stream.  The weighted sum is
+// split by latent columns: wave w accumulates O^T for columns
+// 128w..128w+127 of all 128 heads, reading each transposed value fragment
+// once and reusing it for four head groups; the numerators P^T of all heads
+// go through LDS.  Per tile and CU this reads 184 KB of LDS (keys 147 KB,
+// values 16 KB, P 24 KB with the writes) where per-head value reads would
+// take 275 KB.  The streams are written out instruction by instruction
+// (decode_bf16_asm.inc, generated by gen_decode_bf16_asm.py) because the
+// register budget (Q: 144 VGPRs, O: 256 AGPRs, one wave per SIMD) leaves the
+// compiler's scheduler no room for this overlap.  LDS: four tile buffers
+// (tile k values, tile k+1 keys, tile k+2 landing, tile k+3 being copied)
+// and two P^T buffers.  The softmax is that of the kernel above; the scores
+// are summed in a different order (two chains), so results agree to fp32
+// rounding of the scores rather than bit for bit.
+constexpr int kPipeBufs = 4;
+constexpr int kPipeCopies = kLoadsPerTile / 4;  // 9 copies per wave per tile
+constexpr int kPBytes = kTileT * 128 * 2;        // P^T of one tile, all heads, bf16
+
+#define MLA_ASM_ACC                                                                          \
+  [o0] "+a"(oacc[0]), [o1] "+a"(oacc[1]), [o2] "+a"(oacc[2]), [o3] "+a"(oacc[3]),            \
+      [o4] "+a"(oacc[4]), [o5] "+a"(oacc[5]), [o6] "+a"(oacc[6]), [o7] "+a"(oacc[7]),        \
+      [o8] "+a"(oacc[8]), [o9] "+a"(oacc[9]), [o10] "+a"(oacc[10]), [o11] "+a"(oacc[11]),    \
+      [o12] "+a"(oacc[12]), [o13] "+a"(oacc[13]), [o14] "+a"(oacc[14]), [o15] "+a"(oacc[15])
+#define MLA_ASM_Q                                                                            \
+  [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),       \
+      [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),   \
+      [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),            \
+      [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]),            \
+      [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]),            \
+      [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]),            \
+      [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]),            \
+      [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]),            \
+      [q34] "v"(qf[34]), [q35] "v"(qf[35])
+#define MLA_ASM_KEYS [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [bk] "s"(bk)
+#define MLA_ASM_VALUES \
+  [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [bv] "s"(bv), [bp] "s"(bp)
+#define MLA_ASM_SOFTMAX_STATE [mref] "+v"(m_ref), [mseen] "+v"(m_seen), [lrun] "+v"(l_run), [exc] "+v"(excess)
+#define MLA_ASM_SOFTMAX_IN [scale] "s"(p.scale_log2), [bpw] "s"(bpw), [vlim] "v"(vlim), [tok] "s"(tok), [pa] "v"(pa)
+#define MLA_ASM_COPY                                                                     \
+  [cb] "s"(cb), [cd] "s"(cd), [cl] "s"(cl), [k1152] "s"(kD * 2), [c0] "v"(cpk[0]),            \
+      [c1] "v"(cpk[1]), [c2] "v"(cpk[2]), [c3] "v"(cpk[3]), [c4] "v"(cpk[4])
+#define MLA_ASM_SCRATCH MLA_BF16_ASM_SCRATCH, "memory", "m0", "scc", "vcc"
+
+#include "decode_bf16_asm.inc"
+
+// Workgroups are dispatched to the eight XCDs round-robin by linear id.
+// Remap so that all gridDim.x workgroups of request b run on one XCD: they
+// read the same latent query rows, which that XCD's L2 then fetches once.
+// Requires gridDim.y (the batch) to be a multiple of 8.
+__device__ __forceinline__ void xcd_slot(int& b, int& unit) {
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int xcd = lin & 7, pos = lin >> 3;
+  b = xcd + 8 * (pos / gridDim.x);
+  unit = pos % gridDim.x;
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_bf16_pipe_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(1024))) char tiles_raw[kPipeBufs * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char pbuf_raw[2 * kPBytes];
+  MLA_LDS char* tiles = (MLA_LDS char*)tiles_raw;
+  MLA_LDS char* pbuf = (MLA_LDS char*)pbuf_raw;
+  const uint32_t tiles_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles));
+  const uint32_t pbuf_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(pbuf));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5;
+  int b = blockIdx.y, unit = blockIdx.x;
+  if (p.xcd_group) xcd_slot(b, unit);
+  const int rg = unit % p.row_groups;
+  const int split = unit / p.row_groups;
+
+  const MLA_CONST int32_t* block_table = (const MLA_CONST int32_t*)(p.block_table);
+  int T = ((const MLA_CONST int32_t*)(p.seq_lens))[b];
+  T = T < 0 ? 0 : (T > p.max_seq_len ? p.max_seq_len : T);
+  const int j0 = split * p.split_tokens;
+  const bool direct = p.num_splits == 1;
+  if (!direct && j0 >= T) return;  // empty chunk: the combine step skips it
+  const int j1 = min(j0 + p.split_tokens, T);
+  const int n_tiles = j1 > j0 ? (j1 - j0 + kTileT - 1) / kTileT : 0;
+
+  const int rows_per_req = p.q_len * p.n_h;
+  const int row0 = rg * 128 + wave * 32;
+  const int t_q = row0 / p.n_h;
+  const int h0 = row0 % p.n_h;
+  const int n_tok = b * p.q_len + t_q;
+  const int vis_end = T - p.q_len + t_q + 1;
+  const int my_h = h0 + (lane & 31);
+
+  // per-lane LDS byte offsets of the key fragments (chunk 2s + hf of row
+  // tq, four offsets cycling with s) and of the transposed value fragments
+  // of column tile 4*wave ([h2][column parity]; column tile 4*wave + j adds
+  // (j >> 1) * 128 B and the second 16-token k-step 16 rows = 18432 B)
+  const int tq = lane & 31;
+  const int fq = swz(tq);
+  int ka[4], va[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ka[q] = (tq * kChunks + (((2 * q) | hf) ^ fq)) * 16;
+  {
+    const int L = lane & 15, cg = (lane >> 4) & 1;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int row = 8 * h2 + 4 * hf + (L >> 2);
+      const int f = swz(row);
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int x = 4 * par + 2 * cg + ((L & 3) >> 1);
+        va[2 * h2 + par] = (row * kChunks + (x ^ f)) * 16 + 8 * (L & 1) + 256 * wave;
+      }
+    }
+  }
+
+  // Copy ii of this wave moves wave-wide load i = wave + 4*ii of a tile:
+  // lane -> (row t, swizzled 16-byte chunk c), packed as c*16 | t << 11 in
+  // the low (even ii) or high (odd ii) half of cpk[ii / 2].
+  uint32_t cpk[(kPipeCopies + 1) / 2] = {};
+#pragma unroll
+  for (int ii = 0; ii < kPipeCopies; ++ii) {
+    const int slot = 64 * (wave + 4 * ii) + lane;
+    const int t = slot / kChunks;
+    const int c = (slot - t * kChunks) ^ swz(t);
+    cpk[ii / 2] |= (static_cast<uint32_t>(c * 16) | (static_cast<uint32_t>(t) << 11)) << (16 * (ii & 1));
+  }
+  const int64_t bt_row = static_cast<int64_t>(b) * p.max_blocks;
+  // block-table entry of tile k, and the first cache row of tile k given it
+  auto block_of = [&](int k) { return block_table[bt_row + (j0 + k * kTileT) / p.block_size]; };
+  auto base_from = [&](int blk, int k) -> const char* {
+    const int tok0 = j0 + k * kTileT;
+    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+    return reinterpret_cast<const char*>(p.cache + (static_cast<int64_t>(blk) * p.block_size + tok0 % p.block_size) * kD);
+  };
+  auto tile_base = [&](int k) { return base_from(block_of(k), k); };
+  auto last_row = [&](int k) { return min(kTileT, T - (j0 + k * kTileT)) - 1; };
+  auto issue_tile = [&](int k) {
+    const char* base = tile_base(k);
+    const uint32_t last = static_cast<uint32_t>(last_row(k));
+    const uint32_t dst = tiles_addr + (k & (kPipeBufs - 1)) * kTileBytes;
+#pragma unroll
+    for (int ii = 0; ii < kPipeCopies; ++ii) {
+      const uint32_t pk = cpk[ii / 2] >> (16 * (ii & 1));
+      const uint32_t t = min((pk >> 11) & 31u, last);  // rows past the end repeat a valid row
+      dma16_sv(base, t * (kD * 2) + (pk & 2047u), dst + (wave + 4 * ii) * 1024);
+    }
+  };
+  auto buf_addr = [&](int k) { return tiles_addr + (k & (kPipeBufs - 1)) * kTileBytes; };
+  auto pbuf_addr_of = [&](int k) { return pbuf_addr + (k & 1) * kPBytes; };
+  const uint32_t pa = 16 * lane;
+
+  constexpr float kSlack = 64.f;
+  f32x16_t oacc[16];
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+  float excess = -INFINITY;  // largest tile maximum minus m_ref seen in this pass
+  // token t of tile k is visible iff 8(r/4) + r%4 < vlim - 32k (register r)
+  const int vlim = vis_end - j0 - 4 * hf;
+
+  // The query loads need no table lookup, so they go out first; tiles 0 and
+  // 1 follow and their fetch overlaps the query loads.
+  bf16x8_t qf[36];
+  {
+    const __bf16* qrow = p.q_lat + (static_cast<int64_t>(n_tok) * p.n_h + my_h) * kD + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 36; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s);
+  }
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
+  wait_vmcnt<0>();
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  auto run_pass = [&]() -> bool {
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) oacc[ct] = f32x16_t{};
+    l_run = 0.f;
+    excess = -INFINITY;
+    if (n_tiles == 0) return false;
+    if (n_tiles > 2) issue_tile(2);
+    __builtin_amdgcn_s_barrier();  // tiles 0 and 1 visible to all waves
+    {  // scores and numerators of tile 0
+      const uint32_t bk = buf_addr(0);
+      const uint32_t bpw = pbuf_addr_of(0) + wave * 2048;
+      const int tok = 0;
+      asm volatile(MLA_BF16_FIRST
+                   : MLA_ASM_SOFTMAX_STATE
+                   : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_SOFTMAX_IN
+                   : MLA_ASM_SCRATCH);
+    }
+    int k = 0;
+    // Steps that also copy tile k+3.  Their scored tile k+1 ends at least 32
+    // tokens before the sequence end, so with q_len <= 32 all of it is
+    // visible and the stream skips the mask.
+    // Copy sources are looked up ahead: the block-table entry of tile k+5 is
+    // read in step k and turned into an address in step k+1, so no step
+    // waits for a table read.
+    const char* cb_next = n_tiles > 3 ? tile_base(3) : nullptr;
+    int blk_next = n_tiles > 4 ? block_of(4) : 0;
+    for (; k + 3 < n_tiles; ++k) {
+      const char* cb = cb_next;
+      wait_vmcnt<kPipeCopies>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's P^T of tile k written
+      __builtin_amdgcn_s_barrier();  // tile k+1 and P^T of tile k visible; tile k-1 released
+      const int cl = last_row(k + 3);
+      const uint32_t cd = buf_addr(k + 3) + wave * 1024;
+      const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k), bp = pbuf_addr_of(k);
+      const uint32_t bpw = pbuf_addr_of(k + 1) + wave * 2048;
+      const int tok = 32 * (k + 1);
+      asm volatile(MLA_BF16_STEP_COPY
+                   : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                   : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN, MLA_ASM_COPY
+                   : MLA_ASM_SCRATCH);
+      if (k + 4 < n_tiles) cb_next = base_from(blk_next, k + 4);
+      if (k + 5 < n_tiles) blk_next = block_of(k + 5);
+    }
+    for (; k + 1 < n_tiles; ++k) {
+      if (k + 2 < n_tiles) wait_vmcnt<kPipeCopies>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k), bp = pbuf_addr_of(k);
+      const uint32_t bpw = pbuf_addr_of(k + 1) + wave * 2048;
+      const int tok = 32 * (k + 1);
+      asm volatile(MLA_BF16_STEP_MASKED
+                   : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                   : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN
+                   : MLA_ASM_SCRATCH);
+    }
+    {  // weighted sum of the last tile (its keys were scored in the last step)
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();  // P^T of the last tile visible
+      const uint32_t bv = buf_addr(k), bp = pbuf_addr_of(k);
+      asm volatile(MLA_BF16_PV_ONLY : MLA_ASM_ACC : MLA_ASM_VALUES, [pa] "v"(pa) : MLA_ASM_SCRATCH);
+    }
+    return excess > kSlack;
+  };
+#pragma clang diagnostic pop
+
+  // Cross-wave words (second-pass flag, per-head 1/l) live in tile buffer 0,
+  // which no wave reads once every wave has passed the barrier below.
+  MLA_LDS int* xflag = reinterpret_cast<MLA_LDS int*>(tiles);
+  MLA_LDS float* xinv = reinterpret_cast<MLA_LDS float*>(tiles) + 64;
+  const bool flagged = run_pass();
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  {
+    const int f = __builtin_amdgcn_ballot_w64(flagged) != 0;
+    if (lane == 0) xflag[wave] = f;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  const bool second_pass = (xflag[0] | xflag[1] | xflag[2] | xflag[3]) != 0;
+  if (second_pass) {
+    __builtin_amdgcn_s_barrier();  // every wave has read the flags
+    m_ref = m_seen;
+    if (n_tiles > 0) issue_tile(0);
+    if (n_tiles > 1) issue_tile(1);
+    wait_vmcnt<0>();
+    run_pass();
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  // the softmax wave of each head publishes 1/l; lse is written by it too
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+  if (hf == 0) xinv[wave * 32 + lane] = inv;
+  const int my_row = row0 + (lane & 31);
+  if (direct) {
+    if (p.lse != nullptr && hf == 0) p.lse[static_cast<int64_t>(n_tok) * p.n_h + my_h] = lse_v;
+  } else {
+    const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
+    if (hf == 0) p.lse_part[pr] = lse_v;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  // This wave holds O^T for columns 128*wave.. of head group g in oacc[4j + g].
+  // The normalised rows are staged in LDS (32 KB per wave, 256 B per head,
+  // 16-byte chunk c of head h at c ^ (h & 15)) and then stored as whole
+  // 256-byte row segments, four heads per store instruction.
+  MLA_LDS char* stage = tiles + 1024 + wave * 32768;  // clear of the exchange words
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const float ginv = xinv[g * 32 + (lane & 31)];
+    const int h = g * 32 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4_t v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[4 * j + g][4 * jj + i] * ginv);
+        *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + h * 256 + (((4 * j + jj) ^ (h & 15)) * 16) + 8 * hf) = v;
+      }
+  }
+  const int hrow0 = rg * 128;  // first row (query t_q, head h0 of wave 0) of this row group
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int h = 4 * it + (lane >> 4), c = lane & 15;
+    const bf16x8_t v = *reinterpret_cast<MLA_LDS const bf16x8_t*>(stage + h * 256 + ((c ^ (h & 15)) * 16));
+    const int row = hrow0 + h;
+    __bf16* orow;
+    if (direct) {
+      orow = p.o_lat + (static_cast<int64_t>(b * p.q_len + row / p.n_h) * p.n_h + row % p.n_h) * kDc;
+    } else {
+      orow = p.o_part + ((static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + row) * kDc;
+    }
+    *reinterpret_cast<bf16x8_t*>(orow + 128 * wave + 8 * c) = v;
+  }
+}
+
 // Merge the chunk partials of one row: L = log sum_s exp(lse_s),
 // o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).  The lse of up
 // to 64 splits is read lane-parallel, and the partial rows of each batch of 8
@@ -385,8 +703,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   const int waves = decode_waves_per_group(a.n_h, a.q_len);
   p.row_groups = a.q_len * a.n_h / (32 * waves);
+  const bool pipe = waves == 4 && a.q_len <= 32;
+  p.xcd_group = pipe && a.batch % 8 == 0;
   const dim3 grid(a.num_splits * p.row_groups, a.batch);
-  if (waves == 4)
+  if (pipe)
+    hipLaunchKernelGGL(decode_bf16_pipe_kernel, grid, dim3(256), 0, st, p);
+  else if (waves == 4)
     hipLaunchKernelGGL((decode_bf16_kernel<4, 3>), grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((decode_bf16_kernel<2, 2>), grid, dim3(128), 0, st, p);

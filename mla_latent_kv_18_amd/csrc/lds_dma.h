@@ -28,6 +28,13 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
+// The same 16-byte copy addressed as a uniform 64-bit base plus a per-lane
+// 32-bit byte offset (one VGPR per copy instead of a 64-bit address pair).
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
