@@ -448,13 +448,33 @@ decode_bf16_pipe_kernel(DecodeParams p) {
   // token t of tile k is visible iff 8(r/4) + r%4 < vlim - 32k (register r)
   const int vlim = vis_end - j0 - 4 * hf;
 
-  // The query loads need no table lookup, so they go out first; tiles 0 and
-  // 1 follow and their fetch overlaps the query loads.
+  // Latent queries.  The workgroup's 128 rows are contiguous in q_lat; they
+  // are copied with whole-kilobyte loads into the four tile buffers (32 rows
+  // each, in the tile layout) and each wave then reads its 36 fragments with
+  // the key-fragment addressing.  Loading them straight into registers would
+  // take one 32-byte piece from each of 32 rows per load instruction.
   bf16x8_t qf[36];
   {
-    const __bf16* qrow = p.q_lat + (static_cast<int64_t>(n_tok) * p.n_h + my_h) * kD + 8 * hf;
+    const char* qblk = reinterpret_cast<const char*>(p.q_lat + (static_cast<int64_t>(b) * rows_per_req + rg * 128) * kD);
 #pragma unroll
-    for (int s = 0; s < 36; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s);
+    for (int w = 0; w < 4; ++w) {
+      const char* base = qblk + w * kTileBytes;
+      const uint32_t dst = tiles_addr + w * kTileBytes;
+#pragma unroll
+      for (int ii = 0; ii < kPipeCopies; ++ii) {
+        const uint32_t pk = cpk[ii / 2] >> (16 * (ii & 1));
+        dma16_sv(base, ((pk >> 11) & 31u) * (kD * 2) + (pk & 2047u), dst + (wave + 4 * ii) * 1024);
+      }
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    MLA_LDS const char* qb = tiles + wave * kTileBytes;
+#pragma unroll
+    for (int s = 0; s < 36; ++s)
+      qf[s] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(qb + ka[s & 3] + 128 * (s >> 2));
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+    __builtin_amdgcn_s_barrier();        // every wave done with the buffers
   }
   if (n_tiles > 0) issue_tile(0);
   if (n_tiles > 1) issue_tile(1);
