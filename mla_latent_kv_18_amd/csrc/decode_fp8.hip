@@ -356,6 +356,251 @@ decode_fp8_kernel(Fp8Params p) {
   if (lrow != nullptr && hf == 0) *lrow = lse_v;
 }
 
+// Software-pipelined form for workgroups of four waves (128 rows of one
+// query position), with q_len <= 32.  Step k of a wave is one instruction
+// stream (decode_fp8_asm.inc, generated by gen_decode_fp8_asm.py): the 36
+// score MFMAs of tile k+1 (two accumulators, hi and lo query terms), the 32
+// weighted-sum MFMAs of tile k, the softmax and two-term P' encoding of tile
+// k+1 between the last of them, and the wave's ten copies of tile k+2.  The
+// P' codes of a tile go to a private LDS area of the wave and are read back
+// by the next step.  Tiles use the 16-row-group layout described in the
+// generator, so that each direct copy reads 16 rows x 64 contiguous bytes.
+// LDS: three tile buffers (tile k values, tile k+1 keys, tile k+2 landing)
+// and four 5 KB P' areas.
+constexpr int kF8Bufs = 3;
+constexpr int kF8BufBytes = kTileBytes + 256;  // tile + its 64 token scales
+constexpr int kF8PBytes = 5120;                // hi/lo codes + scales, per wave
+constexpr int kF8Copies = kLoadsPerTile / 4;   // 9 per wave per tile
+
+#include "decode_fp8_asm.inc"
+
+#define MLA_F8_ACC                                                                           \
+  [o0] "+a"(oacc[0]), [o1] "+a"(oacc[1]), [o2] "+a"(oacc[2]), [o3] "+a"(oacc[3]),            \
+      [o4] "+a"(oacc[4]), [o5] "+a"(oacc[5]), [o6] "+a"(oacc[6]), [o7] "+a"(oacc[7]),        \
+      [o8] "+a"(oacc[8]), [o9] "+a"(oacc[9]), [o10] "+a"(oacc[10]), [o11] "+a"(oacc[11]),    \
+      [o12] "+a"(oacc[12]), [o13] "+a"(oacc[13]), [o14] "+a"(oacc[14]), [o15] "+a"(oacc[15])
+#define MLA_F8_Q                                                                             \
+  [qh0] "v"(qf[0]), [qh1] "v"(qf[1]), [qh2] "v"(qf[2]), [qh3] "v"(qf[3]), [qh4] "v"(qf[4]),  \
+      [qh5] "v"(qf[5]), [qh6] "v"(qf[6]), [qh7] "v"(qf[7]), [qh8] "v"(qf[8]),                \
+      [ql0] "v"(ql[0]), [ql1] "v"(ql[1]), [ql2] "v"(ql[2]), [ql3] "v"(ql[3]),                \
+      [ql4] "v"(ql[4]), [ql5] "v"(ql[5]), [ql6] "v"(ql[6]), [ql7] "v"(ql[7]), [ql8] "v"(ql[8])
+#define MLA_F8_KEYS [ka0] "v"(qk_off[0]), [ka1] "v"(qk_off[1]), [bk] "s"(bk)
+#define MLA_F8_VALUES [vo] "v"(pv_off), [bv] "s"(bv)
+#define MLA_F8_COMMON [pa] "v"(pa), [pw] "s"(pw)
+#define MLA_F8_STATE [mref] "+v"(m_ref), [mseen] "+v"(m_seen), [lrun] "+v"(l_run), [exc] "+v"(excess)
+#define MLA_F8_SOFTMAX_IN \
+  [qmul] "v"(qmul), [vlim] "v"(vlim), [tok] "s"(tok), [bks] "s"(bk + kTileBytes), [domask] "s"(domask)
+#define MLA_F8_COPY                                                                          \
+  [cb] "s"(cb), [cd] "s"(cd), [cl] "s"(cl), [csb] "s"(csb), [csd] "s"(csd), [k576] "s"(kD),  \
+      [rl] "v"(crow), [q16] "v"(ccol), [r0] "s"(cR[0]), [r1] "s"(cR[1]), [r2] "s"(cR[2]),    \
+      [r3] "s"(cR[3]), [r4] "s"(cR[4]), [r5] "s"(cR[5]), [r6] "s"(cR[6]), [r7] "s"(cR[7]),   \
+      [r8] "s"(cR[8]), [k0] "s"(cC[0]), [k1] "s"(cC[1]), [k2] "s"(cC[2]), [k3] "s"(cC[3]),   \
+      [k4] "s"(cC[4]), [k5] "s"(cC[5]), [k6] "s"(cC[6]), [k7] "s"(cC[7]), [k8] "s"(cC[8]),    \
+      [docopy] "s"(docopy)
+#define MLA_F8_SCRATCH MLA_FP8_ASM_SCRATCH, "memory", "m0", "scc", "vcc"
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_fp8_pipe_kernel(Fp8Params p) {
+  __shared__ __attribute__((aligned(1024))) char tiles_raw[kF8Bufs * kF8BufBytes];
+  __shared__ __attribute__((aligned(1024))) char pbuf_raw[4 * kF8PBytes];
+  MLA_LDS char* tiles = (MLA_LDS char*)tiles_raw;
+  const uint32_t tiles_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles));
+  const uint32_t pbuf_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MLA_LDS char*)pbuf_raw));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5;
+  const int b = blockIdx.y;
+  int split, rg;
+  if (p.xcd_pack) {
+    const int x8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
+    rg = rest % p.row_groups;
+    split = (rest / p.row_groups) * 8 + x8;
+  } else {
+    rg = blockIdx.x % p.row_groups;
+    split = blockIdx.x / p.row_groups;
+  }
+  if (split >= p.num_splits) return;
+
+  const MLA_CONST int32_t* block_table = (const MLA_CONST int32_t*)(p.block_table);
+  int T = ((const MLA_CONST int32_t*)(p.seq_lens))[b];
+  T = T < 0 ? 0 : (T > p.max_seq_len ? p.max_seq_len : T);
+  const int j0 = split * p.split_tokens;
+  const bool direct = p.num_splits == 1;
+  if (!direct && j0 >= T) return;
+  const int j1 = min(j0 + p.split_tokens, T);
+  const int n_tiles = j1 > j0 ? (j1 - j0 + kTileT - 1) / kTileT : 0;
+
+  const int rows_per_req = p.q_len * p.n_h;
+  const int row0 = rg * 128 + wave * 32;
+  const int t_q = row0 / p.n_h;
+  const int h0 = row0 % p.n_h;
+  const int n_tok = b * p.q_len + t_q;
+  const int vis_end = T - p.q_len + t_q + 1;
+  const int my_h = h0 + (lane & 31);
+
+  // latent query codes of this wave's heads: Q[h, 64s + 32hf .. +32]
+  i32x8_t qf[9], ql[9];
+  float qmul;
+  {
+    const int64_t qrow = static_cast<int64_t>(n_tok) * p.n_h + my_h;
+    const uint8_t* q = p.q_lat + qrow * (2 * kD) + 32 * hf;
+#pragma unroll
+    for (int s = 0; s < 9; ++s) {
+      qf[s] = *reinterpret_cast<const i32x8_t*>(q + 64 * s);
+      ql[s] = *reinterpret_cast<const i32x8_t*>(q + kD + 64 * s);
+    }
+    qmul = p.q_scale[qrow] * p.scale_log2;
+  }
+
+  // per-lane LDS byte offsets in the 16-row-group tile layout
+  const int tq = lane & 31;
+  int qk_off[2];  // chunk 4s + 2hf + x of row tq + 32 beta: + 1024 s + 18432 beta
+#pragma unroll
+  for (int x = 0; x < 2; ++x) qk_off[x] = 16 * (576 * (tq >> 4) + 16 * (2 * hf + x) + ((tq & 15) ^ (4 * x)));
+  const int cg = (lane >> 4) & 1, li = lane & 15, kp = li >> 1, pb = li & 1;
+  const int pv_row = 8 * (kp >> 2) + 4 * hf + (kp & 3);
+  const int pv_off = 16 * (16 * cg + (pv_row ^ (4 * cg))) + 8 * pb;  // + 512 ct + 9216 j
+  const uint32_t pa = 16 * lane;
+  const uint32_t pw = pbuf_addr + wave * kF8PBytes;
+
+  // Copy ii of this wave fills slots 64i.. of a tile, i = wave + 4ii: row
+  // cR[ii] + crow (16-row group i / 9, lane's row in it), byte column
+  // cC[ii] + ccol (chunks 4(i % 9) + lane / 16).
+  const uint32_t crow = (lane & 15) ^ (4 * ((lane >> 4) & 1));
+  const uint32_t ccol = 16 * (lane >> 4);
+  uint32_t cR[kF8Copies], cC[kF8Copies];
+#pragma unroll
+  for (int ii = 0; ii < kF8Copies; ++ii) {
+    const int i = wave + 4 * ii;
+    cR[ii] = 16 * (i / 9);
+    cC[ii] = 64 * (i % 9);
+  }
+  const int64_t bt_row = static_cast<int64_t>(b) * p.max_blocks;
+  auto first_row = [&](int k) -> int64_t {  // cache slot of tile k's first token
+    const int tok0 = j0 + k * kTileT;
+    int blk = block_table[bt_row + tok0 / p.block_size];
+    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+    return static_cast<int64_t>(blk) * p.block_size + tok0 % p.block_size;
+  };
+  auto last_row = [&](int k) { return min(kTileT, T - (j0 + k * kTileT)) - 1; };
+  auto buf_addr = [&](int k) { return tiles_addr + (k % kF8Bufs) * kF8BufBytes; };
+  auto issue_tile = [&](int k) {
+    const int64_t first = first_row(k);
+    const uint8_t* rows = p.cache + first * kD;
+    const uint32_t last = static_cast<uint32_t>(last_row(k));
+    const uint32_t dst = buf_addr(k);
+#pragma unroll
+    for (int ii = 0; ii < kF8Copies; ++ii)  // rows past the end repeat a valid row
+      dma16_sv(rows, min(cR[ii] + crow, last) * kD + cC[ii] + ccol, dst + (wave + 4 * ii) * 1024);
+    dma4(p.cache_scale + first + min(static_cast<uint32_t>(lane), last), dst + kTileBytes);
+  };
+
+  constexpr float kSlack = 64.f;
+  f32x16_t oacc[16];
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f, excess = -INFINITY;
+  const int vlim = vis_end - j0 - 4 * hf;  // token t of tile k visible iff t < vlim - 64k
+
+  if (n_tiles > 0) issue_tile(0);
+  if (n_tiles > 1) issue_tile(1);
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  auto run_pass = [&]() -> bool {
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) oacc[ct] = f32x16_t{};
+    l_run = 0.f;
+    excess = -INFINITY;
+    if (n_tiles == 0) return false;
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // tiles 0 and 1 visible to all waves
+    {
+      const uint32_t bk = buf_addr(0);
+      const int tok = 0, domask = 1;
+      asm volatile(MLA_FP8_FIRST
+                   : MLA_F8_STATE
+                   : MLA_F8_Q, MLA_F8_KEYS, MLA_F8_COMMON, MLA_F8_SOFTMAX_IN
+                   : MLA_F8_SCRATCH);
+    }
+    for (int k = 0; k + 1 < n_tiles; ++k) {
+      wait_vmcnt<0>();                      // tile k+1 landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();        // tile k+1 visible; tile k-1 released by all waves
+      const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k);
+      const int tok = kTileT * (k + 1);
+      // Tile k+2 is copied while it exists.  The scored tile k+1 needs the
+      // mask only near the chunk's end: a tile that ends 64 tokens before
+      // the last one is visible in full for q_len <= 32.
+      // The two guards are counts (zero = off) rather than booleans, so that
+      // they stay scalar: a widened boolean lands in a vector register.
+      const bool copying = k + 2 < n_tiles;
+      const int docopy = max(n_tiles - k - 2, 0);
+      const int domask = max(k + 4 - n_tiles, 0);
+      const int64_t first = copying ? first_row(k + 2) : 0;
+      const uint8_t* cb = p.cache + first * kD;
+      const float* csb = p.cache_scale + first;
+      const int cl = copying ? last_row(k + 2) : 0;
+      const uint32_t cd = buf_addr(k + 2) + wave * 1024;
+      const uint32_t csd = buf_addr(k + 2) + kTileBytes;
+      asm volatile(MLA_FP8_STEP
+                   : MLA_F8_ACC, MLA_F8_STATE
+                   : MLA_F8_Q, MLA_F8_KEYS, MLA_F8_VALUES, MLA_F8_COMMON, MLA_F8_SOFTMAX_IN, MLA_F8_COPY
+                   : MLA_F8_SCRATCH);
+    }
+    {  // weighted sum of the last tile (its codes are in this wave's P' area)
+      const uint32_t bv = buf_addr(n_tiles - 1);
+      asm volatile(MLA_FP8_PV_ONLY : MLA_F8_ACC : MLA_F8_VALUES, MLA_F8_COMMON : MLA_F8_SCRATCH);
+    }
+    return excess > kSlack;
+  };
+#pragma clang diagnostic pop
+
+  // Second-pass flags live in tile buffer 0, free once every wave is past the barrier.
+  MLA_LDS int* xflag = reinterpret_cast<MLA_LDS int*>(tiles);
+  const bool flagged = run_pass();
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  {
+    const int f = __builtin_amdgcn_ballot_w64(flagged) != 0;
+    if (lane == 0) xflag[wave] = f;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  const bool second_pass = (xflag[0] | xflag[1] | xflag[2] | xflag[3]) != 0;
+  if (second_pass) {
+    __builtin_amdgcn_s_barrier();  // every wave has read the flags
+    m_ref = m_seen;
+    if (n_tiles > 0) issue_tile(0);
+    if (n_tiles > 1) issue_tile(1);
+    run_pass();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+  const int my_row = row0 + (lane & 31);
+  __bf16* orow;
+  float* lrow;
+  if (direct) {
+    orow = p.o_lat + (static_cast<int64_t>(n_tok) * p.n_h + my_h) * kDc;
+    lrow = p.lse != nullptr ? p.lse + static_cast<int64_t>(n_tok) * p.n_h + my_h : nullptr;
+  } else {
+    const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
+    orow = p.o_part + pr * kDc;
+    lrow = p.lse_part + pr;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      bf16x4_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[ct][4 * j + i] * inv);
+      *reinterpret_cast<bf16x4_t*>(orow + 32 * ct + 8 * j + 4 * hf) = v;
+    }
+  if (lrow != nullptr && hf == 0) *lrow = lse_v;
+}
+
 }  // namespace
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t st) {
@@ -385,7 +630,9 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t st) {
   p.xcd_pack = a.num_splits > 1 && p.row_groups > 1;
   const int grid_splits = p.xcd_pack ? (a.num_splits + 7) / 8 * 8 : a.num_splits;
   const dim3 grid(grid_splits * p.row_groups, a.batch);
-  if (waves == 4)
+  if (waves == 4 && a.q_len <= 32)
+    hipLaunchKernelGGL(decode_fp8_pipe_kernel, grid, dim3(256), 0, st, p);
+  else if (waves == 4)
     hipLaunchKernelGGL((decode_fp8_kernel<4, 3>), grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((decode_fp8_kernel<2, 2>), grid, dim3(128), 0, st, p);

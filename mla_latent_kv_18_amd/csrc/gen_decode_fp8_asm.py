@@ -1,0 +1,424 @@
+"""Writes decode_fp8_asm.inc: the instruction streams of the fp8 latent
+decode kernel's software-pipelined tile step (decode_fp8.hip).
+
+    python gen_decode_fp8_asm.py > decode_fp8_asm.inc
+
+A workgroup has four waves; wave w owns 32 heads of one query position.
+Tiles are 64 tokens of e4m3 cache rows (one K-step of the fp8 MFMA for the
+weighted sum) plus their 64 fp32 token scales.  Step k of a wave:
+
+  scores   S^T = K Q^T for tile k+1: 9 K-steps of 64 latent dims, two
+           32-token blocks (beta), hi and lo query planes: 36 MFMAs
+           (v_mfma_scale_f32_32x32x64_f8f6f4) into two accumulators
+  softmax  s = S * kscale[t] * qscale[h] * scale * log2(e); p = 2^(s - m_ref);
+           the value-side weight P' = p * kscale[t] is split into two e4m3
+           terms with a power-of-two scale per (head, 32-token block); the
+           codes and scales go to this wave's private LDS area
+  sum      O^T += V^T P'^T for tile k: 16 column tiles x (hi, lo) = 32 MFMAs
+           whose B operand (the codes of tile k) was read back at the start
+
+MFMA order: per K-step [score A hi, score B hi, score A lo, score B lo, sum],
+then the remaining 23 sum MFMAs with the softmax work between them; the
+encoding of P' follows the last sum MFMA (it reuses that MFMA's registers).
+
+Tile layout in LDS (16-row groups): 16-byte chunk c of row t at slot
+576(t >> 4) + 16c + ((t & 15) ^ 4(c & 1)); the 64 token scales follow at
+byte 36864.  Wave-wide copy i (0..35) fills slots 64i..64i+63.
+
+Operands (named in the kernel):
+  %[o0]..%[o15]   O^T accumulators, one per 32 latent columns
+  %[qh0..8], %[ql0..8]  hi and lo latent query codes, 64 dims per K-step
+  %[ka0], %[ka1]  per-lane key byte offsets (chunk parity 0 / 1)
+  %[vo]           per-lane transposed value byte offset
+  %[pa]           16 * lane
+  %[bk], %[bv]    LDS byte address of the scored tile and of the summed tile
+  %[pw]           LDS byte address of this wave's P' area (5120 B: codes at
+                  16*lane + 1024*part, scales at 4096 + 16*lane)
+  %[qmul]         per-head qscale * softmax scale * log2(e)
+  %[mref], %[mseen], %[lrun], %[exc]  per-head softmax state (in/out)
+  %[vlim], %[tok], %[domask]  token t (0..63) of the scored tile is visible
+                  iff t < vlim - tok; the mask is applied when domask != 0
+  %[docopy]       the step copies a tile when non-zero
+  %[cb], %[cd], %[cl], %[csb], %[csd], %[k576], %[rl], %[q16], %[r0..8],
+  %[k0..8]        the tile copy (see Stream.copy)
+The streams use v167-v255, vcc, m0 and scc as scratch.
+"""
+import sys
+
+FIRST_SCRATCH = 167
+T1 = 167                              # temporaries (copy offsets while copying)
+S127, S123 = 168, 169                 # E8M0 scale constants 2^0, 2^-4
+KA = [170, 171]                       # key read addresses (chunk parity)
+VA = 172                              # value read address
+T0 = 173
+MYS, MYSL = 174, 175                  # E8M0 scales of the P' codes (hi, lo)
+PH, PL = 176, 184                     # P' codes being summed (8 VGPRs each)
+KF = [192, 200]                       # key operand slots (8 VGPRs each)
+VF = [208, 216]                       # value operand slots (8 VGPRs each)
+SA, SB = 224, 240                     # score accumulators (beta 0, 1)
+KS = list(range(192, 208))            # token scales, in the key slots once scores are done
+SCA = KA[0]                           # token-scale read address (keys are done by then)
+PAD = KA[1]                           # P' area address when the codes are written
+PAD0 = SA                             # P' area address when they are read (before any score)
+CT, CO = T0, T1                       # copy temporaries
+NEG_INF = "0xff800000"
+
+
+def vr(base, n=8):
+    return f"v[{base}:{base + n - 1}]"
+
+
+class Stream:
+    def __init__(self):
+        self.lines = []
+        self.issued = []
+        self.done = 0
+
+    def emit(self, s):
+        self.lines.append(s)
+
+    def lds(self, tag, text):
+        self.issued.append(tag)
+        self.emit(text)
+
+    def wait_for(self, tag):
+        last = max(i for i, t in enumerate(self.issued) if t == tag)
+        if last < self.done:
+            return
+        n = min(len(self.issued) - (last + 1), 15)
+        self.emit(f"s_waitcnt lgkmcnt({n})")
+        self.done = len(self.issued) - n
+
+    def wait_all(self):
+        if self.done < len(self.issued):
+            self.emit("s_waitcnt lgkmcnt(0)")
+            self.done = len(self.issued)
+
+    # ---- LDS reads
+    def kread(self, s, beta, slot):
+        # key operand of K-step s, block beta: chunks 4s + 2hf + {0, 1} of row tq + 32 beta
+        off = 18432 * beta + 1024 * s
+        base = KF[slot]
+        self.lds(("k", s, beta), f"ds_read_b128 {vr(base, 4)}, v{KA[0]} offset:{off}")
+        self.lds(("k", s, beta), f"ds_read_b128 {vr(base + 4, 4)}, v{KA[1]} offset:{off}")
+
+    def vread(self, ct, slot):
+        base = VF[slot]
+        for j in range(4):
+            self.lds(("v", ct), f"ds_read_b64_tr_b8 {vr(base + 2 * j, 2)}, v{VA} offset:{512 * ct + 9216 * j}")
+
+    def kscales(self, beta):
+        for a4 in range(4):
+            self.lds(("ks", beta), f"ds_read_b128 {vr(KS[4 * a4], 4)}, v{SCA} offset:{128 * beta + 32 * a4}")
+
+    def pcodes(self):
+        # P' codes of the tile being summed: hi dwords 0-3 / 4-7, lo dwords 0-3 / 4-7, scales
+        self.emit(f"v_add_u32 v{PAD0}, %[pw], %[pa]")
+        self.lds(("p",), f"ds_read_b128 {vr(PH, 4)}, v{PAD0} offset:0")
+        self.lds(("p",), f"ds_read_b128 {vr(PH + 4, 4)}, v{PAD0} offset:1024")
+        self.lds(("p",), f"ds_read_b128 {vr(PL, 4)}, v{PAD0} offset:2048")
+        self.lds(("p",), f"ds_read_b128 {vr(PL + 4, 4)}, v{PAD0} offset:3072")
+        self.lds(("p",), f"ds_read_b64 v[{MYS}:{MYSL}], v{PAD0} offset:4096")
+
+    # ---- MFMAs
+    def qk(self, s, beta, lo, slot):
+        self.wait_for(("k", s, beta))
+        acc = SA if beta == 0 else SB
+        c = "0" if (s == 0 and not lo) else vr(acc, 16)
+        q = f"%[ql{s}]" if lo else f"%[qh{s}]"
+        sb = S123 if lo else S127
+        self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 {vr(acc, 16)}, {vr(KF[slot])}, {q}, {c}, "
+                  f"v{S127}, v{sb} op_sel_hi:[0,0,0]")
+
+    def pv(self, i, vslot_of):
+        # MFMA i: column-tile pair i // 4, (ct, hi), (ct+1, hi), (ct, lo), (ct+1, lo)
+        pair, r = i >> 2, i & 3
+        ct = 2 * pair + (r & 1)
+        lo = r >= 2
+        self.wait_for(("v", ct))
+        self.wait_for(("p",))
+        p, sc = (PL, MYSL) if lo else (PH, MYS)
+        self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{ct}], {vr(VF[vslot_of[ct]])}, {vr(p)}, %[o{ct}], "
+                  f"v{S127}, v{sc} op_sel_hi:[0,0,0]")
+
+    def copy(self, ii):
+        # copy ii of the wave: tile row %[r{ii}] + the lane's row in its group
+        # (clamped to the tile's last valid row), byte column %[k{ii}] + the
+        # lane's 16-byte chunk; it lands 4096*ii bytes after the wave's first.
+        # Skipped when %[docopy] is 0 (no tile left to copy).
+        self.emit("s_cmp_lg_u32 %[docopy], 0")
+        self.emit(f"s_cbranch_scc0 .Lnc%=_{ii}")
+        self.emit(f"v_add_u32 v{CT}, %[r{ii}], %[rl]")
+        self.emit(f"v_min_u32 v{CT}, %[cl], v{CT}")
+        self.emit(f"v_mad_u32_u24 v{CO}, v{CT}, %[k576], %[q16]")
+        self.emit(f"v_add_u32 v{CO}, %[k{ii}], v{CO}")
+        self.emit(f"s_add_u32 m0, %[cd], {4096 * ii}")
+        self.emit(f"global_load_lds_dwordx4 v{CO}, %[cb]")
+        self.emit(f".Lnc%=_{ii}:")
+
+    def copy_scales(self):
+        self.emit("s_cmp_lg_u32 %[docopy], 0")
+        self.emit("s_cbranch_scc0 .Lncs%=")
+        self.emit(f"v_lshrrev_b32 v{CT}, 4, %[pa]")             # lane
+        self.emit(f"v_min_u32 v{CT}, %[cl], v{CT}")
+        self.emit(f"v_lshlrev_b32 v{CT}, 2, v{CT}")
+        self.emit("s_mov_b32 m0, %[csd]")
+        self.emit(f"global_load_lds_dword v{CT}, %[csb]")
+        self.emit(".Lncs%=:")
+
+    def text(self):
+        return "\n".join(self.lines)
+
+
+def setup(st, keys, values):
+    st.emit("s_nop 4")
+    st.emit(f"v_mov_b32 v{S127}, 0x7f")
+    st.emit(f"v_mov_b32 v{S123}, 0x7b")
+    if keys:
+        st.emit(f"v_add_u32 v{KA[0]}, %[bk], %[ka0]")
+        st.emit(f"v_add_u32 v{KA[1]}, %[bk], %[ka1]")
+    if values:
+        st.emit(f"v_add_u32 v{VA}, %[bv], %[vo]")
+
+
+def results_ready(st):
+    st.emit("s_nop 7")
+    st.emit("s_nop 7")
+    st.emit("s_nop 3")
+
+
+def softmax_ops(st, masked):
+    """VALU work on the two score accumulators up to the value-side weights
+    P' = p * kscale (in SA, SB) and their per-block maxima; list of groups of
+    instructions (LDS reads are issued through st so that waits are counted)."""
+    a = [SA + r for r in range(16)]
+    b = [SB + r for r in range(16)]
+    ks = KS
+    ops = []
+    # s = S * kscale * qmul, block by block (token scales of the scored tile)
+    ops.append(("lds", lambda: (st.emit(f"v_lshrrev_b32 v{T0}, 9, %[pa]"),
+                                st.emit(f"v_lshl_add_u32 v{SCA}, v{T0}, 4, %[bks]"),
+                                st.kscales(0))))
+    ops.append(("wait", ("ks", 0)))
+    for r in range(16):
+        ops.append([f"v_mul_f32 v{a[r]}, v{a[r]}, v{ks[r]}"])
+    ops.append(("lds", lambda: st.kscales(1)))
+    for r in range(16):
+        ops.append([f"v_mul_f32 v{a[r]}, %[qmul], v{a[r]}"])
+    ops.append(("wait", ("ks", 1)))
+    for r in range(16):
+        ops.append([f"v_mul_f32 v{b[r]}, v{b[r]}, v{ks[r]}", f"v_mul_f32 v{b[r]}, %[qmul], v{b[r]}"])
+    if masked:
+        # tokens past the visible end of the scored tile; skipped when %[domask] is 0
+        lim, neg = CT, CO
+        grp = ["s_cmp_lg_u32 %[domask], 0", "s_cbranch_scc0 .Lnm%=",
+               f"v_subrev_u32 v{lim}, %[tok], %[vlim]", f"v_mov_b32 v{neg}, {NEG_INF}"]
+        for beta, regs in ((0, a), (1, b)):
+            for r in range(16):
+                t = 32 * beta + 8 * (r >> 2) + (r & 3)
+                grp += [f"v_cmp_lt_i32 vcc, {t}, v{lim}", f"v_cndmask_b32 v{regs[r]}, v{neg}, v{regs[r]}, vcc"]
+        grp.append(".Lnm%=:")
+        ops.append(grp)
+    # row maximum over 32 tokens, then over the lane pair (l, l^32)
+    mx, t1, mu, ps = T0, T1, T1, T1       # (mx dies before mu is set, mu before ps)
+    vals = a + b
+    ops.append([f"v_max3_f32 v{mx}, v{vals[0]}, v{vals[1]}, v{vals[2]}"])
+    for i in range(3, 31, 2):
+        ops.append([f"v_max3_f32 v{mx}, v{mx}, v{vals[i]}, v{vals[i + 1]}"])
+    ops.append([f"v_max_f32 v{mx}, v{mx}, v{vals[31]}"])
+    ops.append([f"v_mov_b32 v{t1}, v{mx}", "s_nop 1",
+                f"v_permlane32_swap_b32 v{t1}, v{mx}", f"v_max_f32 v{mx}, v{t1}, v{mx}"])
+    ops.append([f"v_max_f32 %[mseen], %[mseen], v{mx}"])
+    ops.append([f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", f"v_cndmask_b32 %[mref], %[mref], v{mx}, vcc"])
+    ops.append([f"v_sub_f32 v{t1}, v{mx}, %[mref]", f"v_max_f32 %[exc], %[exc], v{t1}"])
+    ops.append([f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", f"v_cndmask_b32_e64 v{mu}, %[mref], 0, vcc"])
+    for r in range(32):
+        ops.append([f"v_sub_f32 v{vals[r]}, v{vals[r]}, v{mu}", f"v_exp_f32 v{vals[r]}, v{vals[r]}"])
+    ops.append([f"v_add_f32 v{ps}, v{vals[0]}, v{vals[1]}"])
+    for r in range(2, 32):
+        ops.append([f"v_add_f32 v{ps}, v{ps}, v{vals[r]}"])
+    ops.append([f"v_add_f32 %[lrun], %[lrun], v{ps}"])
+    # value-side weights P' = p * kscale and their block maxima (pmax0 in T0, pmax1 in T1)
+    ops.append(("lds", lambda: st.kscales(0)))
+    ops.append(("wait", ("ks", 0)))
+    for r in range(16):
+        ops.append([f"v_mul_f32 v{a[r]}, v{a[r]}, v{ks[r]}"])
+    ops.append(("lds", lambda: st.kscales(1)))
+    ops.append([f"v_max3_f32 v{T0}, v{a[0]}, v{a[1]}, v{a[2]}"])
+    for i in range(3, 15, 2):
+        ops.append([f"v_max3_f32 v{T0}, v{T0}, v{a[i]}, v{a[i + 1]}"])
+    ops.append([f"v_max_f32 v{T0}, v{T0}, v{a[15]}"])
+    ops.append(("wait", ("ks", 1)))
+    for r in range(16):
+        ops.append([f"v_mul_f32 v{b[r]}, v{b[r]}, v{ks[r]}"])
+    ops.append([f"v_max3_f32 v{T1}, v{b[0]}, v{b[1]}, v{b[2]}"])
+    for i in range(3, 15, 2):
+        ops.append([f"v_max3_f32 v{T1}, v{T1}, v{b[i]}, v{b[i + 1]}"])
+    ops.append([f"v_max_f32 v{T1}, v{T1}, v{b[15]}"])
+    for t in (T0, T1):   # the token scales are done: their registers are temporaries
+        ops.append([f"v_mov_b32 v{ks[0]}, v{t}", "s_nop 1",
+                    f"v_permlane32_swap_b32 v{ks[0]}, v{t}", f"v_max_f32 v{t}, v{ks[0]}, v{t}"])
+    return ops
+
+
+def encode(st):
+    """Block scales and the two e4m3 terms of P' (after the last sum MFMA:
+    the value slots, the code registers and the scale registers are free)."""
+    a = [SA + r for r in range(16)]
+    b = [SB + r for r in range(16)]
+    e0, e1 = T0, T1
+    div = {0: KS[0], 1: KS[2]}
+    dlo = {0: KS[1], 1: KS[3]}
+    dec = KS[4:8]
+    hic, loc = VF[0], VF[1]          # hi codes dwords 0-7, lo codes dwords 0-7
+    for e in (e0, e1):
+        # exponent of the block maximum, clamped so that both scales stay normal
+        st.emit(f"v_bfe_u32 v{e}, v{e}, 23, 8")
+        st.emit(f"v_max_u32 v{e}, 11, v{e}")
+        st.emit(f"v_min_u32 v{e}, 0xfe, v{e}")
+    for beta, e in ((0, e0), (1, e1)):
+        st.emit(f"v_subrev_u32 v{div[beta]}, 7, v{e}")
+        st.emit(f"v_lshlrev_b32 v{div[beta]}, 23, v{div[beta]}")        # 2^(e - 134)
+        st.emit(f"v_subrev_u32 v{dlo[beta]}, 11, v{e}")
+        st.emit(f"v_lshlrev_b32 v{dlo[beta]}, 23, v{dlo[beta]}")        # 2^(e - 138)
+    # E8M0 scale of this lane's K-block: block hf of the lane
+    st.emit("s_mov_b32 vcc_lo, 0")
+    st.emit("s_mov_b32 vcc_hi, -1")
+    st.emit(f"v_cndmask_b32 v{MYS}, v{e0}, v{e1}, vcc")
+    st.emit(f"v_subrev_u32 v{MYS}, 7, v{MYS}")
+    st.emit(f"v_subrev_u32 v{MYSL}, 4, v{MYS}")
+    for beta, regs in ((0, a), (1, b)):
+        for w in range(4):
+            x = regs[4 * w:4 * w + 4]
+            h = hic + 4 * beta + w
+            l = loc + 4 * beta + w
+            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[0]}, v{x[1]}, v{div[beta]}")
+            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[2]}, v{x[3]}, v{div[beta]} op_sel:[0,0,0,1]")
+            st.emit(f"v_cvt_pk_f32_fp8_e32 v[{dec[0]}:{dec[1]}], v{h}")
+            st.emit(f"v_cvt_pk_f32_fp8_sdwa v[{dec[2]}:{dec[3]}], v{h} src0_sel:WORD_1")
+            for i in range(4):
+                st.emit(f"v_fma_f32 v{x[i]}, -v{dec[i]}, v{div[beta]}, v{x[i]}")
+            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[0]}, v{x[1]}, v{dlo[beta]}")
+            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[2]}, v{x[3]}, v{dlo[beta]} op_sel:[0,0,0,1]")
+    st.emit(f"v_add_u32 v{PAD}, %[pw], %[pa]")
+    st.emit(f"ds_write_b128 v{PAD}, {vr(hic, 4)}")
+    st.emit(f"ds_write_b128 v{PAD}, {vr(hic + 4, 4)} offset:1024")
+    st.emit(f"ds_write_b128 v{PAD}, {vr(loc, 4)} offset:2048")
+    st.emit(f"ds_write_b128 v{PAD}, {vr(loc + 4, 4)} offset:3072")
+    st.emit(f"ds_write_b64 v{PAD}, v[{MYS}:{MYSL}] offset:4096")
+
+
+def run_ops(st, ops):
+    for op in ops:
+        if isinstance(op, tuple):
+            if op[0] == "lds":
+                op[1]()
+            else:
+                st.wait_for(op[1])
+        else:
+            for line in op:
+                st.emit(line)
+
+
+KSEQ = [(s, beta, lo) for s in range(9) for (beta, lo) in ((0, 0), (1, 0), (0, 1), (1, 1))]
+
+
+def pv_and_next_values(st, i, vslot_of):
+    """Sum MFMA i; once column tile ct has had its lo MFMA, column tile ct + 2
+    is read into its slot."""
+    st.pv(i, vslot_of)
+    pair, r = i >> 2, i & 3
+    if r >= 2 and pair + 1 < 8:
+        ct = 2 * pair + (r & 1)
+        st.vread(ct + 2, vslot_of[ct + 2])
+
+
+def step(copies, masked):
+    st = Stream()
+    setup(st, True, True)
+    st.pcodes()
+    if copies:
+        st.copy_scales()
+    # key operand of (K-step s, block beta) in slot beta; K-step s+1's operand
+    # is read once K-step s's lo MFMA of that block has issued
+    st.kread(0, 0, 0)
+    st.kread(0, 1, 1)
+    vslot_of = {ct: ct % 2 for ct in range(16)}
+    st.vread(0, 0)
+    st.vread(1, 1)
+    pv_i = 0
+    for s in range(9):
+        st.qk(s, 0, 0, 0)
+        st.qk(s, 1, 0, 1)
+        for beta in (0, 1):
+            st.qk(s, beta, 1, beta)
+            if s + 1 < 9:
+                st.kread(s + 1, beta, beta)
+        pv_and_next_values(st, pv_i, vslot_of)
+        pv_i += 1
+        if copies:
+            st.copy(s)
+    results_ready(st)
+    ops = softmax_ops(st, masked)
+    rest = list(range(pv_i, 32))
+    per = -(-len(ops) // len(rest))
+    for n, i in enumerate(rest):
+        run_ops(st, ops[n * per:(n + 1) * per])
+        pv_and_next_values(st, i, vslot_of)
+    run_ops(st, ops[len(rest) * per:])
+    st.wait_all()
+    results_ready(st)
+    encode(st)
+    return st.text()
+
+
+def first():
+    """Scores, softmax and P' codes of the first tile of a pass."""
+    st = Stream()
+    setup(st, True, False)
+    st.kread(0, 0, 0)
+    st.kread(0, 1, 1)
+    for s in range(9):
+        for beta, lo in ((0, 0), (1, 0), (0, 1), (1, 1)):
+            st.qk(s, beta, lo, (2 * s + beta) % 2)
+            if lo and s + 1 < 9:
+                st.kread(s + 1, beta, (2 * (s + 1) + beta) % 2)
+    results_ready(st)
+    run_ops(st, softmax_ops(st, True))
+    st.wait_all()
+    encode(st)
+    return st.text()
+
+
+def pv_only():
+    """Weighted sum of the last tile of a pass."""
+    st = Stream()
+    setup(st, False, True)
+    st.pcodes()
+    vslot_of = {ct: ct % 2 for ct in range(16)}
+    st.vread(0, 0)
+    st.vread(1, 1)
+    for i in range(32):
+        pv_and_next_values(st, i, vslot_of)
+    st.wait_all()
+    results_ready(st)
+    return st.text()
+
+
+def as_c_string(name, text):
+    body = "\n".join(f'  "{line}\\n\\t"' for line in text.splitlines())
+    return f"#define {name} \\\n" + " \\\n".join(body.splitlines()) + "\n"
+
+
+def main():
+    out = ["// Generated by gen_decode_fp8_asm.py; do not edit.", ""]
+    regs = ", ".join(f'"v{r}"' for r in range(FIRST_SCRATCH, 256))
+    out.append(f"#define MLA_FP8_ASM_SCRATCH {regs}\n")
+    out.append(as_c_string("MLA_FP8_STEP", step(True, True)))
+    out.append(as_c_string("MLA_FP8_FIRST", first()))
+    out.append(as_c_string("MLA_FP8_PV_ONLY", pv_only()))
+    sys.stdout.write("\n".join(out))
+
+
+if __name__ == "__main__":
+    main()
