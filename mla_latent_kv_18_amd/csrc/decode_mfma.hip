@@ -625,10 +625,12 @@ decode_bf16_pipe_kernel(DecodeParams p) {
 }
 
 // Merge the chunk partials of one row: L = log sum_s exp(lse_s),
-// o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).  The lse of up
-// to 64 splits is read lane-parallel, and the partial rows of each batch of 8
-// splits are requested before any of them is weighted, so the merge costs a
-// few memory round trips rather than one per split.
+// o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).  The lse of the
+// first 64 splits (one per lane) and the partial rows of the first 8 splits
+// are requested together, before the request's length is known: slots of
+// splits past that length hold stale workspace contents and are masked out
+// after loading rather than skipped, so the common case costs one memory
+// round trip.  Further splits follow in batches of 8.
 template <typename OutT>
 __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ o_part,
                                                      const float* __restrict__ lse_part,
@@ -638,12 +640,22 @@ __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ 
                                                      float* __restrict__ lse) {
   const int row = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int rows = q_len * n_h;
-  int T = seq_lens[b];
-  T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
-  const int ns = (T + split_tokens - 1) / split_tokens;
   const int64_t base = static_cast<int64_t>(b) * num_splits * rows + row;
   auto lse_of = [&](int s) { return lse_part[base + static_cast<int64_t>(s) * rows]; };
-  const float v0 = lane < ns ? lse_of(lane) : -INFINITY;  // splits 0..63
+  auto part_of = [&](int s) {
+    return *reinterpret_cast<const bf16x8_t*>(o_part + (base + static_cast<int64_t>(s) * rows) * kDc + lane * 8);
+  };
+  // Indices are clamped rather than branched on, so that every load issues
+  // before the first wait.
+  int T = seq_lens[b];
+  const int last = num_splits - 1;
+  const float lse_lane = lse_of(min(lane, last));
+  bf16x8_t x0[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x0[j] = part_of(min(j, last));
+  T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
+  const int ns = (T + split_tokens - 1) / split_tokens;
+  const float v0 = lane < ns ? lse_lane : -INFINITY;  // splits 0..63
   float mx = v0;
   for (int s = 64 + lane; s < ns; s += 64) mx = fmaxf(mx, lse_of(s));
   mx = wave_max(mx);
@@ -658,20 +670,28 @@ __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ 
       sum += v == -INFINITY ? 0.f : __expf(v - mx);
     }
     L = mx + __logf(wave_sum(sum));
-    for (int s0 = 0; s0 < ns; s0 += 8) {
+    const float w_lane = v0 == -INFINITY ? 0.f : __expf(v0 - L);  // weight of split `lane`
+    auto weight = [&](int s) {  // s is uniform across the wave
+      return s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), s))
+                    : __expf(lse_of(s) - L);
+    };
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < ns) {
+        const float w = weight(j);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, static_cast<float>(x0[j][i]), acc[i]);
+      }
+    for (int s0 = 8; s0 < ns; s0 += 8) {
       bf16x8_t x[8];
-      float w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = s0 + j < ns ? part_of(s0 + j) : bf16x8_t{};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int s = s0 + j;
-        x[j] = s < ns ? *reinterpret_cast<const bf16x8_t*>(o_part + (base + static_cast<int64_t>(s) * rows) * kDc + lane * 8)
-                      : bf16x8_t{};
-        w[j] = s < ns ? __expf(lse_of(s) - L) : 0.f;  // uniform address: one line per wave
+        const float w = s0 + j < ns ? weight(s0 + j) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, static_cast<float>(x[j][i]), acc[i]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], static_cast<float>(x[j][i]), acc[i]);
     }
   }
   const int n = b * q_len + row / n_h, h = row % n_h;
