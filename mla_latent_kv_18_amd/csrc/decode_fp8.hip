@@ -359,17 +359,18 @@ decode_fp8_kernel(Fp8Params p) {
 // Software-pipelined form for workgroups of four waves (128 rows of one
 // query position), with q_len <= 32.  Step k of a wave is one instruction
 // stream (decode_fp8_asm.inc, generated by gen_decode_fp8_asm.py): the 36
-// score MFMAs of tile k+1 (two accumulators, hi and lo query terms), the 32
-// weighted-sum MFMAs of tile k, the softmax and two-term P' encoding of tile
-// k+1 between the last of them, and the wave's ten copies of tile k+2.  The
-// P' codes of a tile go to a private LDS area of the wave and are read back
-// by the next step.  Tiles use the 16-row-group layout described in the
-// generator, so that each direct copy reads 16 rows x 64 contiguous bytes.
+// score MFMAs of tile k+1 (two accumulators, hi and lo query terms) with the
+// two-term encoding of tile k's value-side weights between them, then the 32
+// weighted-sum MFMAs of tile k with the softmax of tile k+1 between them; the
+// wave's nine copies of tile k+2 ride in the score phase.  The weights of a
+// tile wait in a private LDS area of the wave from its softmax to its
+// encoding in the next step.  Tiles use the 16-row-group layout described in
+// the generator, so that each direct copy reads 16 rows x 64 contiguous bytes.
 // LDS: three tile buffers (tile k values, tile k+1 keys, tile k+2 landing)
-// and four 5 KB P' areas.
+// and four 9 KB weight areas.
 constexpr int kF8Bufs = 3;
 constexpr int kF8BufBytes = kTileBytes + 256;  // tile + its 64 token scales
-constexpr int kF8PBytes = 5120;                // hi/lo codes + scales, per wave
+constexpr int kF8PBytes = 9216;                // P' (8 KB) + block maxima, per wave
 constexpr int kF8Copies = kLoadsPerTile / 4;   // 9 per wave per tile
 
 #include "decode_fp8_asm.inc"
@@ -386,7 +387,7 @@ constexpr int kF8Copies = kLoadsPerTile / 4;   // 9 per wave per tile
       [ql4] "v"(ql[4]), [ql5] "v"(ql[5]), [ql6] "v"(ql[6]), [ql7] "v"(ql[7]), [ql8] "v"(ql[8])
 #define MLA_F8_KEYS [ka0] "v"(qk_off[0]), [ka1] "v"(qk_off[1]), [bk] "s"(bk)
 #define MLA_F8_VALUES [vo] "v"(pv_off), [bv] "s"(bv)
-#define MLA_F8_COMMON [pa] "v"(pa), [pw] "s"(pw)
+#define MLA_F8_COMMON [pa] "v"(pa), [sw] "s"(sw)
 #define MLA_F8_STATE [mref] "+v"(m_ref), [mseen] "+v"(m_seen), [lrun] "+v"(l_run), [exc] "+v"(excess)
 #define MLA_F8_SOFTMAX_IN \
   [qmul] "v"(qmul), [vlim] "v"(vlim), [tok] "s"(tok), [bks] "s"(bk + kTileBytes), [domask] "s"(domask)
@@ -461,7 +462,7 @@ decode_fp8_pipe_kernel(Fp8Params p) {
   const int pv_row = 8 * (kp >> 2) + 4 * hf + (kp & 3);
   const int pv_off = 16 * (16 * cg + (pv_row ^ (4 * cg))) + 8 * pb;  // + 512 ct + 9216 j
   const uint32_t pa = 16 * lane;
-  const uint32_t pw = pbuf_addr + wave * kF8PBytes;
+  const uint32_t sw = pbuf_addr + wave * kF8PBytes;
 
   // Copy ii of this wave fills slots 64i.. of a tile, i = wave + 4ii: row
   // cR[ii] + crow (16-row group i / 9, lane's row in it), byte column
@@ -476,12 +477,14 @@ decode_fp8_pipe_kernel(Fp8Params p) {
     cC[ii] = 64 * (i % 9);
   }
   const int64_t bt_row = static_cast<int64_t>(b) * p.max_blocks;
-  auto first_row = [&](int k) -> int64_t {  // cache slot of tile k's first token
+  // block-table entry of tile k, and the cache slot of tile k's first token given it
+  auto block_of = [&](int k) { return block_table[bt_row + (j0 + k * kTileT) / p.block_size]; };
+  auto row_from = [&](int blk, int k) -> int64_t {
     const int tok0 = j0 + k * kTileT;
-    int blk = block_table[bt_row + tok0 / p.block_size];
     blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
     return static_cast<int64_t>(blk) * p.block_size + tok0 % p.block_size;
   };
+  auto first_row = [&](int k) { return row_from(block_of(k), k); };
   auto last_row = [&](int k) { return min(kTileT, T - (j0 + k * kTileT)) - 1; };
   auto buf_addr = [&](int k) { return tiles_addr + (k % kF8Bufs) * kF8BufBytes; };
   auto issue_tile = [&](int k) {
@@ -521,7 +524,13 @@ decode_fp8_pipe_kernel(Fp8Params p) {
                    : MLA_F8_Q, MLA_F8_KEYS, MLA_F8_COMMON, MLA_F8_SOFTMAX_IN
                    : MLA_F8_SCRATCH);
     }
+    // Copy sources are looked up ahead: the block-table entry of tile k+4 is
+    // read in step k and turned into a cache slot in step k+1, so no step
+    // waits for a table read.
+    int64_t first_next = n_tiles > 2 ? first_row(2) : 0;
+    int blk_next = n_tiles > 3 ? block_of(3) : 0;
     for (int k = 0; k + 1 < n_tiles; ++k) {
+      const int64_t first = first_next;
       wait_vmcnt<0>();                      // tile k+1 landed
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();        // tile k+1 visible; tile k-1 released by all waves
@@ -535,7 +544,6 @@ decode_fp8_pipe_kernel(Fp8Params p) {
       const bool copying = k + 2 < n_tiles;
       const int docopy = max(n_tiles - k - 2, 0);
       const int domask = max(k + 4 - n_tiles, 0);
-      const int64_t first = copying ? first_row(k + 2) : 0;
       const uint8_t* cb = p.cache + first * kD;
       const float* csb = p.cache_scale + first;
       const int cl = copying ? last_row(k + 2) : 0;
@@ -545,10 +553,12 @@ decode_fp8_pipe_kernel(Fp8Params p) {
                    : MLA_F8_ACC, MLA_F8_STATE
                    : MLA_F8_Q, MLA_F8_KEYS, MLA_F8_VALUES, MLA_F8_COMMON, MLA_F8_SOFTMAX_IN, MLA_F8_COPY
                    : MLA_F8_SCRATCH);
+      if (k + 3 < n_tiles) first_next = row_from(blk_next, k + 3);
+      if (k + 4 < n_tiles) blk_next = block_of(k + 4);
     }
-    {  // weighted sum of the last tile (its codes are in this wave's P' area)
+    {  // encoding and weighted sum of the last tile (its weights are in this wave's area)
       const uint32_t bv = buf_addr(n_tiles - 1);
-      asm volatile(MLA_FP8_PV_ONLY : MLA_F8_ACC : MLA_F8_VALUES, MLA_F8_COMMON : MLA_F8_SCRATCH);
+      asm volatile(MLA_FP8_LAST : MLA_F8_ACC : MLA_F8_VALUES, MLA_F8_COMMON : MLA_F8_SCRATCH);
     }
     return excess > kSlack;
   };

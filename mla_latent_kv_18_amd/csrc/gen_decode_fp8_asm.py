@@ -5,21 +5,25 @@ decode kernel's software-pipelined tile step (decode_fp8.hip).
 
 A workgroup has four waves; wave w owns 32 heads of one query position.
 Tiles are 64 tokens of e4m3 cache rows (one K-step of the fp8 MFMA for the
-weighted sum) plus their 64 fp32 token scales.  Step k of a wave:
+weighted sum) plus their 64 fp32 token scales.  Step k of a wave has two
+phases:
 
   scores   S^T = K Q^T for tile k+1: 9 K-steps of 64 latent dims, two
            32-token blocks (beta), hi and lo query planes: 36 MFMAs
-           (v_mfma_scale_f32_32x32x64_f8f6f4) into two accumulators
-  softmax  s = S * kscale[t] * qscale[h] * scale * log2(e); p = 2^(s - m_ref);
-           the value-side weight P' = p * kscale[t] is split into two e4m3
-           terms with a power-of-two scale per (head, 32-token block); the
-           codes and scales go to this wave's private LDS area
-  sum      O^T += V^T P'^T for tile k: 16 column tiles x (hi, lo) = 32 MFMAs
-           whose B operand (the codes of tile k) was read back at the start
+           (v_mfma_scale_f32_32x32x64_f8f6f4) into two accumulators.
+           Between them: the encoding of tile k's value-side weights
+           P' = p * kscale[t] into two e4m3 terms with a power-of-two scale
+           per (head, 32-token block), straight into the B-operand registers
+           of the weighted sum, and the wave's copies of tile k+2.
+  sum      O^T += V^T P'^T for tile k: 16 column tiles x (hi, lo) = 32 MFMAs.
+           Between them: the softmax of tile k+1, s = S * kscale[t] *
+           qscale[h] * scale * log2(e), p = 2^(s - m_ref), P' = p * kscale[t],
+           and its block maxima; P' and the maxima go to a private LDS area
+           of the wave, read back by the next step's encoding.
 
-MFMA order: per K-step [score A hi, score B hi, score A lo, score B lo, sum],
-then the remaining 23 sum MFMAs with the softmax work between them; the
-encoding of P' follows the last sum MFMA (it reuses that MFMA's registers).
+So every VALU stretch sits beside MFMAs of another tile: the encoding of
+tile k beside the scores of tile k+1, the softmax of tile k+1 beside the sum
+of tile k.
 
 Tile layout in LDS (16-row groups): 16-byte chunk c of row t at slot
 576(t >> 4) + 16c + ((t & 15) ^ 4(c & 1)); the 64 token scales follow at
@@ -32,8 +36,8 @@ Operands (named in the kernel):
   %[vo]           per-lane transposed value byte offset
   %[pa]           16 * lane
   %[bk], %[bv]    LDS byte address of the scored tile and of the summed tile
-  %[pw]           LDS byte address of this wave's P' area (5120 B: codes at
-                  16*lane + 1024*part, scales at 4096 + 16*lane)
+  %[sw]           LDS byte address of this wave's P' area (9216 B: value
+                  group g at 1024*g + 16*lane, block maxima at 8192 + 16*lane)
   %[qmul]         per-head qscale * softmax scale * log2(e)
   %[mref], %[mseen], %[lrun], %[exc]  per-head softmax state (in/out)
   %[vlim], %[tok], %[domask]  token t (0..63) of the scored tile is visible
@@ -58,9 +62,13 @@ VF = [208, 216]                       # value operand slots (8 VGPRs each)
 SA, SB = 224, 240                     # score accumulators (beta 0, 1)
 KS = list(range(192, 208))            # token scales, in the key slots once scores are done
 SCA = KA[0]                           # token-scale read address (keys are done by then)
-PAD = KA[1]                           # P' area address when the codes are written
-PAD0 = SA                             # P' area address when they are read (before any score)
+PAD = KA[1]                           # P' area address when P' is written (keys are done)
 CT, CO = T0, T1                       # copy temporaries
+# encoding working set (the value slots, free during the score phase)
+XB = [208, 212]                       # two 4-value P' groups being encoded
+DEC = 216                             # 4 decoded hi terms
+DV = 220                              # div0, dlo0, div1, dlo1 (block scales as floats)
+SPA = VA                              # P' area address during the encoding
 NEG_INF = "0xff800000"
 
 
@@ -111,14 +119,14 @@ class Stream:
         for a4 in range(4):
             self.lds(("ks", beta), f"ds_read_b128 {vr(KS[4 * a4], 4)}, v{SCA} offset:{128 * beta + 32 * a4}")
 
-    def pcodes(self):
-        # P' codes of the tile being summed: hi dwords 0-3 / 4-7, lo dwords 0-3 / 4-7, scales
-        self.emit(f"v_add_u32 v{PAD0}, %[pw], %[pa]")
-        self.lds(("p",), f"ds_read_b128 {vr(PH, 4)}, v{PAD0} offset:0")
-        self.lds(("p",), f"ds_read_b128 {vr(PH + 4, 4)}, v{PAD0} offset:1024")
-        self.lds(("p",), f"ds_read_b128 {vr(PL, 4)}, v{PAD0} offset:2048")
-        self.lds(("p",), f"ds_read_b128 {vr(PL + 4, 4)}, v{PAD0} offset:3072")
-        self.lds(("p",), f"ds_read_b64 v[{MYS}:{MYSL}], v{PAD0} offset:4096")
+    def spill_maxima(self):
+        # block maxima of the P' being encoded (pmax0, pmax1 per lane)
+        self.emit(f"v_add_u32 v{SPA}, %[sw], %[pa]")
+        self.lds(("sm",), f"ds_read_b64 v[{DV}:{DV + 1}], v{SPA} offset:8192")
+
+    def spill_group(self, g):
+        # P' values of group g (block g >> 2, registers 4(g & 3)..+3) into XB[g & 1]
+        self.lds(("sp", g), f"ds_read_b128 {vr(XB[g & 1], 4)}, v{SPA} offset:{1024 * g}")
 
     # ---- MFMAs
     def qk(self, s, beta, lo, slot):
@@ -136,7 +144,6 @@ class Stream:
         ct = 2 * pair + (r & 1)
         lo = r >= 2
         self.wait_for(("v", ct))
-        self.wait_for(("p",))
         p, sc = (PL, MYSL) if lo else (PH, MYS)
         self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{ct}], {vr(VF[vslot_of[ct]])}, {vr(p)}, %[o{ct}], "
                   f"v{S127}, v{sc} op_sel_hi:[0,0,0]")
@@ -258,69 +265,86 @@ def softmax_ops(st, masked):
     for t in (T0, T1):   # the token scales are done: their registers are temporaries
         ops.append([f"v_mov_b32 v{ks[0]}, v{t}", "s_nop 1",
                     f"v_permlane32_swap_b32 v{ks[0]}, v{t}", f"v_max_f32 v{t}, v{ks[0]}, v{t}"])
+    ops.append(("lds", lambda: spill_writes(st)))
     return ops
 
 
-def encode(st):
-    """Block scales and the two e4m3 terms of P' (after the last sum MFMA:
-    the value slots, the code registers and the scale registers are free)."""
-    a = [SA + r for r in range(16)]
-    b = [SB + r for r in range(16)]
-    e0, e1 = T0, T1
-    div = {0: KS[0], 1: KS[2]}
-    dlo = {0: KS[1], 1: KS[3]}
-    dec = KS[4:8]
-    hic, loc = VF[0], VF[1]          # hi codes dwords 0-7, lo codes dwords 0-7
+def spill_writes(st):
+    """P' (SA, SB) and its block maxima (T0, T1) to the wave's area."""
+    st.emit(f"v_add_u32 v{PAD}, %[sw], %[pa]")
+    for g in range(8):
+        acc = SA if g < 4 else SB
+        st.lds(("w",), f"ds_write_b128 v{PAD}, {vr(acc + 4 * (g & 3), 4)} offset:{1024 * g}")
+    st.lds(("w",), f"ds_write_b32 v{PAD}, v{T0} offset:8192")
+    st.lds(("w",), f"ds_write_b32 v{PAD}, v{T1} offset:8196")
+
+
+def encode_setup(st):
+    """Block scales of the P' being encoded, from its block maxima (in DV,
+    DV+1): MYS/MYSL (E8M0 scales of the hi and lo terms of this lane's
+    K-block), div0/dlo0/div1/dlo1 (the same powers of two as floats)."""
+    e0, e1 = DV, DV + 1
+    st.wait_for(("sm",))
     for e in (e0, e1):
         # exponent of the block maximum, clamped so that both scales stay normal
         st.emit(f"v_bfe_u32 v{e}, v{e}, 23, 8")
         st.emit(f"v_max_u32 v{e}, 11, v{e}")
         st.emit(f"v_min_u32 v{e}, 0xfe, v{e}")
-    for beta, e in ((0, e0), (1, e1)):
-        st.emit(f"v_subrev_u32 v{div[beta]}, 7, v{e}")
-        st.emit(f"v_lshlrev_b32 v{div[beta]}, 23, v{div[beta]}")        # 2^(e - 134)
-        st.emit(f"v_subrev_u32 v{dlo[beta]}, 11, v{e}")
-        st.emit(f"v_lshlrev_b32 v{dlo[beta]}, 23, v{dlo[beta]}")        # 2^(e - 138)
     # E8M0 scale of this lane's K-block: block hf of the lane
     st.emit("s_mov_b32 vcc_lo, 0")
     st.emit("s_mov_b32 vcc_hi, -1")
     st.emit(f"v_cndmask_b32 v{MYS}, v{e0}, v{e1}, vcc")
     st.emit(f"v_subrev_u32 v{MYS}, 7, v{MYS}")
     st.emit(f"v_subrev_u32 v{MYSL}, 4, v{MYS}")
-    for beta, regs in ((0, a), (1, b)):
-        for w in range(4):
-            x = regs[4 * w:4 * w + 4]
-            h = hic + 4 * beta + w
-            l = loc + 4 * beta + w
-            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[0]}, v{x[1]}, v{div[beta]}")
-            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[2]}, v{x[3]}, v{div[beta]} op_sel:[0,0,0,1]")
-            st.emit(f"v_cvt_pk_f32_fp8_e32 v[{dec[0]}:{dec[1]}], v{h}")
-            st.emit(f"v_cvt_pk_f32_fp8_sdwa v[{dec[2]}:{dec[3]}], v{h} src0_sel:WORD_1")
-            for i in range(4):
-                st.emit(f"v_fma_f32 v{x[i]}, -v{dec[i]}, v{div[beta]}, v{x[i]}")
-            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[0]}, v{x[1]}, v{dlo[beta]}")
-            st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[2]}, v{x[3]}, v{dlo[beta]} op_sel:[0,0,0,1]")
-    st.emit(f"v_add_u32 v{PAD}, %[pw], %[pa]")
-    st.emit(f"ds_write_b128 v{PAD}, {vr(hic, 4)}")
-    st.emit(f"ds_write_b128 v{PAD}, {vr(hic + 4, 4)} offset:1024")
-    st.emit(f"ds_write_b128 v{PAD}, {vr(loc, 4)} offset:2048")
-    st.emit(f"ds_write_b128 v{PAD}, {vr(loc + 4, 4)} offset:3072")
-    st.emit(f"ds_write_b64 v{PAD}, v[{MYS}:{MYSL}] offset:4096")
+    st.emit(f"v_subrev_u32 v{DV + 2}, 7, v{e1}")
+    st.emit(f"v_lshlrev_b32 v{DV + 2}, 23, v{DV + 2}")        # div1 = 2^(e1 - 134)
+    st.emit(f"v_subrev_u32 v{DV + 3}, 11, v{e1}")
+    st.emit(f"v_lshlrev_b32 v{DV + 3}, 23, v{DV + 3}")        # dlo1 = 2^(e1 - 138)
+    st.emit(f"v_subrev_u32 v{DV + 1}, 11, v{e0}")
+    st.emit(f"v_lshlrev_b32 v{DV + 1}, 23, v{DV + 1}")        # dlo0
+    st.emit(f"v_subrev_u32 v{DV}, 7, v{e0}")
+    st.emit(f"v_lshlrev_b32 v{DV}, 23, v{DV}")                # div0
+
+
+def encode_group(st, g):
+    """Two e4m3 terms of P' group g: hi codes into PH[g], lo codes into PL[g]."""
+    beta = g >> 2
+    div, dlo = DV + 2 * beta, DV + 2 * beta + 1
+    x = [XB[g & 1] + i for i in range(4)]
+    h, l = PH + g, PL + g
+    st.wait_for(("sp", g))
+    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[0]}, v{x[1]}, v{div}")
+    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[2]}, v{x[3]}, v{div} op_sel:[0,0,0,1]")
+    st.emit(f"v_cvt_pk_f32_fp8_e32 v[{DEC}:{DEC + 1}], v{h}")
+    st.emit(f"v_cvt_pk_f32_fp8_sdwa v[{DEC + 2}:{DEC + 3}], v{h} src0_sel:WORD_1")
+    for i in range(4):
+        st.emit(f"v_fma_f32 v{x[i]}, -v{DEC + i}, v{div}, v{x[i]}")
+    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[0]}, v{x[1]}, v{dlo}")
+    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[2]}, v{x[3]}, v{dlo} op_sel:[0,0,0,1]")
+
+
+def encode_ops(st):
+    """The encoding as groups of instructions to spread between MFMAs; the
+    P' group reads run two groups ahead of their use."""
+    ops = [("lds", lambda: (st.spill_maxima(), st.spill_group(0), st.spill_group(1))),
+           ("fn", lambda: encode_setup(st))]
+    for g in range(8):
+        ops.append(("fn", lambda g=g: encode_group(st, g)))
+        if g + 2 < 8:
+            ops.append(("lds", lambda g=g: st.spill_group(g + 2)))
+    return ops
 
 
 def run_ops(st, ops):
     for op in ops:
         if isinstance(op, tuple):
-            if op[0] == "lds":
+            if op[0] in ("lds", "fn"):
                 op[1]()
             else:
                 st.wait_for(op[1])
         else:
             for line in op:
                 st.emit(line)
-
-
-KSEQ = [(s, beta, lo) for s in range(9) for (beta, lo) in ((0, 0), (1, 0), (0, 1), (1, 1))]
 
 
 def pv_and_next_values(st, i, vslot_of):
@@ -333,75 +357,95 @@ def pv_and_next_values(st, i, vslot_of):
         st.vread(ct + 2, vslot_of[ct + 2])
 
 
-def step(copies, masked):
-    st = Stream()
-    setup(st, True, True)
-    st.pcodes()
-    if copies:
-        st.copy_scales()
-    # key operand of (K-step s, block beta) in slot beta; K-step s+1's operand
-    # is read once K-step s's lo MFMA of that block has issued
+def interleave(st, ops, n_slots, emit_slot):
+    """emit_slot(i) for i < n_slots, the op groups spread evenly before them."""
+    n, j = len(ops), 0
+    for i in range(n_slots):
+        target = -(-(i + 1) * n // n_slots)
+        run_ops(st, ops[j:target])
+        j = target
+        emit_slot(i)
+    run_ops(st, ops[j:])
+
+
+def score_phase(st, copies, enc):
+    """The 36 score MFMAs of the tile at %[bk]; between them the encoding of
+    the P' in the wave's area (enc), the wave's tile copies (copies) and, once
+    the encoding is done, the reads of the first two value column tiles."""
     st.kread(0, 0, 0)
     st.kread(0, 1, 1)
-    vslot_of = {ct: ct % 2 for ct in range(16)}
-    st.vread(0, 0)
-    st.vread(1, 1)
-    pv_i = 0
-    for s in range(9):
-        st.qk(s, 0, 0, 0)
-        st.qk(s, 1, 0, 1)
-        for beta in (0, 1):
-            st.qk(s, beta, 1, beta)
-            if s + 1 < 9:
-                st.kread(s + 1, beta, beta)
-        pv_and_next_values(st, pv_i, vslot_of)
-        pv_i += 1
-        if copies:
+    ops = encode_ops(st) if enc else []
+    n_enc = 27 if enc else 0              # MFMA slots the encoding is spread over
+
+    def slot(i):
+        s, j = divmod(i, 4)
+        beta, lo = ((0, 0), (1, 0), (0, 1), (1, 1))[j]
+        st.qk(s, beta, lo, beta)
+        if lo and s + 1 < 9:
+            st.kread(s + 1, beta, beta)
+        if j == 3 and copies:
             st.copy(s)
-    results_ready(st)
-    ops = softmax_ops(st, masked)
-    rest = list(range(pv_i, 32))
-    per = -(-len(ops) // len(rest))
-    for n, i in enumerate(rest):
-        run_ops(st, ops[n * per:(n + 1) * per])
-        pv_and_next_values(st, i, vslot_of)
-    run_ops(st, ops[len(rest) * per:])
+    if enc:
+        interleave(st, ops, n_enc, slot)
+        for i in range(n_enc, 36):
+            slot(i)
+            if i == n_enc:
+                st.emit(f"v_add_u32 v{VA}, %[bv], %[vo]")
+                st.vread(0, 0)
+                st.vread(1, 1)
+    else:
+        for i in range(36):
+            slot(i)
+
+
+def sum_phase(st, soft, masked):
+    """The 32 sum MFMAs of the tile at %[bv] (codes in PH/PL, scales in
+    MYS/MYSL, first two value tiles already requested); between them the
+    softmax of the scores just computed and its P' writes (soft)."""
+    vslot_of = {ct: ct % 2 for ct in range(16)}
+    st.emit("s_nop 7")                    # encoded operands written by VALU
+    if soft:
+        results_ready(st)
+        ops = softmax_ops(st, masked)
+        interleave(st, ops, 32, lambda i: pv_and_next_values(st, i, vslot_of))
+    else:
+        for i in range(32):
+            pv_and_next_values(st, i, vslot_of)
     st.wait_all()
     results_ready(st)
-    encode(st)
+
+
+def step():
+    """Step k: encoding of tile k and scores of tile k+1 (with the copies of
+    tile k+2), then the sum of tile k and the softmax of tile k+1."""
+    st = Stream()
+    setup(st, True, False)
+    st.copy_scales()
+    score_phase(st, True, True)
+    sum_phase(st, True, True)
     return st.text()
 
 
 def first():
-    """Scores, softmax and P' codes of the first tile of a pass."""
+    """Scores and softmax of the first tile of a pass."""
     st = Stream()
     setup(st, True, False)
-    st.kread(0, 0, 0)
-    st.kread(0, 1, 1)
-    for s in range(9):
-        for beta, lo in ((0, 0), (1, 0), (0, 1), (1, 1)):
-            st.qk(s, beta, lo, (2 * s + beta) % 2)
-            if lo and s + 1 < 9:
-                st.kread(s + 1, beta, (2 * (s + 1) + beta) % 2)
+    score_phase(st, False, False)
     results_ready(st)
     run_ops(st, softmax_ops(st, True))
     st.wait_all()
-    encode(st)
     return st.text()
 
 
-def pv_only():
-    """Weighted sum of the last tile of a pass."""
+def last():
+    """Encoding and sum of the last tile of a pass."""
     st = Stream()
-    setup(st, False, True)
-    st.pcodes()
-    vslot_of = {ct: ct % 2 for ct in range(16)}
+    setup(st, False, False)
+    run_ops(st, encode_ops(st))
+    st.emit(f"v_add_u32 v{VA}, %[bv], %[vo]")
     st.vread(0, 0)
     st.vread(1, 1)
-    for i in range(32):
-        pv_and_next_values(st, i, vslot_of)
-    st.wait_all()
-    results_ready(st)
+    sum_phase(st, False, False)
     return st.text()
 
 
@@ -414,9 +458,9 @@ def main():
     out = ["// Generated by gen_decode_fp8_asm.py; do not edit.", ""]
     regs = ", ".join(f'"v{r}"' for r in range(FIRST_SCRATCH, 256))
     out.append(f"#define MLA_FP8_ASM_SCRATCH {regs}\n")
-    out.append(as_c_string("MLA_FP8_STEP", step(True, True)))
+    out.append(as_c_string("MLA_FP8_STEP", step()))
     out.append(as_c_string("MLA_FP8_FIRST", first()))
-    out.append(as_c_string("MLA_FP8_PV_ONLY", pv_only()))
+    out.append(as_c_string("MLA_FP8_LAST", last()))
     sys.stdout.write("\n".join(out))
 
 
