@@ -402,11 +402,13 @@ constexpr int kF8Copies = kLoadsPerTile / 4;   // 9 per wave per tile
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_fp8_pipe_kernel(Fp8Params p) {
-  __shared__ __attribute__((aligned(1024))) char tiles_raw[kF8Bufs * kF8BufBytes];
-  __shared__ __attribute__((aligned(1024))) char pbuf_raw[4 * kF8PBytes];
-  MLA_LDS char* tiles = (MLA_LDS char*)tiles_raw;
+  // tile buffers, then the waves' P' areas; at the start the first 144 KB
+  // hold the waves' latent queries instead
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kF8Bufs * kF8BufBytes + 4 * kF8PBytes];
+  static_assert(4 * kTileBytes <= kF8Bufs * kF8BufBytes + 4 * kF8PBytes, "query staging fits");
+  MLA_LDS char* tiles = (MLA_LDS char*)lds_raw;
   const uint32_t tiles_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles));
-  const uint32_t pbuf_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MLA_LDS char*)pbuf_raw));
+  const uint32_t pbuf_addr = tiles_addr + kF8Bufs * kF8BufBytes;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;
@@ -439,22 +441,41 @@ decode_fp8_pipe_kernel(Fp8Params p) {
   const int vis_end = T - p.q_len + t_q + 1;
   const int my_h = h0 + (lane & 31);
 
-  // latent query codes of this wave's heads: Q[h, 64s + 32hf .. +32]
+  const int tq = lane & 31;
+  // Latent query codes of this wave's heads: Q[h, 64s + 32hf .. +32] (hi and
+  // lo planes).  The wave's 32 rows (1152 B each) are contiguous in q_lat;
+  // they are copied with whole-kilobyte loads into a 36 KB slot of LDS, where
+  // 16-byte chunk c of row r sits at chunk 72r + (c ^ (r & 6)): the two
+  // chunks of a fragment stay adjacent and in order, and eight consecutive
+  // rows land in distinct bank groups.  Loading them straight into registers
+  // would take one 32-byte piece from each of 32 rows per load instruction.
   i32x8_t qf[9], ql[9];
   float qmul;
   {
-    const int64_t qrow = static_cast<int64_t>(n_tok) * p.n_h + my_h;
-    const uint8_t* q = p.q_lat + qrow * (2 * kD) + 32 * hf;
+    const int64_t qrow0 = static_cast<int64_t>(n_tok) * p.n_h + h0;
+    const uint8_t* qsrc = p.q_lat + qrow0 * (2 * kD);
+    const uint32_t slot = tiles_addr + wave * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i) {
+      const int pos = 64 * i + lane, r = pos / 72, c = (pos % 72) ^ (r & 6);
+      dma16_sv(qsrc, r * (2 * kD) + 16 * c, slot + 1024 * i);
+    }
+    qmul = p.q_scale[qrow0 + tq] * p.scale_log2;
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    MLA_LDS const char* qrow = tiles + wave * kTileBytes + 16 * (72 * tq);
+    const int fr = tq & 6;
 #pragma unroll
     for (int s = 0; s < 9; ++s) {
-      qf[s] = *reinterpret_cast<const i32x8_t*>(q + 64 * s);
-      ql[s] = *reinterpret_cast<const i32x8_t*>(q + kD + 64 * s);
+      const int c = 4 * s + 2 * hf;
+      qf[s] = *reinterpret_cast<MLA_LDS const i32x8_t*>(qrow + 16 * (c ^ fr));
+      ql[s] = *reinterpret_cast<MLA_LDS const i32x8_t*>(qrow + 16 * ((36 + c) ^ fr));
     }
-    qmul = p.q_scale[qrow] * p.scale_log2;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): codes in registers
+    __builtin_amdgcn_s_barrier();        // every wave done with its slot
   }
 
   // per-lane LDS byte offsets in the 16-row-group tile layout
-  const int tq = lane & 31;
   int qk_off[2];  // chunk 4s + 2hf + x of row tq + 32 beta: + 1024 s + 18432 beta
 #pragma unroll
   for (int x = 0; x < 2; ++x) qk_off[x] = 16 * (576 * (tq >> 4) + 16 * (2 * hf + x) + ((tq & 15) ^ (4 * x)));
@@ -585,20 +606,20 @@ decode_fp8_pipe_kernel(Fp8Params p) {
     run_pass();
   }
 
+  // Epilogue.  Lane-derived values are recomputed here from an opaque lane
+  // id rather than kept live across the tile loop, where every register
+  // outside the streams' scratch range holds an operand.  The wave's 32
+  // normalised rows are staged through LDS (16-byte chunk q of head h at
+  // chunk q ^ (h & 15) of a 1 KB row) and stored as whole 1 KB rows.
+  int lane_e;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int he = lane_e & 31, hfe = lane_e >> 5;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
-  const int my_row = row0 + (lane & 31);
-  __bf16* orow;
-  float* lrow;
-  if (direct) {
-    orow = p.o_lat + (static_cast<int64_t>(n_tok) * p.n_h + my_h) * kDc;
-    lrow = p.lse != nullptr ? p.lse + static_cast<int64_t>(n_tok) * p.n_h + my_h : nullptr;
-  } else {
-    const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
-    orow = p.o_part + pr * kDc;
-    lrow = p.lse_part + pr;
-  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();  // every wave is done with the tile buffers
+  MLA_LDS char* stage = tiles + wave * kTileBytes;
 #pragma unroll
   for (int ct = 0; ct < 16; ++ct)
 #pragma unroll
@@ -606,9 +627,23 @@ decode_fp8_pipe_kernel(Fp8Params p) {
       bf16x4_t v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16(oacc[ct][4 * j + i] * inv);
-      *reinterpret_cast<bf16x4_t*>(orow + 32 * ct + 8 * j + 4 * hf) = v;
+      *reinterpret_cast<MLA_LDS bf16x4_t*>(stage + he * 1024 + (((4 * ct + j) ^ (he & 15)) * 16) + 8 * hfe) = v;
     }
-  if (lrow != nullptr && hf == 0) *lrow = lse_v;
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's rows staged
+  int64_t row_base;                     // output row of head h0 (+ h for head h0 + h)
+  if (direct) {
+    row_base = static_cast<int64_t>(n_tok) * p.n_h + h0;
+  } else {
+    row_base = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + row0;
+  }
+  __bf16* obase = direct ? p.o_lat : p.o_part;
+#pragma unroll 4
+  for (int h = 0; h < 32; ++h) {
+    const bf16x8_t v = *reinterpret_cast<MLA_LDS const bf16x8_t*>(stage + h * 1024 + ((lane_e ^ (h & 15)) * 16));
+    *reinterpret_cast<bf16x8_t*>(obase + (row_base + h) * kDc + 8 * lane_e) = v;
+  }
+  float* lbase = direct ? p.lse : p.lse_part;
+  if (lbase != nullptr && hfe == 0) lbase[row_base + he] = lse_v;
 }
 
 }  // namespace

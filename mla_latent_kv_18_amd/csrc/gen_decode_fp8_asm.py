@@ -45,29 +45,29 @@ Operands (named in the kernel):
   %[docopy]       the step copies a tile when non-zero
   %[cb], %[cd], %[cl], %[csb], %[csd], %[k576], %[rl], %[q16], %[r0..8],
   %[k0..8]        the tile copy (see Stream.copy)
-The streams use v167-v255, vcc, m0 and scc as scratch.
+The streams use v176-v255, vcc, m0 and scc as scratch.
 """
 import sys
 
-FIRST_SCRATCH = 167
-T1 = 167                              # temporaries (copy offsets while copying)
-S127, S123 = 168, 169                 # E8M0 scale constants 2^0, 2^-4
-KA = [170, 171]                       # key read addresses (chunk parity)
-VA = 172                              # value read address
-T0 = 173
-MYS, MYSL = 174, 175                  # E8M0 scales of the P' codes (hi, lo)
-PH, PL = 176, 184                     # P' codes being summed (8 VGPRs each)
-KF = [192, 200]                       # key operand slots (8 VGPRs each)
-VF = [208, 216]                       # value operand slots (8 VGPRs each)
+FIRST_SCRATCH = 176
+S127, S123 = 176, 177                 # E8M0 scale constants 2^0, 2^-4
+KA = [178, 179]                       # key read addresses (chunk parity)
+VA = 180                              # value read address
+T0 = 181                              # temporary (copy offset while copying)
+MYS, MYSL = 182, 183                  # E8M0 scales of the P' codes (hi, lo)
+PH, PL = 184, 192                     # P' codes being summed (8 VGPRs each)
+KF = [200, 208]                       # key operand slots (8 VGPRs each)
+VF = 216                              # value operand slot (8 VGPRs)
 SA, SB = 224, 240                     # score accumulators (beta 0, 1)
-KS = list(range(192, 208))            # token scales, in the key slots once scores are done
+KS = list(range(200, 216))            # token scales, in the key slots once scores are done
+KT0, KT1 = KS[0], KS[1]               # softmax temporaries while the key slots hold no scales
 SCA = KA[0]                           # token-scale read address (keys are done by then)
 PAD = KA[1]                           # P' area address when P' is written (keys are done)
-CT, CO = T0, T1                       # copy temporaries
-# encoding working set (the value slots, free during the score phase)
-XB = [208, 212]                       # two 4-value P' groups being encoded
-DEC = 216                             # 4 decoded hi terms
-DV = 220                              # div0, dlo0, div1, dlo1 (block scales as floats)
+CT = T0                               # copy offset
+# encoding working set (the value slot, free during the score phase)
+XB = 216                              # the 4-value P' group being encoded
+DEC = 220                             # 2 decoded hi terms, then the lo-term scale
+DV = 222                              # div0, div1 (block scales as floats)
 SPA = VA                              # P' area address during the encoding
 NEG_INF = "0xff800000"
 
@@ -110,8 +110,8 @@ class Stream:
         self.lds(("k", s, beta), f"ds_read_b128 {vr(base, 4)}, v{KA[0]} offset:{off}")
         self.lds(("k", s, beta), f"ds_read_b128 {vr(base + 4, 4)}, v{KA[1]} offset:{off}")
 
-    def vread(self, ct, slot):
-        base = VF[slot]
+    def vread(self, ct):
+        base = VF
         for j in range(4):
             self.lds(("v", ct), f"ds_read_b64_tr_b8 {vr(base + 2 * j, 2)}, v{VA} offset:{512 * ct + 9216 * j}")
 
@@ -125,8 +125,8 @@ class Stream:
         self.lds(("sm",), f"ds_read_b64 v[{DV}:{DV + 1}], v{SPA} offset:8192")
 
     def spill_group(self, g):
-        # P' values of group g (block g >> 2, registers 4(g & 3)..+3) into XB[g & 1]
-        self.lds(("sp", g), f"ds_read_b128 {vr(XB[g & 1], 4)}, v{SPA} offset:{1024 * g}")
+        # P' values of group g (block g >> 2, registers 4(g & 3)..+3) into XB
+        self.lds(("sp", g), f"ds_read_b128 {vr(XB, 4)}, v{SPA} offset:{1024 * g}")
 
     # ---- MFMAs
     def qk(self, s, beta, lo, slot):
@@ -138,14 +138,12 @@ class Stream:
         self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 {vr(acc, 16)}, {vr(KF[slot])}, {q}, {c}, "
                   f"v{S127}, v{sb} op_sel_hi:[0,0,0]")
 
-    def pv(self, i, vslot_of):
-        # MFMA i: column-tile pair i // 4, (ct, hi), (ct+1, hi), (ct, lo), (ct+1, lo)
-        pair, r = i >> 2, i & 3
-        ct = 2 * pair + (r & 1)
-        lo = r >= 2
+    def pv(self, i):
+        # MFMA i: column tile i >> 1, hi codes (even i) or lo codes (odd i)
+        ct, lo = i >> 1, i & 1
         self.wait_for(("v", ct))
         p, sc = (PL, MYSL) if lo else (PH, MYS)
-        self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{ct}], {vr(VF[vslot_of[ct]])}, {vr(p)}, %[o{ct}], "
+        self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{ct}], {vr(VF)}, {vr(p)}, %[o{ct}], "
                   f"v{S127}, v{sc} op_sel_hi:[0,0,0]")
 
     def copy(self, ii):
@@ -157,10 +155,10 @@ class Stream:
         self.emit(f"s_cbranch_scc0 .Lnc%=_{ii}")
         self.emit(f"v_add_u32 v{CT}, %[r{ii}], %[rl]")
         self.emit(f"v_min_u32 v{CT}, %[cl], v{CT}")
-        self.emit(f"v_mad_u32_u24 v{CO}, v{CT}, %[k576], %[q16]")
-        self.emit(f"v_add_u32 v{CO}, %[k{ii}], v{CO}")
+        self.emit(f"v_mad_u32_u24 v{CT}, v{CT}, %[k576], %[q16]")
+        self.emit(f"v_add_u32 v{CT}, %[k{ii}], v{CT}")
         self.emit(f"s_add_u32 m0, %[cd], {4096 * ii}")
-        self.emit(f"global_load_lds_dwordx4 v{CO}, %[cb]")
+        self.emit(f"global_load_lds_dwordx4 v{CT}, %[cb]")
         self.emit(f".Lnc%=_{ii}:")
 
     def copy_scales(self):
@@ -217,7 +215,7 @@ def softmax_ops(st, masked):
         ops.append([f"v_mul_f32 v{b[r]}, v{b[r]}, v{ks[r]}", f"v_mul_f32 v{b[r]}, %[qmul], v{b[r]}"])
     if masked:
         # tokens past the visible end of the scored tile; skipped when %[domask] is 0
-        lim, neg = CT, CO
+        lim, neg = T0, KT0
         grp = ["s_cmp_lg_u32 %[domask], 0", "s_cbranch_scc0 .Lnm%=",
                f"v_subrev_u32 v{lim}, %[tok], %[vlim]", f"v_mov_b32 v{neg}, {NEG_INF}"]
         for beta, regs in ((0, a), (1, b)):
@@ -227,7 +225,7 @@ def softmax_ops(st, masked):
         grp.append(".Lnm%=:")
         ops.append(grp)
     # row maximum over 32 tokens, then over the lane pair (l, l^32)
-    mx, t1, mu, ps = T0, T1, T1, T1       # (mx dies before mu is set, mu before ps)
+    mx, t1, mu, ps = T0, KT1, KT1, KT1    # (mx dies before mu is set, mu before ps)
     vals = a + b
     ops.append([f"v_max3_f32 v{mx}, v{vals[0]}, v{vals[1]}, v{vals[2]}"])
     for i in range(3, 31, 2):
@@ -245,7 +243,7 @@ def softmax_ops(st, masked):
     for r in range(2, 32):
         ops.append([f"v_add_f32 v{ps}, v{ps}, v{vals[r]}"])
     ops.append([f"v_add_f32 %[lrun], %[lrun], v{ps}"])
-    # value-side weights P' = p * kscale and their block maxima (pmax0 in T0, pmax1 in T1)
+    # value-side weights P' = p * kscale and their block maxima (pmax0 in T0, pmax1 in KT1)
     ops.append(("lds", lambda: st.kscales(0)))
     ops.append(("wait", ("ks", 0)))
     for r in range(16):
@@ -258,11 +256,11 @@ def softmax_ops(st, masked):
     ops.append(("wait", ("ks", 1)))
     for r in range(16):
         ops.append([f"v_mul_f32 v{b[r]}, v{b[r]}, v{ks[r]}"])
-    ops.append([f"v_max3_f32 v{T1}, v{b[0]}, v{b[1]}, v{b[2]}"])
+    ops.append([f"v_max3_f32 v{KT1}, v{b[0]}, v{b[1]}, v{b[2]}"])
     for i in range(3, 15, 2):
-        ops.append([f"v_max3_f32 v{T1}, v{T1}, v{b[i]}, v{b[i + 1]}"])
-    ops.append([f"v_max_f32 v{T1}, v{T1}, v{b[15]}"])
-    for t in (T0, T1):   # the token scales are done: their registers are temporaries
+        ops.append([f"v_max3_f32 v{KT1}, v{KT1}, v{b[i]}, v{b[i + 1]}"])
+    ops.append([f"v_max_f32 v{KT1}, v{KT1}, v{b[15]}"])
+    for t in (T0, KT1):  # the token scales are done: their registers are temporaries
         ops.append([f"v_mov_b32 v{ks[0]}, v{t}", "s_nop 1",
                     f"v_permlane32_swap_b32 v{ks[0]}, v{t}", f"v_max_f32 v{t}, v{ks[0]}, v{t}"])
     ops.append(("lds", lambda: spill_writes(st)))
@@ -270,19 +268,19 @@ def softmax_ops(st, masked):
 
 
 def spill_writes(st):
-    """P' (SA, SB) and its block maxima (T0, T1) to the wave's area."""
+    """P' (SA, SB) and its block maxima (T0, KT1) to the wave's area."""
     st.emit(f"v_add_u32 v{PAD}, %[sw], %[pa]")
     for g in range(8):
         acc = SA if g < 4 else SB
         st.lds(("w",), f"ds_write_b128 v{PAD}, {vr(acc + 4 * (g & 3), 4)} offset:{1024 * g}")
     st.lds(("w",), f"ds_write_b32 v{PAD}, v{T0} offset:8192")
-    st.lds(("w",), f"ds_write_b32 v{PAD}, v{T1} offset:8196")
+    st.lds(("w",), f"ds_write_b32 v{PAD}, v{KT1} offset:8196")
 
 
 def encode_setup(st):
     """Block scales of the P' being encoded, from its block maxima (in DV,
     DV+1): MYS/MYSL (E8M0 scales of the hi and lo terms of this lane's
-    K-block), div0/dlo0/div1/dlo1 (the same powers of two as floats)."""
+    K-block) and div0/div1 (the hi-term scales as floats, in place)."""
     e0, e1 = DV, DV + 1
     st.wait_for(("sm",))
     for e in (e0, e1):
@@ -296,42 +294,40 @@ def encode_setup(st):
     st.emit(f"v_cndmask_b32 v{MYS}, v{e0}, v{e1}, vcc")
     st.emit(f"v_subrev_u32 v{MYS}, 7, v{MYS}")
     st.emit(f"v_subrev_u32 v{MYSL}, 4, v{MYS}")
-    st.emit(f"v_subrev_u32 v{DV + 2}, 7, v{e1}")
-    st.emit(f"v_lshlrev_b32 v{DV + 2}, 23, v{DV + 2}")        # div1 = 2^(e1 - 134)
-    st.emit(f"v_subrev_u32 v{DV + 3}, 11, v{e1}")
-    st.emit(f"v_lshlrev_b32 v{DV + 3}, 23, v{DV + 3}")        # dlo1 = 2^(e1 - 138)
-    st.emit(f"v_subrev_u32 v{DV + 1}, 11, v{e0}")
-    st.emit(f"v_lshlrev_b32 v{DV + 1}, 23, v{DV + 1}")        # dlo0
-    st.emit(f"v_subrev_u32 v{DV}, 7, v{e0}")
-    st.emit(f"v_lshlrev_b32 v{DV}, 23, v{DV}")                # div0
+    for e in (e0, e1):
+        st.emit(f"v_subrev_u32 v{e}, 7, v{e}")
+        st.emit(f"v_lshlrev_b32 v{e}, 23, v{e}")              # div = 2^(e - 134)
 
 
 def encode_group(st, g):
-    """Two e4m3 terms of P' group g: hi codes into PH[g], lo codes into PL[g]."""
-    beta = g >> 2
-    div, dlo = DV + 2 * beta, DV + 2 * beta + 1
-    x = [XB[g & 1] + i for i in range(4)]
+    """Two e4m3 terms of P' group g: hi codes into PH[g], lo codes into PL[g];
+    the lo terms use div / 16 (the exponent field lowered by 4)."""
+    div = DV + (g >> 2)
+    x = [XB + i for i in range(4)]
     h, l = PH + g, PL + g
     st.wait_for(("sp", g))
     st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[0]}, v{x[1]}, v{div}")
     st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{h}, v{x[2]}, v{x[3]}, v{div} op_sel:[0,0,0,1]")
     st.emit(f"v_cvt_pk_f32_fp8_e32 v[{DEC}:{DEC + 1}], v{h}")
-    st.emit(f"v_cvt_pk_f32_fp8_sdwa v[{DEC + 2}:{DEC + 3}], v{h} src0_sel:WORD_1")
-    for i in range(4):
-        st.emit(f"v_fma_f32 v{x[i]}, -v{DEC + i}, v{div}, v{x[i]}")
-    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[0]}, v{x[1]}, v{dlo}")
-    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[2]}, v{x[3]}, v{dlo} op_sel:[0,0,0,1]")
+    st.emit(f"v_fma_f32 v{x[0]}, -v{DEC}, v{div}, v{x[0]}")
+    st.emit(f"v_fma_f32 v{x[1]}, -v{DEC + 1}, v{div}, v{x[1]}")
+    st.emit(f"v_cvt_pk_f32_fp8_sdwa v[{DEC}:{DEC + 1}], v{h} src0_sel:WORD_1")
+    st.emit(f"v_fma_f32 v{x[2]}, -v{DEC}, v{div}, v{x[2]}")
+    st.emit(f"v_fma_f32 v{x[3]}, -v{DEC + 1}, v{div}, v{x[3]}")
+    st.emit(f"v_subrev_u32 v{DEC}, 0x2000000, v{div}")
+    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[0]}, v{x[1]}, v{DEC}")
+    st.emit(f"v_cvt_scalef32_pk_fp8_f32 v{l}, v{x[2]}, v{x[3]}, v{DEC} op_sel:[0,0,0,1]")
 
 
 def encode_ops(st):
-    """The encoding as groups of instructions to spread between MFMAs; the
-    P' group reads run two groups ahead of their use."""
-    ops = [("lds", lambda: (st.spill_maxima(), st.spill_group(0), st.spill_group(1))),
+    """The encoding as groups of instructions to spread between MFMAs; each
+    P' group is read once the previous one is encoded."""
+    ops = [("lds", lambda: (st.spill_maxima(), st.spill_group(0))),
            ("fn", lambda: encode_setup(st))]
     for g in range(8):
         ops.append(("fn", lambda g=g: encode_group(st, g)))
-        if g + 2 < 8:
-            ops.append(("lds", lambda g=g: st.spill_group(g + 2)))
+        if g + 1 < 8:
+            ops.append(("lds", lambda g=g: st.spill_group(g + 1)))
     return ops
 
 
@@ -347,14 +343,13 @@ def run_ops(st, ops):
                 st.emit(line)
 
 
-def pv_and_next_values(st, i, vslot_of):
-    """Sum MFMA i; once column tile ct has had its lo MFMA, column tile ct + 2
-    is read into its slot."""
-    st.pv(i, vslot_of)
-    pair, r = i >> 2, i & 3
-    if r >= 2 and pair + 1 < 8:
-        ct = 2 * pair + (r & 1)
-        st.vread(ct + 2, vslot_of[ct + 2])
+def pv_and_next_values(st, i):
+    """Sum MFMA i; after the lo MFMA of column tile ct, column tile ct + 1 is
+    read into the value slot."""
+    st.pv(i)
+    ct = i >> 1
+    if i & 1 and ct + 1 < 16:
+        st.vread(ct + 1)
 
 
 def interleave(st, ops, n_slots, emit_slot):
@@ -371,7 +366,7 @@ def interleave(st, ops, n_slots, emit_slot):
 def score_phase(st, copies, enc):
     """The 36 score MFMAs of the tile at %[bk]; between them the encoding of
     the P' in the wave's area (enc), the wave's tile copies (copies) and, once
-    the encoding is done, the reads of the first two value column tiles."""
+    the encoding is done, the read of the first value column tile."""
     st.kread(0, 0, 0)
     st.kread(0, 1, 1)
     ops = encode_ops(st) if enc else []
@@ -391,8 +386,7 @@ def score_phase(st, copies, enc):
             slot(i)
             if i == n_enc:
                 st.emit(f"v_add_u32 v{VA}, %[bv], %[vo]")
-                st.vread(0, 0)
-                st.vread(1, 1)
+                st.vread(0)
     else:
         for i in range(36):
             slot(i)
@@ -400,17 +394,16 @@ def score_phase(st, copies, enc):
 
 def sum_phase(st, soft, masked):
     """The 32 sum MFMAs of the tile at %[bv] (codes in PH/PL, scales in
-    MYS/MYSL, first two value tiles already requested); between them the
+    MYS/MYSL, first value column tile already requested); between them the
     softmax of the scores just computed and its P' writes (soft)."""
-    vslot_of = {ct: ct % 2 for ct in range(16)}
     st.emit("s_nop 7")                    # encoded operands written by VALU
     if soft:
         results_ready(st)
         ops = softmax_ops(st, masked)
-        interleave(st, ops, 32, lambda i: pv_and_next_values(st, i, vslot_of))
+        interleave(st, ops, 32, lambda i: pv_and_next_values(st, i))
     else:
         for i in range(32):
-            pv_and_next_values(st, i, vslot_of)
+            pv_and_next_values(st, i)
     st.wait_all()
     results_ready(st)
 
@@ -443,8 +436,7 @@ def last():
     setup(st, False, False)
     run_ops(st, encode_ops(st))
     st.emit(f"v_add_u32 v{VA}, %[bv], %[vo]")
-    st.vread(0, 0)
-    st.vread(1, 1)
+    st.vread(0)
     sum_phase(st, False, False)
     return st.text()
 
