@@ -460,7 +460,8 @@ decode_fp8_pipe_kernel(Fp8Params p) {
       const int pos = 64 * i + lane, r = pos / 72, c = (pos % 72) ^ (r & 6);
       dma16_sv(qsrc, r * (2 * kD) + 16 * c, slot + 1024 * i);
     }
-    qmul = p.q_scale[qrow0 + tq] * p.scale_log2;
+    // kept positive: the streams take the row maximum of S * kscale before scaling by it
+    qmul = fmaxf(p.q_scale[qrow0 + tq] * p.scale_log2, 1.17549435e-38f);
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     MLA_LDS const char* qrow = tiles + wave * kTileBytes + 16 * (72 * tq);

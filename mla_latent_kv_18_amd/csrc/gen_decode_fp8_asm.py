@@ -38,7 +38,8 @@ Operands (named in the kernel):
   %[bk], %[bv]    LDS byte address of the scored tile and of the summed tile
   %[sw]           LDS byte address of this wave's P' area (9216 B: value
                   group g at 1024*g + 16*lane, block maxima at 8192 + 16*lane)
-  %[qmul]         per-head qscale * softmax scale * log2(e)
+  %[qmul]         per-head qscale * softmax scale * log2(e), at least the
+                  smallest normal float (the streams rely on qmul > 0)
   %[mref], %[mseen], %[lrun], %[exc]  per-head softmax state (in/out)
   %[vlim], %[tok], %[domask]  token t (0..63) of the scored tile is visible
                   iff t < vlim - tok; the mask is applied when domask != 0
@@ -57,10 +58,13 @@ T0 = 181                              # temporary (copy offset while copying)
 MYS, MYSL = 182, 183                  # E8M0 scales of the P' codes (hi, lo)
 PH, PL = 184, 192                     # P' codes being summed (8 VGPRs each)
 KF = [200, 208]                       # key operand slots (8 VGPRs each)
-VF = 216                              # value operand slot (8 VGPRs)
+VF = 216                              # value operand slot of even column tiles (8 VGPRs)
+VF2 = 208                             # ... of odd column tiles: the upper key slot, free once scores are done
 SA, SB = 224, 240                     # score accumulators (beta 0, 1)
 KS = list(range(200, 216))            # token scales, in the key slots once scores are done
 KT0, KT1 = KS[0], KS[1]               # softmax temporaries while the key slots hold no scales
+# the token scales pass through KS[0..7] four at a time (two buffers), so
+# that KS[8..15] can hold the second value operand
 SCA = KA[0]                           # token-scale read address (keys are done by then)
 PAD = KA[1]                           # P' area address when P' is written (keys are done)
 CT = T0                               # copy offset
@@ -111,13 +115,13 @@ class Stream:
         self.lds(("k", s, beta), f"ds_read_b128 {vr(base + 4, 4)}, v{KA[1]} offset:{off}")
 
     def vread(self, ct):
-        base = VF
+        base = VF if ct % 2 == 0 else VF2
         for j in range(4):
             self.lds(("v", ct), f"ds_read_b64_tr_b8 {vr(base + 2 * j, 2)}, v{VA} offset:{512 * ct + 9216 * j}")
 
-    def kscales(self, beta):
-        for a4 in range(4):
-            self.lds(("ks", beta), f"ds_read_b128 {vr(KS[4 * a4], 4)}, v{SCA} offset:{128 * beta + 32 * a4}")
+    def kchunk(self, tag, c):
+        # token scales of block c >> 2, lane tokens 8(c & 3) + 4hf .. +3, into buffer c & 1
+        self.lds((tag, c), f"ds_read_b128 {vr(KS[4 * (c & 1)], 4)}, v{SCA} offset:{128 * (c >> 2) + 32 * (c & 3)}")
 
     def spill_maxima(self):
         # block maxima of the P' being encoded (pmax0, pmax1 per lane)
@@ -139,11 +143,15 @@ class Stream:
                   f"v{S127}, v{sb} op_sel_hi:[0,0,0]")
 
     def pv(self, i):
-        # MFMA i: column tile i >> 1, hi codes (even i) or lo codes (odd i)
-        ct, lo = i >> 1, i & 1
+        # MFMA i: column-tile pair i >> 2 in the order (ct, hi), (ct+1, hi),
+        # (ct, lo), (ct+1, lo); even column tiles in VF, odd ones in VF2
+        pair, r = i >> 2, i & 3
+        ct = 2 * pair + (r & 1)
+        lo = r >= 2
         self.wait_for(("v", ct))
         p, sc = (PL, MYSL) if lo else (PH, MYS)
-        self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{ct}], {vr(VF)}, {vr(p)}, %[o{ct}], "
+        v = VF if ct % 2 == 0 else VF2
+        self.emit(f"v_mfma_scale_f32_32x32x64_f8f6f4 %[o{ct}], {vr(v)}, {vr(p)}, %[o{ct}], "
                   f"v{S127}, v{sc} op_sel_hi:[0,0,0]")
 
     def copy(self, ii):
@@ -192,6 +200,19 @@ def results_ready(st):
     st.emit("s_nop 3")
 
 
+def scale_ops(st, ops, tag, a, b):
+    """Multiply a[r] (block 0) and b[r] (block 1) by their token scales, read
+    four at a time into two alternating buffers, two chunks ahead."""
+    ops.append(("lds", lambda: (st.kchunk(tag, 0), st.kchunk(tag, 1))))
+    for c in range(8):
+        ops.append(("wait", (tag, c)))
+        regs = (a if c < 4 else b)[4 * (c & 3):4 * (c & 3) + 4]
+        buf = KS[4 * (c & 1):4 * (c & 1) + 4]
+        ops.append([f"v_mul_f32 v{regs[i]}, v{regs[i]}, v{buf[i]}" for i in range(4)])
+        if c + 2 < 8:
+            ops.append(("lds", lambda c=c: st.kchunk(tag, c + 2)))
+
+
 def softmax_ops(st, masked):
     """VALU work on the two score accumulators up to the value-side weights
     P' = p * kscale (in SA, SB) and their per-block maxima; list of groups of
@@ -200,19 +221,11 @@ def softmax_ops(st, masked):
     b = [SB + r for r in range(16)]
     ks = KS
     ops = []
-    # s = S * kscale * qmul, block by block (token scales of the scored tile)
-    ops.append(("lds", lambda: (st.emit(f"v_lshrrev_b32 v{T0}, 9, %[pa]"),
-                                st.emit(f"v_lshl_add_u32 v{SCA}, v{T0}, 4, %[bks]"),
-                                st.kscales(0))))
-    ops.append(("wait", ("ks", 0)))
-    for r in range(16):
-        ops.append([f"v_mul_f32 v{a[r]}, v{a[r]}, v{ks[r]}"])
-    ops.append(("lds", lambda: st.kscales(1)))
-    for r in range(16):
-        ops.append([f"v_mul_f32 v{a[r]}, %[qmul], v{a[r]}"])
-    ops.append(("wait", ("ks", 1)))
-    for r in range(16):
-        ops.append([f"v_mul_f32 v{b[r]}, v{b[r]}, v{ks[r]}", f"v_mul_f32 v{b[r]}, %[qmul], v{b[r]}"])
+    # t = S * kscale, block by block (token scales of the scored tile); the
+    # per-head factor qmul > 0 is applied to the maximum and inside the
+    # exponent's fma (s = t * qmul)
+    ops.append([f"v_lshrrev_b32 v{T0}, 9, %[pa]", f"v_lshl_add_u32 v{SCA}, v{T0}, 4, %[bks]"])
+    scale_ops(st, ops, "ks", a, b)
     if masked:
         # tokens past the visible end of the scored tile; skipped when %[domask] is 0
         lim, neg = T0, KT0
@@ -230,7 +243,7 @@ def softmax_ops(st, masked):
     ops.append([f"v_max3_f32 v{mx}, v{vals[0]}, v{vals[1]}, v{vals[2]}"])
     for i in range(3, 31, 2):
         ops.append([f"v_max3_f32 v{mx}, v{mx}, v{vals[i]}, v{vals[i + 1]}"])
-    ops.append([f"v_max_f32 v{mx}, v{mx}, v{vals[31]}"])
+    ops.append([f"v_max_f32 v{mx}, v{mx}, v{vals[31]}", f"v_mul_f32 v{mx}, %[qmul], v{mx}"])
     ops.append([f"v_mov_b32 v{t1}, v{mx}", "s_nop 1",
                 f"v_permlane32_swap_b32 v{t1}, v{mx}", f"v_max_f32 v{mx}, v{t1}, v{mx}"])
     ops.append([f"v_max_f32 %[mseen], %[mseen], v{mx}"])
@@ -238,24 +251,17 @@ def softmax_ops(st, masked):
     ops.append([f"v_sub_f32 v{t1}, v{mx}, %[mref]", f"v_max_f32 %[exc], %[exc], v{t1}"])
     ops.append([f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", f"v_cndmask_b32_e64 v{mu}, %[mref], 0, vcc"])
     for r in range(32):
-        ops.append([f"v_sub_f32 v{vals[r]}, v{vals[r]}, v{mu}", f"v_exp_f32 v{vals[r]}, v{vals[r]}"])
+        ops.append([f"v_fma_f32 v{vals[r]}, v{vals[r]}, %[qmul], -v{mu}", f"v_exp_f32 v{vals[r]}, v{vals[r]}"])
     ops.append([f"v_add_f32 v{ps}, v{vals[0]}, v{vals[1]}"])
     for r in range(2, 32):
         ops.append([f"v_add_f32 v{ps}, v{ps}, v{vals[r]}"])
     ops.append([f"v_add_f32 %[lrun], %[lrun], v{ps}"])
     # value-side weights P' = p * kscale and their block maxima (pmax0 in T0, pmax1 in KT1)
-    ops.append(("lds", lambda: st.kscales(0)))
-    ops.append(("wait", ("ks", 0)))
-    for r in range(16):
-        ops.append([f"v_mul_f32 v{a[r]}, v{a[r]}, v{ks[r]}"])
-    ops.append(("lds", lambda: st.kscales(1)))
+    scale_ops(st, ops, "kp", a, b)
     ops.append([f"v_max3_f32 v{T0}, v{a[0]}, v{a[1]}, v{a[2]}"])
     for i in range(3, 15, 2):
         ops.append([f"v_max3_f32 v{T0}, v{T0}, v{a[i]}, v{a[i + 1]}"])
     ops.append([f"v_max_f32 v{T0}, v{T0}, v{a[15]}"])
-    ops.append(("wait", ("ks", 1)))
-    for r in range(16):
-        ops.append([f"v_mul_f32 v{b[r]}, v{b[r]}, v{ks[r]}"])
     ops.append([f"v_max3_f32 v{KT1}, v{b[0]}, v{b[1]}, v{b[2]}"])
     for i in range(3, 15, 2):
         ops.append([f"v_max3_f32 v{KT1}, v{KT1}, v{b[i]}, v{b[i + 1]}"])
@@ -344,12 +350,12 @@ def run_ops(st, ops):
 
 
 def pv_and_next_values(st, i):
-    """Sum MFMA i; after the lo MFMA of column tile ct, column tile ct + 1 is
-    read into the value slot."""
+    """Sum MFMA i; once column tile ct has had its lo MFMA, column tile ct + 2
+    is read into its slot."""
     st.pv(i)
-    ct = i >> 1
-    if i & 1 and ct + 1 < 16:
-        st.vread(ct + 1)
+    pair, r = i >> 2, i & 3
+    if r >= 2 and pair + 1 < 8:
+        st.vread(2 * pair + (r & 1) + 2)
 
 
 def interleave(st, ops, n_slots, emit_slot):
@@ -392,10 +398,13 @@ def score_phase(st, copies, enc):
             slot(i)
 
 
-def sum_phase(st, soft, masked):
+def sum_phase(st, soft, masked, second_value=True):
     """The 32 sum MFMAs of the tile at %[bv] (codes in PH/PL, scales in
-    MYS/MYSL, first value column tile already requested); between them the
-    softmax of the scores just computed and its P' writes (soft)."""
+    MYS/MYSL, value column tile 0 already requested, tile 1 requested here);
+    between them the softmax of the scores just computed and its P' writes
+    (soft)."""
+    if second_value:
+        st.vread(1)                       # the upper key slot is free once scores are done
     st.emit("s_nop 7")                    # encoded operands written by VALU
     if soft:
         results_ready(st)
