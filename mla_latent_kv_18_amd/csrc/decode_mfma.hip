@@ -630,15 +630,19 @@ decode_bf16_pipe_kernel(DecodeParams p) {
 // are requested together, before the request's length is known: slots of
 // splits past that length hold stale workspace contents and are masked out
 // after loading rather than skipped, so the common case costs one memory
-// round trip.  Further splits follow in batches of 8.
+// round trip.  Further splits follow in batches of 8.  With xcd_group the
+// rows of request b run on XCD b % 8, where the pipelined kernel wrote the
+// request's partials, so that their reads can hit that XCD's L2.
 template <typename OutT>
 __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ o_part,
                                                      const float* __restrict__ lse_part,
                                                      const int32_t* __restrict__ seq_lens,
                                                      int num_splits, int split_tokens, int q_len,
                                                      int n_h, int max_seq_len, OutT* __restrict__ o_lat,
-                                                     float* __restrict__ lse) {
-  const int row = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+                                                     float* __restrict__ lse, int xcd_group) {
+  int row = blockIdx.x, b = blockIdx.y;
+  if (xcd_group) xcd_slot(b, row);  // the XCD whose L2 took the request's partials
+  const int lane = threadIdx.x;
   const int rows = q_len * n_h;
   const int64_t base = static_cast<int64_t>(b) * num_splits * rows + row;
   auto lse_of = [&](int s) { return lse_part[base + static_cast<int64_t>(s) * rows]; };
@@ -754,17 +758,17 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_bf16_kernel<2, 2>), grid, dim3(128), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.num_splits == 1) return e;
-  return launch_combine(a, st);
+  return launch_combine(a, st, p.xcd_group != 0);
 }
 
-hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st, bool xcd_group) {
   const size_t rows = static_cast<size_t>(a.batch) * a.num_splits * a.q_len * a.n_h;
   const __bf16* o_part = static_cast<const __bf16*>(a.workspace);
   const float* lse_part = reinterpret_cast<const float*>(o_part + rows * kDc);
   const dim3 cgrid(a.q_len * a.n_h, a.batch);
   hipLaunchKernelGGL((combine_kernel<__bf16>), cgrid, dim3(64), 0, st, o_part, lse_part, a.seq_lens,
                      a.num_splits, a.split_tokens, a.q_len, a.n_h, a.max_seq_len,
-                     static_cast<__bf16*>(a.o_lat), a.lse);
+                     static_cast<__bf16*>(a.o_lat), a.lse, xcd_group && a.batch % 8 == 0 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -78,6 +78,7 @@ size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits);
 hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
 hipError_t launch_decode_fp8(const DecodeArgs&, hipStream_t);
 // merge of the chunk partials that a split decode left in the workspace
-hipError_t launch_combine(const DecodeArgs&, hipStream_t);
+// (xcd_group: the partials of request b were written on XCD b % 8, batch % 8 == 0)
+hipError_t launch_combine(const DecodeArgs&, hipStream_t, bool xcd_group = false);
 
 }  // namespace mla
