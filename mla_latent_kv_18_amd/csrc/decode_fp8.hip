@@ -553,9 +553,11 @@ decode_fp8_pipe_kernel(Fp8Params p) {
     int blk_next = n_tiles > 3 ? block_of(3) : 0;
     for (int k = 0; k + 1 < n_tiles; ++k) {
       const int64_t first = first_next;
-      wait_vmcnt<0>();                      // tile k+1 landed
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();        // tile k+1 visible; tile k-1 released by all waves
+      // Tile k+1 landed and visible; tile k-1 released by all waves: every
+      // LDS read of a shared buffer was waited for inside the streams, and
+      // what may still be in flight are the wave's own P' writes.
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
       const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k);
       const int tok = kTileT * (k + 1);
       // Tile k+2 is copied while it exists.  The scored tile k+1 needs the

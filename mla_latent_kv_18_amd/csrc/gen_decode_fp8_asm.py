@@ -219,7 +219,6 @@ def softmax_ops(st, masked):
     instructions (LDS reads are issued through st so that waits are counted)."""
     a = [SA + r for r in range(16)]
     b = [SB + r for r in range(16)]
-    ks = KS
     ops = []
     # t = S * kscale, block by block (token scales of the scored tile); the
     # per-head factor qmul > 0 is applied to the maximum and inside the
@@ -237,38 +236,46 @@ def softmax_ops(st, masked):
                 grp += [f"v_cmp_lt_i32 vcc, {t}, v{lim}", f"v_cndmask_b32 v{regs[r]}, v{neg}, v{regs[r]}, vcc"]
         grp.append(".Lnm%=:")
         ops.append(grp)
-    # row maximum over 32 tokens, then over the lane pair (l, l^32)
-    mx, t1, mu, ps = T0, KT1, KT1, KT1    # (mx dies before mu is set, mu before ps)
-    vals = a + b
-    ops.append([f"v_max3_f32 v{mx}, v{vals[0]}, v{vals[1]}, v{vals[2]}"])
-    for i in range(3, 31, 2):
-        ops.append([f"v_max3_f32 v{mx}, v{mx}, v{vals[i]}, v{vals[i + 1]}"])
-    ops.append([f"v_max_f32 v{mx}, v{mx}, v{vals[31]}", f"v_mul_f32 v{mx}, %[qmul], v{mx}"])
+    # row maximum over 32 tokens (two interleaved chains, T0 over block 0 and
+    # KT0 over block 1), then over the lane pair (l, l^32)
+    mx, t1, mu = T0, KT1, KT1             # (t1 dies before mu is set)
+
+    def max_chains(acc_a, acc_b, last):
+        chains = []
+        for acc, v in ((acc_a, a), (acc_b, b)):
+            c = [f"v_max3_f32 v{acc}, v{v[0]}, v{v[1]}, v{v[2]}"]
+            c += [f"v_max3_f32 v{acc}, v{acc}, v{v[i]}, v{v[i + 1]}" for i in range(3, 15, 2)]
+            c.append(f"v_max_f32 v{acc}, v{acc}, v{v[15]}")
+            chains.append(c)
+        for x, y in zip(*chains):
+            ops.append([x, y])
+        ops.append(last)
+
+    max_chains(mx, KT0, [f"v_max_f32 v{mx}, v{mx}, v{KT0}", f"v_mul_f32 v{mx}, %[qmul], v{mx}"])
     ops.append([f"v_mov_b32 v{t1}, v{mx}", "s_nop 1",
                 f"v_permlane32_swap_b32 v{t1}, v{mx}", f"v_max_f32 v{mx}, v{t1}, v{mx}"])
     ops.append([f"v_max_f32 %[mseen], %[mseen], v{mx}"])
     ops.append([f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", f"v_cndmask_b32 %[mref], %[mref], v{mx}, vcc"])
     ops.append([f"v_sub_f32 v{t1}, v{mx}, %[mref]", f"v_max_f32 %[exc], %[exc], v{t1}"])
     ops.append([f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", f"v_cndmask_b32_e64 v{mu}, %[mref], 0, vcc"])
-    for r in range(32):
-        ops.append([f"v_fma_f32 v{vals[r]}, v{vals[r]}, %[qmul], -v{mu}", f"v_exp_f32 v{vals[r]}, v{vals[r]}"])
-    ops.append([f"v_add_f32 v{ps}, v{vals[0]}, v{vals[1]}"])
-    for r in range(2, 32):
-        ops.append([f"v_add_f32 v{ps}, v{ps}, v{vals[r]}"])
-    ops.append([f"v_add_f32 %[lrun], %[lrun], v{ps}"])
+    vals = a + b
+    for r0 in range(0, 32, 4):   # four fmas, then their four exponentials
+        ops.append([f"v_fma_f32 v{vals[r]}, v{vals[r]}, %[qmul], -v{mu}" for r in range(r0, r0 + 4)] +
+                   [f"v_exp_f32 v{vals[r]}, v{vals[r]}" for r in range(r0, r0 + 4)])
+    # row sum in four partial sums (KS[0..3]: no token scales are held now)
+    ps = KS[0:4]
+    ops.append([f"v_add_f32 v{ps[j]}, v{vals[j]}, v{vals[j + 4]}" for j in range(4)])
+    for r0 in range(8, 32, 4):
+        ops.append([f"v_add_f32 v{ps[j]}, v{ps[j]}, v{vals[r0 + j]}" for j in range(4)])
+    ops.append([f"v_add_f32 v{ps[0]}, v{ps[0]}, v{ps[1]}", f"v_add_f32 v{ps[2]}, v{ps[2]}, v{ps[3]}",
+                f"v_add_f32 v{ps[0]}, v{ps[0]}, v{ps[2]}", f"v_add_f32 %[lrun], %[lrun], v{ps[0]}"])
     # value-side weights P' = p * kscale and their block maxima (pmax0 in T0, pmax1 in KT1)
     scale_ops(st, ops, "kp", a, b)
-    ops.append([f"v_max3_f32 v{T0}, v{a[0]}, v{a[1]}, v{a[2]}"])
-    for i in range(3, 15, 2):
-        ops.append([f"v_max3_f32 v{T0}, v{T0}, v{a[i]}, v{a[i + 1]}"])
-    ops.append([f"v_max_f32 v{T0}, v{T0}, v{a[15]}"])
-    ops.append([f"v_max3_f32 v{KT1}, v{b[0]}, v{b[1]}, v{b[2]}"])
-    for i in range(3, 15, 2):
-        ops.append([f"v_max3_f32 v{KT1}, v{KT1}, v{b[i]}, v{b[i + 1]}"])
-    ops.append([f"v_max_f32 v{KT1}, v{KT1}, v{b[15]}"])
+    max_chains(T0, KT1, [])
+    ops.pop()
     for t in (T0, KT1):  # the token scales are done: their registers are temporaries
-        ops.append([f"v_mov_b32 v{ks[0]}, v{t}", "s_nop 1",
-                    f"v_permlane32_swap_b32 v{ks[0]}, v{t}", f"v_max_f32 v{t}, v{ks[0]}, v{t}"])
+        ops.append([f"v_mov_b32 v{KT0}, v{t}", "s_nop 1",
+                    f"v_permlane32_swap_b32 v{KT0}, v{t}", f"v_max_f32 v{t}, v{KT0}, v{t}"])
     ops.append(("lds", lambda: spill_writes(st)))
     return ops
 
@@ -358,14 +365,35 @@ def pv_and_next_values(st, i):
         st.vread(2 * pair + (r & 1) + 2)
 
 
-def interleave(st, ops, n_slots, emit_slot):
-    """emit_slot(i) for i < n_slots, the op groups spread evenly before them."""
+def flatten(ops):
+    """Instruction groups split into single instructions (groups holding a
+    branch stay whole), so that interleave() spreads VALU work by count."""
+    out = []
+    for op in ops:
+        if isinstance(op, list) and not any(l.startswith("s_cbranch") or l.endswith(":") or l.startswith("s_nop")
+                                            for l in op):
+            out.extend([l] for l in op)
+        else:
+            out.append(op)
+    return out
+
+
+def interleave(st, ops, n_slots, emit_slot, mfma_first):
+    """emit_slot(i) for i < n_slots with the ops spread evenly between them.
+    With mfma_first each MFMA issues before the waits and VALU work of its
+    slot, so that it runs while they wait (the sum phase, whose softmax waits
+    on token-scale reads); otherwise the slot's ops come first (the score
+    phase, whose encoding reads were issued a slot earlier)."""
+    ops = flatten(ops)
     n, j = len(ops), 0
     for i in range(n_slots):
+        if mfma_first:
+            emit_slot(i)
         target = -(-(i + 1) * n // n_slots)
         run_ops(st, ops[j:target])
         j = target
-        emit_slot(i)
+        if not mfma_first:
+            emit_slot(i)
     run_ops(st, ops[j:])
 
 
@@ -387,7 +415,7 @@ def score_phase(st, copies, enc):
         if j == 3 and copies:
             st.copy(s)
     if enc:
-        interleave(st, ops, n_enc, slot)
+        interleave(st, ops, n_enc, slot, False)
         for i in range(n_enc, 36):
             slot(i)
             if i == n_enc:
@@ -398,23 +426,25 @@ def score_phase(st, copies, enc):
             slot(i)
 
 
-def sum_phase(st, soft, masked, second_value=True):
+def sum_phase(st, soft, masked, second_value=True, final_wait=True):
     """The 32 sum MFMAs of the tile at %[bv] (codes in PH/PL, scales in
     MYS/MYSL, value column tile 0 already requested, tile 1 requested here);
     between them the softmax of the scores just computed and its P' writes
-    (soft)."""
+    (soft).  Without final_wait the stream may end with this wave's P'
+    writes in flight: only the wave itself reads them, in order."""
     if second_value:
         st.vread(1)                       # the upper key slot is free once scores are done
     st.emit("s_nop 7")                    # encoded operands written by VALU
     if soft:
         results_ready(st)
         ops = softmax_ops(st, masked)
-        interleave(st, ops, 32, lambda i: pv_and_next_values(st, i))
+        interleave(st, ops, 32, lambda i: pv_and_next_values(st, i), True)
     else:
         for i in range(32):
             pv_and_next_values(st, i)
-    st.wait_all()
-    results_ready(st)
+    if final_wait:
+        st.wait_all()
+        results_ready(st)
 
 
 def step():
@@ -424,7 +454,7 @@ def step():
     setup(st, True, False)
     st.copy_scales()
     score_phase(st, True, True)
-    sum_phase(st, True, True)
+    sum_phase(st, True, True, final_wait=False)
     return st.text()
 
 
