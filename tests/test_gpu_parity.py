@@ -110,6 +110,8 @@ SMALL_BF16 = {
     "v3_two_queries": dict(batch=2, lens=(70, 129), q_len=2),
     "kimi_heads64": dict(n_h=64, batch=3, lens=(33, 64, 300), shuffle=True),
     "kimi_heads64_q2": dict(n_h=64, batch=2, lens=(2, 200), q_len=2),
+    # a batch of 8: each request's chunks share an XCD and so do its merge rows
+    "v3_batch8_grouped": dict(batch=8, lens=(1, 2, 63, 64, 65, 500, 1000, 2048), shuffle=True),
 }
 
 
@@ -144,14 +146,18 @@ def test_split_and_paging_invariance_and_determinism():
     assert d <= 1e-6, f"block-table permutation changes o_lat by {d}"
 
 
-def test_empty_request_gives_zero_and_neg_inf():
-    w = WORKLOADS["v3_bs64_ctx4k"].scaled(name="empty", batch=2, lens=(0, 50), seed=9)
+@pytest.mark.parametrize("lens", [(0, 50), (0, 50, 0, 1, 100, 0, 64, 65)])
+def test_empty_request_gives_zero_and_neg_inf(lens):
+    # the batch of 8 runs with each request's chunks and merge rows on one XCD
+    w = WORKLOADS["v3_bs64_ctx4k"].scaled(name="empty", batch=len(lens), lens=lens, seed=9)
     for st in (0, 64):
         gen, step = _run(w, st)
-        o = step.o_lat[0].float()
-        assert torch.all(o == 0).item()
-        assert torch.all(torch.isneginf(step.lse[0])).item()
-        check_request(step, gen, 1, list(range(w.n_h)), ov.TOL["bf16"], 2e-2)
+        for b, T in enumerate(lens):
+            if T == 0:
+                assert torch.all(step.o_lat[b].float() == 0).item()
+                assert torch.all(torch.isneginf(step.lse[b])).item()
+            else:
+                check_request(step, gen, b, list(range(w.n_h)), ov.TOL["bf16"], 2e-2)
 
 
 SMALL_FP8 = {
