@@ -1,0 +1,123 @@
+"""GPU parity of the three per-step projections, each called alone through
+the C ABI at token counts that cover one and two 32-token tiles per pass,
+ragged tails and several passes, against the float64 oracle:
+
+  mla_append_latent -> cache rows (RMSNorm latent, RoPE key) at the slots
+  mla_absorb_q      -> latent query rows (bf16, or the two e4m3 planes)
+  mla_out_proj      -> per-head W^UV products
+
+Bar: max|err| <= tol * max|ref| (2e-2 bf16, 6e-2 fp8).  Inputs are seeded
+N(0,1) activations and N(0,1)/sqrt(fan_in) weights, rounded to bf16 on the
+host; the oracle is fed the rounded values.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs
+from oracle import mla_ref as ref
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mla_latent_kv_18_amd as mla
+
+N_H, D_C, D_H, D_R, D_V = 64, 512, 128, 64, 128
+TOKENS = (1, 31, 32, 33, 64, 65, 100, 300)
+TOL = {"bf16": 2e-2, "fp8": 6e-2}
+
+
+def _bf16(rng, shape, scale=1.0):
+    """Seeded values rounded to bf16: (device tensor, float64 host copy)."""
+    t = torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * np.float32(scale)).bfloat16()
+    host = codecs.bf16_decode(t.view(torch.int16).numpy().view(np.uint16))
+    return t.cuda(), host
+
+
+def _rel_err(got, want):
+    return float(np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30))
+
+
+def _host_bf16(t):
+    return codecs.bf16_decode(t.cpu().view(torch.int16).numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("d_model", [448, 7168])
+@pytest.mark.parametrize("n", TOKENS)
+def test_append_rows(n, d_model, cache_dtype):
+    rng = np.random.default_rng(1000 + n)
+    dims = mla.make_dims(N_H, D_C, D_H, D_R, D_V, d_model, 64, cache_dtype, "bf16")
+    h, h64 = _bf16(rng, (n, d_model))
+    w, w64 = _bf16(rng, (D_C + D_R, d_model), 1.0 / np.sqrt(d_model))
+    gamma64 = 1.0 + 0.1 * rng.standard_normal(D_C)
+    gamma = torch.from_numpy(gamma64.astype(np.float32)).cuda()
+    pos64 = rng.integers(0, 131072, n)
+    pos = torch.from_numpy(pos64.astype(np.int32)).cuda()
+    n_blocks = (2 * n + 63) // 64
+    slots64 = rng.permutation(n_blocks * 64)[:n]
+    slots64[0] = -1 if n > 1 else slots64[0]   # a padding token: written nowhere
+    slots = torch.from_numpy(slots64.astype(np.int64)).cuda()
+    if cache_dtype == "fp8":
+        cache = torch.zeros(n_blocks, 64, D_C + D_R, dtype=torch.uint8, device="cuda")
+        scale = torch.zeros(n_blocks * 64, dtype=torch.float32, device="cuda")
+    else:
+        cache = torch.zeros(n_blocks, 64, D_C + D_R, dtype=torch.bfloat16, device="cuda")
+        scale = None
+    mla.append_latent(dims, h, w, gamma, pos, slots, cache, scale)
+    torch.cuda.synchronize()
+    c_ref, kr_ref = ref.latent_rows(h64, w64, gamma64, pos64, D_C, 1e-6, 10000.0)
+    want = np.concatenate([c_ref, kr_ref], axis=-1)
+    flat = cache.reshape(-1, D_C + D_R).cpu()
+    if cache_dtype == "fp8":
+        rows = codecs.e4m3_dequantize_rows(flat.numpy(), scale.cpu().numpy().astype(np.float64))
+    else:
+        rows = _host_bf16(flat)
+    keep = slots64 >= 0
+    got = rows[slots64[keep]]
+    assert _rel_err(got[:, :D_C], want[keep, :D_C]) <= TOL[cache_dtype], "latent"
+    assert _rel_err(got[:, D_C:], want[keep, D_C:]) <= TOL[cache_dtype], "rope key"
+    # every slot not named by a token is untouched
+    untouched = np.setdiff1d(np.arange(flat.shape[0]), slots64[keep])
+    assert not np.any(rows[untouched]), "rows outside the slot mapping were written"
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("n", TOKENS)
+def test_absorb_rows(n, cache_dtype):
+    rng = np.random.default_rng(2000 + n)
+    dims = mla.make_dims(N_H, D_C, D_H, D_R, D_V, 1024, 64, cache_dtype, "bf16")
+    q_nope, qn64 = _bf16(rng, (n, N_H, D_H))
+    q_pe, qp64 = _bf16(rng, (n, N_H, D_R))
+    w_uk, wuk64 = _bf16(rng, (N_H, D_H, D_C), 1.0 / np.sqrt(D_H))
+    pos64 = rng.integers(0, 131072, n)
+    pos = torch.from_numpy(pos64.astype(np.int32)).cuda()
+    want = ref.absorb_q(qn64, qp64, pos64, wuk64)
+    if cache_dtype == "fp8":
+        q_lat = torch.empty(n, N_H, 2 * (D_C + D_R), dtype=torch.uint8, device="cuda")
+        q_scale = torch.empty(n, N_H, dtype=torch.float32, device="cuda")
+        mla.absorb_q(dims, q_nope, q_pe, w_uk, pos, q_lat, q_scale)
+        torch.cuda.synchronize()
+        planes = codecs.e4m3_decode(q_lat.cpu().numpy())
+        D = D_C + D_R
+        got = (planes[..., :D] + planes[..., D:] / 16.0) * q_scale.cpu().numpy().astype(np.float64)[..., None]
+    else:
+        q_lat = torch.empty(n, N_H, D_C + D_R, dtype=torch.bfloat16, device="cuda")
+        mla.absorb_q(dims, q_nope, q_pe, w_uk, pos, q_lat)
+        torch.cuda.synchronize()
+        got = _host_bf16(q_lat)
+    assert _rel_err(got[..., :D_C], want[..., :D_C]) <= TOL[cache_dtype], "latent part"
+    assert _rel_err(got[..., D_C:], want[..., D_C:]) <= TOL[cache_dtype], "rope part"
+
+
+@pytest.mark.parametrize("n", TOKENS)
+def test_out_proj_rows(n):
+    rng = np.random.default_rng(3000 + n)
+    dims = mla.make_dims(N_H, D_C, D_H, D_R, D_V, 1024, 64, "bf16", "bf16")
+    o_lat, o64 = _bf16(rng, (n, N_H, D_C))
+    w_uv, wuv64 = _bf16(rng, (N_H, D_V, D_C), 1.0 / np.sqrt(D_C))
+    out = torch.empty(n, N_H, D_V, dtype=torch.bfloat16, device="cuda")
+    mla.out_proj(dims, o_lat, w_uv, out)
+    torch.cuda.synchronize()
+    assert _rel_err(_host_bf16(out), ref.out_proj(o64, wuv64)) <= TOL["bf16"]
