@@ -17,6 +17,8 @@
  *   mla_decode         scores over [c^KV ; k^R], softmax, latent-weighted sum
  *                      (split over the context, then a combine kernel)
  *   mla_out_proj       o_i = W^UV_i o_lat_i
+ *   mla_linear         the dense projections around them (query path
+ *                      W^DQ, W^UQ, W^QR; output W^O or the absorbed B_i)
  *
  * Conventions
  *   - All tensors are dense row-major; every pointer argument except those
@@ -196,6 +198,29 @@ int32_t mla_decode_default_split(const mla_dims_t* dims, int32_t batch, int32_t 
  * o_lat: [n_tokens, n_h, d_c], out: [n_tokens, n_h, d_v], act_dtype. */
 mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv,
                           int32_t n_tokens, void* out, mla_stream_t stream);
+
+/* --------------------------------------------------------------- linear
+ * The dense projections on either side of the four calls above, as one
+ * skinny bf16 GEMM (fp32 accumulation):
+ *   y[m, :] = W x[m, :]        y = x W^T,  x: [m, k], w: [n, k], y: [m, n]
+ * It serves the query path [MLA explainer, query-compression section
+ * eq.(17): c^Q = W^DQ h, q^C = W^UQ c^Q; decoupled RoPE section eq.(15):
+ * the RoPE query part is RoPE(W^QR c^Q), rotated by mla_absorb_q] and the
+ * output projection [MLA explainer, value-side absorption eq.(11): u =
+ * sum_i W^O_i o_i, i.e. x = out viewed as [m, n_h * d_v] and w = W^O; or,
+ * absorbed, u = sum_i B_i o_lat_i with B_i = W^O_i W^UV_i, x = o_lat viewed
+ * as [m, n_h * d_c] and w = [B_1 ... B_nh]].
+ * x, w, y: row-major bf16 device buffers, owned by the caller; m >= 1,
+ * n a multiple of 128, k a multiple of 16.  m = 0 returns MLA_OK and
+ * launches nothing.
+ * workspace: at least mla_linear_workspace_size(m, n, k) bytes of device
+ * memory (fp32 partial sums over slices of k; may be NULL if that is 0).
+ * Other shapes return MLA_ERR_UNSUPPORTED, NULL buffers
+ * MLA_ERR_INVALID_ARGUMENT, a short workspace MLA_ERR_WORKSPACE_TOO_SMALL;
+ * nothing is launched then. */
+size_t mla_linear_workspace_size(int32_t m, int32_t n, int32_t k);
+mla_status_t mla_linear(const void* x, const void* w, int32_t m, int32_t n, int32_t k, void* y,
+                        void* workspace, size_t workspace_bytes, mla_stream_t stream);
 
 /* ------------------------------------------------------------ diagnostics */
 const char* mla_status_string(mla_status_t status);

@@ -23,8 +23,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
 # every entry point declared in include/mla.h
 EXPORTS = ("mla_cache_row_bytes", "mla_q_lat_row_bytes", "mla_append_workspace_size", "mla_append_latent",
            "mla_absorb_workspace_size", "mla_absorb_q", "mla_decode_workspace_size",
-           "mla_decode", "mla_decode_default_split", "mla_out_proj", "mla_status_string",
-           "mla_last_error_message", "mla_version")
+           "mla_decode", "mla_decode_default_split", "mla_out_proj", "mla_linear_workspace_size",
+           "mla_linear", "mla_status_string", "mla_last_error_message", "mla_version")
 
 
 class MlaError(RuntimeError):
@@ -71,6 +71,8 @@ def lib():
         "mla_decode": (I32, [DP, P, P, P, P, P, I32, I32, P, I32, I32, I32, I32, P, SZ, P, P, P]),
         "mla_decode_default_split": (I32, [DP, I32, I32, I32]),
         "mla_out_proj": (I32, [DP, P, P, I32, P, P]),
+        "mla_linear_workspace_size": (SZ, [I32, I32, I32]),
+        "mla_linear": (I32, [P, P, I32, I32, I32, P, P, SZ, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error_message": (ctypes.c_char_p, []),
         "mla_version": (I32, []),
@@ -163,6 +165,26 @@ def out_proj(dims, o_lat, w_uv, out):
     """mla_out_proj: out [N, n_h, d_v] = W^UV_i o_lat."""
     _check(lib().mla_out_proj(ctypes.byref(dims), _ptr(o_lat), _ptr(w_uv), o_lat.shape[0],
                               _ptr(out), _stream(o_lat.device)))
+
+
+def linear_workspace_size(m, n, k):
+    return lib().mla_linear_workspace_size(m, n, k)
+
+
+def linear(x, w, y, workspace=None):
+    """mla_linear: y [m, n] = x [m, k] w [n, k]^T (bf16); x and y may be any
+    contiguous tensors whose leading dimension is m."""
+    m = x.shape[0]
+    n, k = w.shape[0], w.numel() // w.shape[0]
+    if x.numel() != m * k or y.numel() != m * n or y.shape[0] != m:
+        raise ValueError(f"linear: x {tuple(x.shape)}, w {tuple(w.shape)}, y {tuple(y.shape)} do not match")
+    if not (x.dtype == w.dtype == y.dtype == torch.bfloat16):
+        raise ValueError("linear: x, w and y must be bfloat16")
+    need = linear_workspace_size(m, n, k)
+    if workspace is None:
+        workspace, _ = _workspace(need, y.device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().mla_linear(_ptr(x), _ptr(w), m, n, k, _ptr(y), _ptr(workspace), nbytes, _stream(y.device)))
 
 
 def version():

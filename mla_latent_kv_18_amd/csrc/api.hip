@@ -239,6 +239,25 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void*
   return hip_status(r.mfma ? mla::launch_out_proj_mfma(a, s) : mla::launch_out_proj_f32(a, s), "mla_out_proj");
 }
 
+size_t mla_linear_workspace_size(int32_t m, int32_t n, int32_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || n % 128 != 0 || k % 16 != 0) return 0;
+  return mla::linear_workspace(m, n, k);
+}
+
+mla_status_t mla_linear(const void* x, const void* w, int32_t m, int32_t n, int32_t k, void* y,
+                        void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+  if (m < 0 || n <= 0 || k <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "m < 0 or n, k <= 0");
+  if (n % 128 != 0 || k % 16 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "linear needs n %% 128 == 0 and k %% 16 == 0 (got n=%d, k=%d)", n, k);
+  if (m == 0) return hip_status(hipSuccess, "");
+  if (!x || !w || !y) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t need = mla_linear_workspace_size(m, n, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "linear needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  mla::LinearArgs a{x, w, m, n, k, y, workspace};
+  return hip_status(mla::launch_linear(a, static_cast<hipStream_t>(stream)), "mla_linear");
+}
+
 const char* mla_status_string(mla_status_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";
@@ -252,6 +271,6 @@ const char* mla_status_string(mla_status_t status) {
 
 const char* mla_last_error_message(void) { return g_err; }
 
-int32_t mla_version(void) { return 100; }
+int32_t mla_version(void) { return 200; }
 
 }  // extern "C"

@@ -59,6 +59,15 @@ struct OutProjArgs {
   void* out;
 };
 
+// y [m, n] = x [m, k] w [n, k]^T, bf16 (n % 128 == 0, k % 16 == 0)
+struct LinearArgs {
+  const void* x;
+  const void* w;
+  int m, n, k;
+  void* y;
+  void* workspace;
+};
+
 // fp32, any dims
 hipError_t launch_append_f32(const AppendArgs&, hipStream_t);
 hipError_t launch_absorb_q_f32(const AbsorbArgs&, hipStream_t);
@@ -77,6 +86,11 @@ int decode_waves_per_group(int n_h, int q_len);
 size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits);
 hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
 hipError_t launch_decode_fp8(const DecodeArgs&, hipStream_t);
+// skinny GEMM of the projections around the attention block
+int linear_chunks(int m, int n, int k);
+size_t linear_workspace(int m, int n, int k);
+hipError_t launch_linear(const LinearArgs&, hipStream_t);
+
 // merge of the chunk partials that a split decode left in the workspace
 // (xcd_group: the partials of request b were written on XCD b % 8, batch % 8 == 0)
 hipError_t launch_combine(const DecodeArgs&, hipStream_t, bool xcd_group = false);

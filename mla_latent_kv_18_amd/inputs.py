@@ -213,3 +213,22 @@ def generate(w: Workload):
     out["q_positions"] = np.concatenate(
         [np.arange(w.q_len) + seq[b] - w.q_len for b in range(B)]).astype(np.int32)
     return out
+
+
+def generate_block_weights(w: Workload, d_cq: int = 1536):
+    """Seeded weights of the projections around the attention block, in
+    storage form (N(0,1)/sqrt(fan_in), like the others):
+      w_dq [d_cq, d_model], w_uq [n_h*d_h, d_cq], w_qr [n_h*d_r, d_cq],
+      w_o [d_model, n_h*d_v].
+    d_cq = 1536 is the V3 query-latent width.  Drawn from their own stream
+    (seed + 1000), so generate() is unchanged."""
+    rng = np.random.default_rng(w.seed + 1000)
+    act = w.act_dtype
+    return {
+        "d_cq": d_cq,
+        "w_dq": _store(rng.standard_normal((d_cq, w.d_model), dtype=np.float32) / np.sqrt(w.d_model), act),
+        "w_uq": _store(rng.standard_normal((w.n_h * w.d_h, d_cq), dtype=np.float32) / np.sqrt(d_cq), act),
+        "w_qr": _store(rng.standard_normal((w.n_h * w.d_r, d_cq), dtype=np.float32) / np.sqrt(d_cq), act),
+        "w_o": _store(rng.standard_normal((w.d_model, w.n_h * w.d_v), dtype=np.float32) / np.sqrt(w.n_h * w.d_v),
+                      act),
+    }

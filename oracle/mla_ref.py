@@ -7,8 +7,10 @@ What it follows (pages on Multi-head Latent Attention):
   low-rank section eqs.(2)-(3); matrix-absorption section eq.(8);
   value-side absorption eqs.(9)-(10); "RoPE breaks absorption" section
   (its rope() helper fixes the half-split pairing); decoupled-RoPE section
-  eqs.(14)-(16) and the 1/sqrt(d_h+d_R) softmax scale; trade-offs section
-  (RMSNorm on the cached latent; absorbed form = MQA with head dim 576).
+  eqs.(14)-(16) and the 1/sqrt(d_h+d_R) softmax scale; query-compression
+  section eq.(17); value-side absorption into W^O, eq.(11); trade-offs
+  section (RMSNorm on the cached latent; absorbed form = MQA with head dim
+  576).
 * [V2 summary] abeam.tech, DeepSeek-V2 / MLA KV-cache article: the
   four-step inference flow.
 * [attention variants] youngju.dev: the extra RMSNorm after the compressed
@@ -20,6 +22,8 @@ Conventions (row-major, one token per row):
   kv = h @ W_dkv_kr.T gives [W^DKV h ; W^KR h].
 * W_UK [n_h, d_h, d_c] stacks W^UK_i (d_h x d_c): k^C_{j,i} = W^UK_i c_j.
 * W_UV [n_h, d_v, d_c] stacks W^UV_i (d_v x d_c): v^C_{j,i} = W^UV_i c_j.
+* W_DQ [d'_c, d_model], W_UQ [n_h*d_h, d'_c], W_QR [n_h*d_R, d'_c] (head
+  i's rows contiguous); W_O [d_model, n_h*d_v] (W^O_i = column block i).
 * RoPE: half-split pairs (x_k, x_{k+d/2}), angle pos / base^(2k/d).
 * Query t of a request with T cached rows (the rows appended this step
   included) sits at position T - q_len + t and sees keys 0..its position.
@@ -180,6 +184,51 @@ def out_proj(o_lat, w_uv):
     o_lat = np.asarray(o_lat, np.float64)
     w_uv = np.asarray(w_uv, np.float64)
     return np.stack([o_lat[:, i] @ w_uv[i].T for i in range(o_lat.shape[1])], axis=1)
+
+
+# ------------------------------------ projections around the attention block
+def query_from_hidden(h, w_dq, w_uq, w_qr, n_h):
+    """The query of every head from the hidden state, through the query
+    latent.  c^Q = W^DQ h; content part q^C = W^UQ c^Q; RoPE part W^QR c^Q
+    before its rotation (absorb_q rotates it).  [MLA explainer,
+    query-compression section eq.(17); decoupled RoPE section eq.(15)].
+    h [N, d]; w_dq [d'_c, d]; w_uq [n_h*d_h, d'_c] and w_qr [n_h*d_R, d'_c]
+    with head i's rows contiguous.  Returns (c_q [N, d'_c],
+    q_nope [N, n_h, d_h], q_pe [N, n_h, d_R])."""
+    h = np.asarray(h, np.float64)
+    c_q = h @ np.asarray(w_dq, np.float64).T
+    q_nope = (c_q @ np.asarray(w_uq, np.float64).T).reshape(h.shape[0], n_h, -1)
+    q_pe = (c_q @ np.asarray(w_qr, np.float64).T).reshape(h.shape[0], n_h, -1)
+    return c_q, q_nope, q_pe
+
+
+def output_projection(o, w_o):
+    """u = sum_i W^O_i o_i, where W^O_i (d x d_v) is column block i of W^O.
+    [MLA explainer, value-side absorption eq.(11), left-hand form].
+    o [N, n_h, d_v], w_o [d, n_h*d_v] -> u [N, d]."""
+    o = np.asarray(o, np.float64)
+    w_o = np.asarray(w_o, np.float64)
+    d_v = o.shape[2]
+    return sum(o[:, i] @ w_o[:, i * d_v:(i + 1) * d_v].T for i in range(o.shape[1]))
+
+
+def absorbed_output_weights(w_o, w_uv):
+    """B_i = W^O_i W^UV_i (d x d_c), side by side: [d, n_h*d_c].
+    [MLA explainer, value-side absorption eq.(11)].  w_o [d, n_h*d_v],
+    w_uv [n_h, d_v, d_c]."""
+    w_o = np.asarray(w_o, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    d_v = w_uv.shape[1]
+    return np.concatenate([w_o[:, i * d_v:(i + 1) * d_v] @ w_uv[i] for i in range(w_uv.shape[0])], axis=1)
+
+
+def output_projection_absorbed(o_lat, b):
+    """u = sum_i B_i o_lat_i [MLA explainer eq.(11), right-hand form].
+    o_lat [N, n_h, d_c], b [d, n_h*d_c] -> u [N, d]."""
+    o_lat = np.asarray(o_lat, np.float64)
+    b = np.asarray(b, np.float64)
+    d_c = o_lat.shape[2]
+    return sum(o_lat[:, i] @ b[:, i * d_c:(i + 1) * d_c].T for i in range(o_lat.shape[1]))
 
 
 def combine_partials(o_parts, lse_parts):

@@ -108,3 +108,28 @@ def test_missing_workspace_and_scales_are_reported():
     assert lib.mla_append_latent(ctypes.byref(d8), 1, 1, 1, 1, 1, 64, 4096, 1, None, 1, 1 << 30, None) == 1
     assert lib.mla_absorb_q(ctypes.byref(d8), 1, 1, 1, 1, 64, 1, None, 1, 1 << 30, None) == 1
     assert call_decode(d8) == 1
+
+
+def test_linear_sizes_and_host_checks():
+    lib = mla.lib()
+    # slices of k: W^O (7168 x 16384) at 64 tokens, 56 row groups x 8 slices
+    assert mla.linear_workspace_size(64, 7168, 16384) == 8 * 64 * 7168 * 4
+    # W^UQ (16384 x 1536): 128 row groups x 4 slices
+    assert mla.linear_workspace_size(64, 16384, 1536) == 4 * 64 * 16384 * 4
+    # W^DQ (1536 x 7168): 12 row groups x 16 slices, partials at most half the weight bytes
+    assert mla.linear_workspace_size(64, 1536, 7168) == 16 * 64 * 1536 * 4
+    assert mla.linear_workspace_size(64, 1536, 7168) <= 1536 * 7168
+    # W^QR (8192 x 1536): 64 row groups x 4 slices
+    assert mla.linear_workspace_size(64, 8192, 1536) == 4 * 64 * 8192 * 4
+    # many tokens, few columns: the cap leaves one slice
+    assert mla.linear_workspace_size(4096, 128, 4096) == 0
+    # a large row count needs no slices
+    assert mla.linear_workspace_size(64, 65536, 128) == 0
+    assert mla.linear_workspace_size(64, 100, 128) == 0              # unsupported: 0
+    P = ctypes.c_void_p
+    assert lib.mla_linear(P(1), P(1), 4, 100, 128, P(1), None, 0, None) == 2          # n % 128
+    assert lib.mla_linear(P(1), P(1), 4, 128, 100, P(1), None, 0, None) == 2          # k % 16
+    assert lib.mla_linear(P(1), P(1), -1, 128, 128, P(1), None, 0, None) == 1
+    assert lib.mla_linear(None, P(1), 4, 128, 128, P(1), None, 0, None) == 1
+    assert lib.mla_linear(P(1), P(1), 0, 128, 128, P(1), None, 0, None) == 0          # nothing to do
+    assert lib.mla_linear(P(1), P(1), 64, 7168, 16384, P(1), P(1), 16, None) == 3     # workspace too small

@@ -517,3 +517,71 @@ def test_paged_gather_follows_block_table():
     rows = ref.gather_rows(pool, table, T, bs)
     for t in range(T):
         assert np.array_equal(rows[t], pool[table[t // bs], t % bs])
+
+
+# ---------------------------------------------------------------------------
+# The projections around the attention block: query path and W^O.
+# ---------------------------------------------------------------------------
+def test_page_query_path_value(page_example):
+    """The page's printed score pins the oracle's query path: c^Q = W^DQ h,
+    q^C = W^UQ c^Q with head i's rows contiguous (a transposed or mis-sliced
+    W^UQ changes the value)."""
+    e = page_example
+    g = e["g"]["key_absorption"]
+    n_h, d_h, d_r = e["n_h"], e["d_h"], e["d_r"]
+    s = e["g"]["setup"]
+    rng = np.random.default_rng(s["seed"])
+    rng.normal(size=(e["T"], s["d"]))                      # H, W_DKV, W_UK are redrawn in page order
+    rng.normal(size=(s["d"], e["d_c"]))
+    rng.normal(size=(e["d_c"], n_h * d_h))
+    W_DQ = rng.normal(size=(s["d"], s["d_cq"])) / np.sqrt(s["d"])
+    W_UQ = rng.normal(size=(s["d_cq"], n_h * d_h)) / np.sqrt(s["d_cq"])
+    # page layout (row vectors) -> [out, in]
+    c_q, q_nope, q_pe = ref.query_from_hidden(e["H"], W_DQ.T, W_UQ.T, e["W_QR"].T, n_h)
+    assert q_nope.shape == (e["T"], n_h, d_h) and q_pe.shape == (e["T"], n_h, d_r)
+    S = np.einsum("tih,jih->tji", q_nope, _expanded_keys(e))
+    assert abs(S[3, 1, 0] - g["S_naive_t3_j1_h0"]) < 1e-12
+
+
+def test_output_projection_picks_head_column_blocks():
+    """A one-hot per-head output selects exactly one column of W^O: o_i with a
+    single 1 at position k gives u = W^O[:, i*d_v + k] (eq.(11), W^O_i is
+    column block i)."""
+    rng = np.random.default_rng(31)
+    n_h, d_v, d = 3, 4, 5
+    w_o = rng.normal(size=(d, n_h * d_v))
+    for i in range(n_h):
+        for k in range(d_v):
+            o = np.zeros((1, n_h, d_v))
+            o[0, i, k] = 1.0
+            assert np.array_equal(ref.output_projection(o, w_o)[0], w_o[:, i * d_v + k])
+
+
+def test_output_projection_brute_force():
+    rng = np.random.default_rng(32)
+    n_h, d_v, d, N = 3, 4, 5, 2
+    w_o = rng.normal(size=(d, n_h * d_v))
+    o = rng.normal(size=(N, n_h, d_v))
+    u = ref.output_projection(o, w_o)
+    for t in range(N):
+        for m in range(d):
+            acc = 0.0
+            for i in range(n_h):
+                for k in range(d_v):
+                    acc += w_o[m, i * d_v + k] * o[t, i, k]
+            assert abs(u[t, m] - acc) < 1e-12
+
+
+def test_absorbed_output_weights_equal_the_two_step_path():
+    """eq.(11): sum_i B_i o_lat_i with B_i = W^O_i W^UV_i equals W^O applied
+    after the per-head W^UV, in float64 at the V3 head shape (few heads)."""
+    rng = np.random.default_rng(33)
+    n_h, d_c, d_v, d, N = 4, 512, 128, 256, 3
+    w_uv = rng.normal(size=(n_h, d_v, d_c)) / np.sqrt(d_c)
+    w_o = rng.normal(size=(d, n_h * d_v)) / np.sqrt(n_h * d_v)
+    o_lat = rng.normal(size=(N, n_h, d_c))
+    two_step = ref.output_projection(ref.out_proj(o_lat, w_uv), w_o)
+    b = ref.absorbed_output_weights(w_o, w_uv)
+    assert b.shape == (d, n_h * d_c)
+    absorbed = ref.output_projection_absorbed(o_lat, b)
+    assert np.max(np.abs(two_step - absorbed)) <= 1e-12 * np.max(np.abs(two_step))
