@@ -12,7 +12,10 @@ Prints one JSON line.  `value` is latent-cache GB/s of the whole step
 `roofline` object covers the decode call (its algorithmic cache bytes per
 launch / its average launch time from HIP events on the launch stream);
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the
-same workload.
+same workload.  `block` (skipped with --no-block) times the whole attention
+block around the step: the query path W^DQ, W^UQ, W^QR and the output
+projection W^O through mla_linear, with W^O against its weight-read bound
+and the pages' absorbed output form (B_i = W^O_i W^UV_i) beside it.
 """
 
 import argparse
@@ -88,12 +91,75 @@ def cpu_baseline(gen, min_seconds=10.0, max_units=64):
             "kind": "oracle", "sample": f"{what}, non-absorbed float64 MLA, {dt:.1f} s"}
 
 
+def _event_us(fn, reps=50, warmup=5):
+    """Average duration of fn() between HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / reps
+
+
+def block_measurements(w, gen, steps, warmup):
+    """The whole attention block around the four calls: query path
+    (W^DQ, W^UQ, W^QR) and output projection W^O through mla_linear, timed
+    as whole steps like `value`; W^O alone against its weight-read bound;
+    and the two output forms of the pages (W^UV then W^O, or the absorbed
+    B_i = W^O_i W^UV_i applied to o_lat)."""
+    import torch
+
+    from mla_latent_kv_18_amd.inputs import generate_block_weights
+    from mla_latent_kv_18_amd.step import BlockStep
+
+    blk = BlockStep(gen, generate_block_weights(w), device="cuda:0")
+    for _ in range(warmup):
+        blk.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        blk.run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    N = w.batch * w.q_len
+    elem = 2
+    wo_bytes = w.d_model * w.n_h * w.d_v * elem
+    q_bytes = (blk.d_cq * w.d_model + (w.n_h * w.d_h + w.n_h * w.d_r) * blk.d_cq) * elem
+    t_query = _event_us(blk.query)
+    t_wo = _event_us(blk.o_proj)
+    t_uv = _event_us(blk.out_proj)
+    blk.absorbed_output_weights()
+    t_b = _event_us(blk.o_proj_absorbed)
+    gbs = wo_bytes / (t_wo * 1e-6) / 1e9
+    return {
+        "ms_per_step": round(ms, 5),
+        "tokens_per_s": round(N / (ms * 1e-3), 1),
+        "d_cq": blk.d_cq,
+        "query_path_us": round(t_query, 2),
+        "query_weight_bytes": q_bytes,
+        "w_o_us": round(t_wo, 2),
+        "w_o": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": wo_bytes},
+        "out_proj_then_w_o_us": round(t_uv + t_wo, 2),
+        "absorbed_b_us": round(t_b, 2),
+        "absorbed_b_weight_bytes": w.d_model * w.n_h * w.d_c * elem,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the whole-attention-block measurement (query path and W^O around the step)")
     ap.add_argument("--workload", default=WORKLOAD,
                     help="workload name from mla_latent_kv_18_amd.inputs.WORKLOADS (default: the "
                          "V3 shape, batch 64, 4096 cached tokens, bf16)")
@@ -202,6 +268,10 @@ def main():
         "decode_mfma_frac": round(tflops / mfma_peak, 4),
         "roofline": roof,
     }
+    if not args.no_block:
+        del step
+        torch.cuda.empty_cache()
+        out["block"] = block_measurements(w, gen, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(gen)
     print(json.dumps(out), flush=True)

@@ -9,7 +9,8 @@ import ctypes
 import numpy as np
 import torch
 
-from . import absorb_q, append_latent, decode, decode_workspace_size, lib, make_dims, out_proj
+from . import (absorb_q, append_latent, decode, decode_workspace_size, lib, linear, linear_workspace_size,
+               make_dims, out_proj)
 
 
 def _dev(a, device, fmt):
@@ -99,3 +100,59 @@ class DeviceStep:
             fn()
         torch.cuda.synchronize()
         return g
+
+
+class BlockStep(DeviceStep):
+    """The whole attention block of one decode step: the query path from the
+    new tokens' hidden states (c^Q = W^DQ h, q^C = W^UQ c^Q, W^QR c^Q), the
+    four calls, and the output projection u = sum_i W^O_i o_i, all through
+    libmla (mla_linear for the dense projections).  The new tokens' hidden
+    states are the ones the append writes into the cache."""
+
+    def __init__(self, gen, block, device="cuda:0", split_tokens=0):
+        super().__init__(gen, device, split_tokens)
+        w = self.w
+        act = w.act_dtype
+        N = w.batch * w.q_len
+        if self.h.shape[0] != N:
+            raise ValueError("the block needs every request to append its q_len query tokens")
+        self.d_cq = block["d_cq"]
+        self.w_dq = _dev(block["w_dq"], device, act)
+        self.w_uq = _dev(block["w_uq"], device, act)
+        self.w_qr = _dev(block["w_qr"], device, act)
+        self.w_o = _dev(block["w_o"], device, act)
+        self.c_q = torch.empty(N, self.d_cq, dtype=torch.bfloat16, device=device)
+        self.u = torch.empty(N, w.d_model, dtype=torch.bfloat16, device=device)
+        shapes = [(self.d_cq, w.d_model), (w.n_h * w.d_h, self.d_cq), (w.n_h * w.d_r, self.d_cq),
+                  (w.d_model, w.n_h * w.d_v), (w.d_model, w.n_h * w.d_c)]
+        nws = max(linear_workspace_size(N, n, k) for n, k in shapes)
+        self.linear_ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
+        self.b = None
+
+    def query(self):
+        linear(self.h, self.w_dq, self.c_q, workspace=self.linear_ws)
+        linear(self.c_q, self.w_uq, self.q_nope, workspace=self.linear_ws)
+        linear(self.c_q, self.w_qr, self.q_pe, workspace=self.linear_ws)
+
+    def o_proj(self):
+        linear(self.out, self.w_o, self.u, workspace=self.linear_ws)
+
+    def run(self):
+        self.query()
+        super().run()
+        self.o_proj()
+
+    def absorbed_output_weights(self):
+        """B_i = W^O_i W^UV_i side by side [d_model, n_h * d_c], formed once
+        (as at model load) with torch in float32 and stored in bf16."""
+        w = self.w
+        b = torch.empty(w.d_model, w.n_h * w.d_c, dtype=torch.bfloat16, device=self.device)
+        for i in range(w.n_h):
+            wo_i = self.w_o[:, i * w.d_v:(i + 1) * w.d_v].float().contiguous()
+            b[:, i * w.d_c:(i + 1) * w.d_c] = (wo_i @ self.w_uv[i].float().contiguous()).bfloat16()
+        self.b = b
+        return b
+
+    def o_proj_absorbed(self):
+        """u = sum_i B_i o_lat_i straight from the latent output."""
+        linear(self.o_lat, self.b, self.u, workspace=self.linear_ws)
