@@ -55,6 +55,21 @@ def measured_traffic():
     return c.get("hbm_bytes_per_launch")
 
 
+def measured_linear_traffic():
+    """HBM bytes per W^O launch of mla_linear (V3, 64 tokens) from the
+    committed counter runs, or None when absent or taken on other source."""
+    path = os.path.join(ROOT, "profiles", "linear_w_o_v3_bs64_counters.json")
+    src = os.path.join(ROOT, "mla_latent_kv_18_amd", "csrc", "linear_mfma.hip")
+    try:
+        with open(path) as f:
+            c = json.load(f)
+        with open(src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    return c.get("hbm_bytes_per_launch") if c.get("linear_source_sha256_16") == h else None
+
+
 def cpu_baseline(gen, min_seconds=10.0, max_units=64):
     """The float64 oracle, as it stands (non-absorbed MLA), on whole requests
     of the workload (all heads) until at least `min_seconds` of CPU work; for
@@ -145,7 +160,8 @@ def block_measurements(w, gen, steps, warmup):
         "query_weight_bytes": q_bytes,
         "w_o_us": round(t_wo, 2),
         "w_o": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": wo_bytes},
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": wo_bytes,
+                "traffic": measured_linear_traffic() if w.name == WORKLOAD else None},
         "out_proj_then_w_o_us": round(t_uv + t_wo, 2),
         "absorbed_b_us": round(t_b, 2),
         "absorbed_b_weight_bytes": w.d_model * w.n_h * w.d_c * elem,
