@@ -18,7 +18,10 @@
  *                      (split over the context, then a combine kernel)
  *   mla_out_proj       o_i = W^UV_i o_lat_i
  *   mla_linear         the dense projections around them (query path
- *                      W^DQ, W^UQ, W^QR; output W^O or the absorbed B_i)
+ *                      W^DQ, W^UQ, W^QR; output W^O or the absorbed B_i;
+ *                      prefill keys and values W^UK c, W^UV c)
+ *   mla_prefill_attention  the prompt's causal attention with per-head
+ *                      keys and values (no absorption)
  *
  * Conventions
  *   - All tensors are dense row-major; every pointer argument except those
@@ -199,6 +202,27 @@ int32_t mla_decode_default_split(const mla_dims_t* dims, int32_t batch, int32_t 
 mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv,
                           int32_t n_tokens, void* out, mla_stream_t stream);
 
+/* -------------------------------------------------------------- prefill
+ * Causal attention of one prompt of seq_len tokens, the non-absorbed way
+ * the pages prescribe for prefill [MLA explainer, trade-offs section (no
+ * absorption while the prompt is processed); decoupled RoPE eqs.(14)-(16)]:
+ * per head i, q_t = [q^C_t ; RoPE(q^R_t, t)], k_j = [k^C_j ; k^R_j],
+ * s = q_t . k_j * softmax_scale for j <= t, o_t = softmax(s) V.  Tokens sit
+ * at positions 0..seq_len-1.
+ * q_nope [seq_len, n_h, d_h], q_pe [seq_len, n_h, d_R] (before RoPE),
+ * k_nope [seq_len, n_h, d_h] (= W^UK_i c_j, e.g. from mla_linear over the
+ * latent rows), v [seq_len, n_h, d_v] (= W^UV_i c_j), out [seq_len, n_h, d_v]:
+ * bf16.  k_rope: the RoPE'd shared key of token j at k_rope + j *
+ * k_rope_stride (d_R bf16 values; k_rope = cache rows + d_c and stride
+ * d_c + d_R reads them from contiguous cache rows).  lse [seq_len, n_h] fp32
+ * natural log, or NULL.  Needs the bf16 dims (d_h = d_v = 128, d_R = 64,
+ * bf16 cache and activations); others return MLA_ERR_UNSUPPORTED.
+ * seq_len = 0 returns MLA_OK and launches nothing. */
+mla_status_t mla_prefill_attention(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
+                                   const void* k_nope, const void* k_rope, int32_t k_rope_stride,
+                                   const void* v, int32_t seq_len, void* out, float* lse,
+                                   mla_stream_t stream);
+
 /* --------------------------------------------------------------- linear
  * The dense projections on either side of the four calls above, as one
  * skinny bf16 GEMM (fp32 accumulation):
@@ -211,7 +235,9 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void*
  * absorbed, u = sum_i B_i o_lat_i with B_i = W^O_i W^UV_i, x = o_lat viewed
  * as [m, n_h * d_c] and w = [B_1 ... B_nh]].
  * x, w, y: row-major bf16 device buffers, owned by the caller; m >= 1,
- * n a multiple of 128, k a multiple of 16.  m = 0 returns MLA_OK and
+ * n a multiple of 128, k a multiple of 16.  ldx: elements between rows of
+ * x (>= k, a multiple of 8: 16-byte aligned rows), so that x can be the
+ * latent part of cache rows (ldx = d_c + d_R).  m = 0 returns MLA_OK and
  * launches nothing.
  * workspace: at least mla_linear_workspace_size(m, n, k) bytes of device
  * memory (fp32 partial sums over slices of k; may be NULL if that is 0).
@@ -219,8 +245,8 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void*
  * MLA_ERR_INVALID_ARGUMENT, a short workspace MLA_ERR_WORKSPACE_TOO_SMALL;
  * nothing is launched then. */
 size_t mla_linear_workspace_size(int32_t m, int32_t n, int32_t k);
-mla_status_t mla_linear(const void* x, const void* w, int32_t m, int32_t n, int32_t k, void* y,
-                        void* workspace, size_t workspace_bytes, mla_stream_t stream);
+mla_status_t mla_linear(const void* x, int32_t ldx, const void* w, int32_t m, int32_t n, int32_t k,
+                        void* y, void* workspace, size_t workspace_bytes, mla_stream_t stream);
 
 /* ------------------------------------------------------------ diagnostics */
 const char* mla_status_string(mla_status_t status);

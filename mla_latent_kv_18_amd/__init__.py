@@ -24,7 +24,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
 EXPORTS = ("mla_cache_row_bytes", "mla_q_lat_row_bytes", "mla_append_workspace_size", "mla_append_latent",
            "mla_absorb_workspace_size", "mla_absorb_q", "mla_decode_workspace_size",
            "mla_decode", "mla_decode_default_split", "mla_out_proj", "mla_linear_workspace_size",
-           "mla_linear", "mla_status_string", "mla_last_error_message", "mla_version")
+           "mla_linear", "mla_prefill_attention", "mla_status_string", "mla_last_error_message",
+           "mla_version")
 
 
 class MlaError(RuntimeError):
@@ -72,7 +73,8 @@ def lib():
         "mla_decode_default_split": (I32, [DP, I32, I32, I32]),
         "mla_out_proj": (I32, [DP, P, P, I32, P, P]),
         "mla_linear_workspace_size": (SZ, [I32, I32, I32]),
-        "mla_linear": (I32, [P, P, I32, I32, I32, P, P, SZ, P]),
+        "mla_prefill_attention": (I32, [DP, P, P, P, P, I32, P, I32, P, P, P]),
+        "mla_linear": (I32, [P, I32, P, I32, I32, I32, P, P, SZ, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error_message": (ctypes.c_char_p, []),
         "mla_version": (I32, []),
@@ -171,20 +173,45 @@ def linear_workspace_size(m, n, k):
     return lib().mla_linear_workspace_size(m, n, k)
 
 
-def linear(x, w, y, workspace=None):
-    """mla_linear: y [m, n] = x [m, k] w [n, k]^T (bf16); x and y may be any
-    contiguous tensors whose leading dimension is m."""
+def linear(x, w, y, workspace=None, ldx=None):
+    """mla_linear: y [m, n] = x [m, k] w [n, k]^T (bf16).  x and y may be any
+    contiguous tensors whose leading dimension is m; with ldx, x is a 2-D
+    view whose rows are ldx elements apart (e.g. the latent part of cache
+    rows, x = rows[:, :d_c], ldx = d_c + d_R)."""
     m = x.shape[0]
     n, k = w.shape[0], w.numel() // w.shape[0]
-    if x.numel() != m * k or y.numel() != m * n or y.shape[0] != m:
-        raise ValueError(f"linear: x {tuple(x.shape)}, w {tuple(w.shape)}, y {tuple(y.shape)} do not match")
+    if ldx is None:
+        if not x.is_contiguous() or x.numel() != m * k:
+            raise ValueError(f"linear: x {tuple(x.shape)} does not match w {tuple(w.shape)}")
+        ldx, xp = k, _ptr(x)
+    else:
+        if x.dim() != 2 or x.shape[1] != k or x.stride() != (ldx, 1) or not x.is_cuda:
+            raise ValueError(f"linear: x must be a [{m}, {k}] view with row stride {ldx}")
+        xp = x.data_ptr()
+    if y.numel() != m * n or y.shape[0] != m:
+        raise ValueError(f"linear: y {tuple(y.shape)} does not match [{m}, {n}]")
     if not (x.dtype == w.dtype == y.dtype == torch.bfloat16):
         raise ValueError("linear: x, w and y must be bfloat16")
     need = linear_workspace_size(m, n, k)
     if workspace is None:
         workspace, _ = _workspace(need, y.device)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().mla_linear(_ptr(x), _ptr(w), m, n, k, _ptr(y), _ptr(workspace), nbytes, _stream(y.device)))
+    _check(lib().mla_linear(xp, ldx, _ptr(w), m, n, k, _ptr(y), _ptr(workspace), nbytes, _stream(y.device)))
+
+
+def prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out, lse=None):
+    """mla_prefill_attention over one prompt of q_nope.shape[0] tokens.
+    k_rope is a [T, d_R] view whose rows may be strided (e.g. the RoPE part
+    of contiguous cache rows)."""
+    T = q_nope.shape[0]
+    if k_rope.dim() != 2 or k_rope.stride(1) != 1 or k_rope.shape[0] != T or not k_rope.is_cuda:
+        raise ValueError("prefill_attention: k_rope must be a [T, d_R] device view with unit column stride")
+    for name, t in (("q_pe", q_pe), ("k_nope", k_nope), ("v", v), ("out", out)):
+        if t.shape[0] != T:
+            raise ValueError(f"prefill_attention: {name} has {t.shape[0]} rows, expected {T}")
+    _check(lib().mla_prefill_attention(ctypes.byref(dims), _ptr(q_nope), _ptr(q_pe), _ptr(k_nope),
+                                       k_rope.data_ptr(), k_rope.stride(0), _ptr(v), T, _ptr(out), _ptr(lse),
+                                       _stream(out.device)))
 
 
 def version():

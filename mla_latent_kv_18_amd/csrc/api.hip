@@ -239,14 +239,33 @@ mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void*
   return hip_status(r.mfma ? mla::launch_out_proj_mfma(a, s) : mla::launch_out_proj_f32(a, s), "mla_out_proj");
 }
 
+mla_status_t mla_prefill_attention(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
+                                   const void* k_nope, const void* k_rope, int32_t k_rope_stride,
+                                   const void* v, int32_t seq_len, void* out, float* lse, mla_stream_t stream) {
+  Resolved r;
+  mla_status_t st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (!r.mfma || r.act_dtype != MLA_BF16 || r.cache_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "prefill attention needs the bf16 MFMA dims (d_h = d_v = 128, d_R = 64)");
+  if (seq_len < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "seq_len < 0");
+  if (seq_len == 0) return hip_status(hipSuccess, "");
+  if (!q_nope || !q_pe || !k_nope || !k_rope || !v || !out)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (k_rope_stride < r.d_r || k_rope_stride % 8 != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "k_rope_stride must be >= d_R and a multiple of 8 (got %d)", k_rope_stride);
+  mla::PrefillArgs a{q_nope, q_pe, k_nope, k_rope, k_rope_stride, v, seq_len, r.n_h, r.scale, r.theta, out, lse};
+  return hip_status(mla::launch_prefill_attention(a, static_cast<hipStream_t>(stream)), "mla_prefill_attention");
+}
+
 size_t mla_linear_workspace_size(int32_t m, int32_t n, int32_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || n % 128 != 0 || k % 16 != 0) return 0;
   return mla::linear_workspace(m, n, k);
 }
 
-mla_status_t mla_linear(const void* x, const void* w, int32_t m, int32_t n, int32_t k, void* y,
+mla_status_t mla_linear(const void* x, int32_t ldx, const void* w, int32_t m, int32_t n, int32_t k, void* y,
                         void* workspace, size_t workspace_bytes, mla_stream_t stream) {
   if (m < 0 || n <= 0 || k <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "m < 0 or n, k <= 0");
+  if (ldx < k || ldx % 8 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "ldx must be >= k and a multiple of 8 (got %d)", ldx);
   if (n % 128 != 0 || k % 16 != 0)
     return fail(MLA_ERR_UNSUPPORTED, "linear needs n %% 128 == 0 and k %% 16 == 0 (got n=%d, k=%d)", n, k);
   if (m == 0) return hip_status(hipSuccess, "");
@@ -254,7 +273,7 @@ mla_status_t mla_linear(const void* x, const void* w, int32_t m, int32_t n, int3
   const size_t need = mla_linear_workspace_size(m, n, k);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "linear needs %zu workspace bytes, got %zu", need, workspace_bytes);
-  mla::LinearArgs a{x, w, m, n, k, y, workspace};
+  mla::LinearArgs a{x, w, m, n, k, ldx, y, workspace};
   return hip_status(mla::launch_linear(a, static_cast<hipStream_t>(stream)), "mla_linear");
 }
 

@@ -59,11 +59,11 @@ struct OutProjArgs {
   void* out;
 };
 
-// y [m, n] = x [m, k] w [n, k]^T, bf16 (n % 128 == 0, k % 16 == 0)
+// y [m, n] = x [m, k] w [n, k]^T, bf16 (n % 128 == 0, k % 16 == 0, x rows ldx apart)
 struct LinearArgs {
   const void* x;
   const void* w;
-  int m, n, k;
+  int m, n, k, ldx;
   void* y;
   void* workspace;
 };
@@ -86,6 +86,22 @@ int decode_waves_per_group(int n_h, int q_len);
 size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits);
 hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
 hipError_t launch_decode_fp8(const DecodeArgs&, hipStream_t);
+// causal prefill attention of one sequence with per-head keys and values
+// (q, k: [d_h content ; d_R RoPE part] = 192 wide, v: 128 wide)
+struct PrefillArgs {
+  const void* q_nope;
+  const void* q_pe;
+  const void* k_nope;
+  const void* k_rope;
+  int k_rope_stride;
+  const void* v;
+  int seq_len, n_h;
+  float scale, theta;
+  void* out;
+  float* lse;
+};
+hipError_t launch_prefill_attention(const PrefillArgs&, hipStream_t);
+
 // skinny GEMM of the projections around the attention block
 int linear_chunks(int m, int n, int k);
 size_t linear_workspace(int m, int n, int k);

@@ -1,6 +1,6 @@
 // Skinny bf16 GEMM for the projections around the attention block:
 //
-//   y[m][n] = sum_k x[m][k] * w[n][k]     x [M, K], w [N, K], y [M, N]
+//   y[m][n] = sum_k x[m][k] * w[n][k]     x [M, K] (row stride ldx), w [N, K], y [M, N]
 //
 // used for the query path c^Q = W^DQ h, q^C = W^UQ c^Q, W^QR c^Q
 // [MLA explainer, query-compression section eq.(17); decoupled RoPE
@@ -38,7 +38,7 @@ __device__ __forceinline__ bf16x8_t load8(const __bf16* p) { return *reinterpret
 
 template <int MT>
 __global__ void __launch_bounds__(256) linear_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ w,
-                                                     int M, int N, int K, int chunk_len,
+                                                     int ldx, int M, int N, int K, int chunk_len,
                                                      float* __restrict__ partial, __bf16* __restrict__ y) {
   constexpr int kTile = 32 * MT * 256;  // bytes of one batch's activation tile
   constexpr int kPer = 2 * MT;          // 16-byte tile chunks copied per thread
@@ -56,7 +56,7 @@ __global__ void __launch_bounds__(256) linear_kernel(const __bf16* __restrict__ 
 #pragma unroll
     for (int s = 0; s < kPer; ++s) {
       const int i = tid + 256 * s, r = i >> 4, c = i & 15;
-      xrow[s] = x + static_cast<int64_t>(min(m0 + r, M - 1)) * K + k_begin + 8 * (c & 1);
+      xrow[s] = x + static_cast<int64_t>(min(m0 + r, M - 1)) * ldx + k_begin + 8 * (c & 1);
       xc[s] = c >> 1;
       xoff[s] = (r * 16 + (c ^ (r & 15))) * 16;
     }
@@ -171,7 +171,7 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t st) {
   const dim3 grid(a.n / kLinRows, chunks, groups);
   auto kern = mt == 1 ? linear_kernel<1> : linear_kernel<2>;
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const __bf16*>(a.x), static_cast<const __bf16*>(a.w),
-                     a.m, a.n, a.k, a.k / chunks, partial, static_cast<__bf16*>(a.y));
+                     a.ldx, a.m, a.n, a.k, a.k / chunks, partial, static_cast<__bf16*>(a.y));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunks == 1) return e;
   auto red = chunks <= 4 ? linear_reduce_kernel<4>

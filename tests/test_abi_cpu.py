@@ -127,9 +127,10 @@ def test_linear_sizes_and_host_checks():
     assert mla.linear_workspace_size(64, 65536, 128) == 0
     assert mla.linear_workspace_size(64, 100, 128) == 0              # unsupported: 0
     P = ctypes.c_void_p
-    assert lib.mla_linear(P(1), P(1), 4, 100, 128, P(1), None, 0, None) == 2          # n % 128
-    assert lib.mla_linear(P(1), P(1), 4, 128, 100, P(1), None, 0, None) == 2          # k % 16
-    assert lib.mla_linear(P(1), P(1), -1, 128, 128, P(1), None, 0, None) == 1
-    assert lib.mla_linear(None, P(1), 4, 128, 128, P(1), None, 0, None) == 1
-    assert lib.mla_linear(P(1), P(1), 0, 128, 128, P(1), None, 0, None) == 0          # nothing to do
-    assert lib.mla_linear(P(1), P(1), 64, 7168, 16384, P(1), P(1), 16, None) == 3     # workspace too small
+    assert lib.mla_linear(P(1), 128, P(1), 4, 100, 128, P(1), None, 0, None) == 2          # n % 128
+    assert lib.mla_linear(P(1), 128, P(1), 4, 128, 100, P(1), None, 0, None) == 2          # k % 16
+    assert lib.mla_linear(P(1), 128, P(1), -1, 128, 128, P(1), None, 0, None) == 1
+    assert lib.mla_linear(None, 128, P(1), 4, 128, 128, P(1), None, 0, None) == 1
+    assert lib.mla_linear(P(1), 128, P(1), 0, 128, 128, P(1), None, 0, None) == 0     # nothing to do
+    assert lib.mla_linear(P(1), 100, P(1), 4, 128, 128, P(1), None, 0, None) == 1   # ldx < k
+    assert lib.mla_linear(P(1), 16384, P(1), 64, 7168, 16384, P(1), P(1), 16, None) == 3     # workspace too small

@@ -1,0 +1,76 @@
+"""GPU parity of the prefill path: keys and values materialised per head
+from the latent cache rows by mla_linear (k^C = W^UK_i c, v = W^UV_i c),
+then mla_prefill_attention, against the float64 oracle's non-absorbed
+attention over the same rows (queries at positions 0..T-1, causal), and
+its log-sum-exp against the absorbed oracle form.
+Bar: max|err| <= 2e-2 * max|ref| for the output, |err| <= 2e-2 for lse.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs
+from oracle import mla_ref as ref
+from tests import oracle_views as ov
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mla_latent_kv_18_amd as mla
+
+D_C, D_R, D_H, D_V = 512, 64, 128, 128
+
+
+def _bf16(rng, shape, scale=1.0):
+    t = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)).bfloat16()
+    return t.cuda(), codecs.bf16_decode(t.view(torch.int16).numpy().view(np.uint16))
+
+
+def _host_bf16(t):
+    return codecs.bf16_decode(t.cpu().view(torch.int16).numpy().view(np.uint16))
+
+
+@pytest.mark.parametrize("T,n_h", [(1, 64), (31, 64), (33, 64), (129, 64), (300, 64), (200, 128)])
+def test_prefill_matches_nonabsorbed_oracle(T, n_h):
+    rng = np.random.default_rng(4000 + T + n_h)
+    dims = mla.make_dims(n_h, D_C, D_H, D_R, D_V, 1024, 64, "bf16", "bf16")
+    rows, rows64 = _bf16(rng, (T, D_C + D_R))                 # latent cache rows [c ; k^R]
+    w_uk, wuk64 = _bf16(rng, (n_h, D_H, D_C), 1.0 / np.sqrt(D_C))
+    w_uv, wuv64 = _bf16(rng, (n_h, D_V, D_C), 1.0 / np.sqrt(D_C))
+    q_nope, qn64 = _bf16(rng, (T, n_h, D_H))
+    q_pe, qp64 = _bf16(rng, (T, n_h, D_R))
+    c = rows[:, :D_C]                                        # strided view of the rows
+    k_nope = torch.empty(T, n_h, D_H, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty(T, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    mla.linear(c, w_uk.view(n_h * D_H, D_C), k_nope, ldx=D_C + D_R)
+    mla.linear(c, w_uv.view(n_h * D_V, D_C), v, ldx=D_C + D_R)
+    out = torch.empty(T, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(T, n_h, dtype=torch.float32, device="cuda")
+    mla.prefill_attention(dims, q_nope, q_pe, k_nope, rows[:, D_C:], v, out, lse)
+    torch.cuda.synchronize()
+
+    pos = np.arange(T)
+    scale = 1.0 / np.sqrt(D_H + D_R)
+    want = ref.attention_nonabsorbed(qn64, qp64, pos, rows64[:, :D_C], rows64[:, D_C:], wuk64, wuv64, scale)
+    assert ov.rel_err(_host_bf16(out), want) <= ov.TOL["bf16"]
+    q_lat = ref.absorb_q(qn64, qp64, pos, wuk64)
+    _, lse_ref = ref.decode_absorbed(q_lat, pos, rows64[:, :D_C], rows64[:, D_C:], scale)
+    assert np.max(np.abs(lse.cpu().numpy() - lse_ref)) <= 2e-2
+
+
+def test_prefill_first_token_is_its_own_value():
+    """Query 0 sees only key 0: its output is v_0 exactly up to bf16 rounding
+    (softmax over one key), whatever the scores."""
+    rng = np.random.default_rng(4100)
+    n_h, T = 64, 40
+    dims = mla.make_dims(n_h, D_C, D_H, D_R, D_V, 1024, 64, "bf16", "bf16")
+    q_nope, _ = _bf16(rng, (T, n_h, D_H), 10.0)
+    q_pe, _ = _bf16(rng, (T, n_h, D_R), 10.0)
+    k_nope, _ = _bf16(rng, (T, n_h, D_H))
+    k_rope, _ = _bf16(rng, (T, D_R))
+    v, v64 = _bf16(rng, (T, n_h, D_V))
+    out = torch.empty(T, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    mla.prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host_bf16(out)[0], v64[0])
