@@ -168,12 +168,66 @@ def block_measurements(w, gen, steps, warmup):
     }
 
 
+def prefill_measurements(w, seq_len=4096):
+    """The prefill side of the method on one prompt of seq_len tokens with the
+    workload's head shape: keys and values materialised per head from the
+    latent rows (two mla_linear calls, W^UK c and W^UV c) and the causal
+    attention (mla_prefill_attention), which is MFMA bound.  Inputs are
+    seeded synthetic values of the same distributions as the decode's."""
+    import torch
+
+    import mla_latent_kv_18_amd as mla
+
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(w.seed + 2000)
+    T, n_h, D = seq_len, w.n_h, w.d_c + w.d_r
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(*shape, generator=g, device="cuda:0") * scale).bfloat16()
+
+    rows = rnd(T, D)
+    w_uk = rnd(n_h * w.d_h, w.d_c, scale=w.d_c ** -0.5)
+    w_uv = rnd(n_h * w.d_v, w.d_c, scale=w.d_c ** -0.5)
+    q_nope, q_pe = rnd(T, n_h, w.d_h), rnd(T, n_h, w.d_r)
+    k_nope = torch.empty(T, n_h, w.d_h, dtype=torch.bfloat16, device="cuda:0")
+    v = torch.empty(T, n_h, w.d_v, dtype=torch.bfloat16, device="cuda:0")
+    out = torch.empty(T, n_h, w.d_v, dtype=torch.bfloat16, device="cuda:0")
+    dims = mla.make_dims(n_h, w.d_c, w.d_h, w.d_r, w.d_v, w.d_model, w.block_size, "bf16", "bf16")
+    ws = torch.empty(max(mla.linear_workspace_size(T, n_h * w.d_h, w.d_c), 1), dtype=torch.uint8, device="cuda:0")
+    c = rows[:, :w.d_c]
+
+    def kv():
+        mla.linear(c, w_uk, k_nope, workspace=ws, ldx=D)
+        mla.linear(c, w_uv, v, workspace=ws, ldx=D)
+
+    def attn():
+        mla.prefill_attention(dims, q_nope, q_pe, k_nope, rows[:, w.d_c:], v, out)
+
+    t_kv = _event_us(kv, reps=20)
+    t_attn = _event_us(attn, reps=20)
+    flops = T * (T + 1) // 2 * n_h * 2 * (w.d_h + w.d_r + w.d_v)      # causal QK^T and PV
+    kv_flops = 2 * T * w.d_c * n_h * (w.d_h + w.d_v)
+    tf = flops / (t_attn * 1e-6) / 1e12
+    peak = MFMA_PEAK_TFLOPS["bf16"]
+    return {
+        "seq_len": T, "num_heads": n_h,
+        "kv_up_projection_us": round(t_kv, 2),
+        "kv_up_projection_tflops": round(kv_flops / (t_kv * 1e-6) / 1e12, 2),
+        "attention_us": round(t_attn, 2),
+        "attention": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                      "frac": round(tf / peak, 4), "flops_per_launch": flops},
+        "tokens_per_s": round(T / ((t_kv + t_attn) * 1e-6), 1),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill measurement (a 4096-token prompt, non-absorbed attention)")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the whole-attention-block measurement (query path and W^O around the step)")
     ap.add_argument("--workload", default=WORKLOAD,
@@ -288,6 +342,8 @@ def main():
         del step
         torch.cuda.empty_cache()
         out["block"] = block_measurements(w, gen, args.steps, args.warmup)
+    if not args.no_prefill and args.workload == WORKLOAD:
+        out["prefill"] = prefill_measurements(w)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(gen)
     print(json.dumps(out), flush=True)

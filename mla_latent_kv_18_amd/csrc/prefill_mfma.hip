@@ -8,14 +8,16 @@
 //
 // One sequence of T tokens at positions 0..T-1; query t sees keys 0..t.
 //
-// Work decomposition: workgroup = (block of 128 queries, head), 4 waves; wave
+// Work decomposition: workgroup = (block of 256 queries, head), 8 waves; wave
 // w owns queries 32w..32w+31 of the block.  The keys and values of each
-// 32-token tile are staged once in LDS and shared by the four waves.  Per
-// tile, per wave (bf16 MFMA 32x32x16, fp32 accumulate):
+// 64-token tile are staged once in LDS and shared by the eight waves (a
+// workgroup of 128 queries fetched twice the bytes per flop and was bound by
+// them).  Per 32-key sub-tile, per wave (bf16 MFMA 32x32x16, fp32 accumulate):
 //   S^T[key, q] = sum_d K[key, d] Q[q, d]     A = K tile (ds_read_b128),
 //                                             B = Q^T, register resident
-//   online softmax over the keys (per lane: one query, 16 keys; the other 16
-//   keys of that query sit in lane ^ 32), rescaling O when the maximum grows
+//   (two chains over the even and odd k-steps), online softmax over the keys
+//   (per lane: one query, 16 keys; the other 16 keys of that query sit in
+//   lane ^ 32), rescaling O only in the tiles where some query's maximum grows
 //   O^T[v, q] += sum_key V^T[v, key] P^T[key, q]   A = V^T read with
 //                                             ds_read_b64_tr_b16, B = P^T
 //                                             straight from the S^T registers
@@ -28,6 +30,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace mla {
 namespace {
@@ -37,9 +40,15 @@ constexpr int kPR = 64;         // d_R
 constexpr int kPD = kPH + kPR;  // 192
 constexpr int kPV = 128;        // d_v
 constexpr int kKC = kPD * 2 / 16;   // 24 sixteen-byte chunks per key row
-constexpr int kVS = 18;             // chunks per staged value row (16 used; 2 of padding)
-constexpr int kKTile = 32 * kKC * 16;   // 12,288 B
-constexpr int kVTile = 32 * kVS * 16;   //  9,216 B
+constexpr int kVS = 16;             // chunks per staged value row
+constexpr int kWaves = 8;               // 32 queries each: 256 queries per workgroup
+constexpr int kQB = 32 * kWaves;
+constexpr int kTK = 64;                 // keys per staged tile (two 32-key MFMA sub-tiles)
+constexpr int kKTile = kTK * kKC * 16;  // 24,576 B
+constexpr int kVTile = kTK * kVS * 16;  // 16,384 B
+constexpr int kBuf = kKTile + kVTile;   // one tile: 40 wave-wide 1 KB copies
+constexpr int kNBuf = 3;                // tiles in LDS: the one computed and two landing
+constexpr int kCopies = kBuf / 1024 / kWaves;  // copies per wave per tile
 
 struct PrefillParams {
   const __bf16* q_nope;  // [T, n_h, 128]
@@ -57,17 +66,30 @@ __device__ __forceinline__ bf16x8_t ld8(const __bf16* p) { return *reinterpret_c
 
 // K tile: chunk c of key row r at r * 24 + (c ^ ((r >> 1) & 7)): the XOR stays
 // inside the chunk's group of eight, and 16 consecutive rows of one logical
-// chunk land on 16 distinct bank groups.  V tile: rows of 18 chunks.
+// chunk land on 16 distinct bank groups.  V tile: chunk c of row r at
+// r * 16 + (c ^ 2(r & 3)), so the four rows of a transposed read hit four
+// different 32-byte spans.  Tiles arrive by direct global->LDS copies (lane l of copy i fills
+// slot 64i + l, so the layout is chosen by which chunk each lane fetches),
+// up to two tiles ahead of the one being computed.
 __device__ __forceinline__ int k_slot(int r, int c) { return r * kKC + (c ^ ((r >> 1) & 7)); }
 
-__global__ void __launch_bounds__(256) prefill_attention_kernel(PrefillParams p, RopeTable64 rope) {
-  __shared__ __attribute__((aligned(16))) char ktile[kKTile];
-  __shared__ __attribute__((aligned(16))) char vtile[kVTile];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int head = blockIdx.y;
-  const int nqb = (p.T + 127) / 128;
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x);  // longest blocks first
-  const int q0 = qb * 128 + 32 * wave;                   // this wave's first query
+__global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillParams p, RopeTable64 rope) {
+  __shared__ __attribute__((aligned(1024))) char tiles_raw[kNBuf * kBuf];
+  MLA_LDS char* tiles = (MLA_LDS char*)tiles_raw;
+  const uint32_t tiles_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles));
+  const int tid = threadIdx.x, lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroups reach the eight XCDs round-robin by linear id.  The n-th
+  // workgroup on XCD x takes head x + 8(n / nqb) and query block n % nqb
+  // (longest first), so the query blocks of one head run together on one XCD
+  // and read that head's keys and values through its L2.
+  const int nqb = (p.T + kQB - 1) / kQB;
+  const int id = blockIdx.x + gridDim.x * blockIdx.y;
+  const int xcd = id & 7, n = id >> 3;
+  const int head = xcd + 8 * (n / nqb);
+  const int qb = nqb - 1 - n % nqb;
+  if (head >= p.n_h) return;
+  const int q0 = qb * kQB + 32 * wave;                   // this wave's first query
   const int my_q = q0 + l32;
   const int qc = min(my_q, p.T - 1);
 
@@ -92,6 +114,7 @@ __global__ void __launch_bounds__(256) prefill_attention_kernel(PrefillParams p,
         qf[8 + s][e] = f32_to_bf16(a * cs - b * sn);
         qf[10 + s][e] = f32_to_bf16(a * sn + b * cs);
       }
+    wait_vmcnt<0>();  // complete before the tile copies start counting
   }
 
   // per-lane LDS offsets
@@ -108,37 +131,28 @@ __global__ void __launch_bounds__(256) prefill_attention_kernel(PrefillParams p,
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int chunk = 8 * (ct >> 1) + 4 * (ct & 1) + 2 * cg + ((L & 3) >> 1);
-        pv_off[ks][h2][ct] = (row * kVS + chunk) * 16 + 8 * (L & 1);
+        pv_off[ks][h2][ct] = (row * kVS + (chunk ^ (2 * (row & 3)))) * 16 + 8 * (L & 1);
       }
     }
 
-  // staging: thread t copies key chunks t + 256m (m < 3) and value chunks t + 256m (m < 2)
-  bf16x8_t kr[3], vr[2];
-  auto fetch = [&](int k) {
+  // copies of tile k into buffer bi: copy i = wave + 8j; the first 24 fill the
+  // key rows, the last 16 the value rows
+  auto issue = [&](int k, int bi) {
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const int i = tid + 256 * m, r = i / kKC, c = i - r * kKC;
-      const int key = min(32 * k + r, p.T - 1);
-      kr[m] = c < 16 ? ld8(p.k_nope + (static_cast<int64_t>(key) * p.n_h + head) * kPH + 8 * c)
-                     : ld8(p.k_rope + static_cast<int64_t>(key) * p.k_rope_stride + 8 * (c - 16));
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int i = tid + 256 * m, r = i >> 4, c = i & 15;
-      const int key = min(32 * k + r, p.T - 1);
-      vr[m] = ld8(p.v + (static_cast<int64_t>(key) * p.n_h + head) * kPV + 8 * c);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const int i = tid + 256 * m, r = i / kKC, c = i - r * kKC;
-      *reinterpret_cast<bf16x8_t*>(ktile + k_slot(r, c) * 16) = kr[m];
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int i = tid + 256 * m, r = i >> 4, c = i & 15;
-      *reinterpret_cast<bf16x8_t*>(vtile + (r * kVS + c) * 16) = vr[m];
+    for (int j = 0; j < kCopies; ++j) {
+      const int i = wave + kWaves * j, slot = 64 * i + lane;
+      const __bf16* g;
+      if (i < kKTile / 1024) {
+        const int r = slot / kKC, c = (slot - r * kKC) ^ ((r >> 1) & 7);
+        const int key = min(kTK * k + r, p.T - 1);
+        g = c < 16 ? p.k_nope + (static_cast<int64_t>(key) * p.n_h + head) * kPH + 8 * c
+                   : p.k_rope + static_cast<int64_t>(key) * p.k_rope_stride + 8 * (c - 16);
+      } else {
+        const int s2 = slot - kKTile / 16, r = s2 / kVS, c = (s2 - r * kVS) ^ (2 * (r & 3));
+        const int key = min(kTK * k + r, p.T - 1);
+        g = p.v + (static_cast<int64_t>(key) * p.n_h + head) * kPV + 8 * c;
+      }
+      dma16(g, tiles_addr + bi * kBuf + i * 1024);
     }
   };
 
@@ -146,26 +160,39 @@ __global__ void __launch_bounds__(256) prefill_attention_kernel(PrefillParams p,
 #pragma unroll
   for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int last_key = min(qb * 128 + 127, p.T - 1);
-  const int n_tiles = last_key / 32 + 1;
-  fetch(0);
-  for (int k = 0; k < n_tiles; ++k) {
-    stage();
-    __syncthreads();
-    if (k + 1 < n_tiles) fetch(k + 1);
-    if (32 * k <= q0 + 31) {  // some key of the tile is visible to this wave
-      f32x16_t sacc = f32x16_t{};
+  const int last_key = min(qb * kQB + kQB - 1, p.T - 1);
+  const int n_tiles = last_key / kTK + 1;
 #pragma unroll
-      for (int s = 0; s < kPD / 16; ++s) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ktile + kq_off[s]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc, 0, 0, 0);
+  for (int k = 0; k < kNBuf - 1; ++k)
+    if (k < n_tiles) issue(k, k);
+  for (int k = 0; k < n_tiles; ++k) {
+    // copies still allowed in flight: those of the tiles issued after tile k
+    if (k + 1 < n_tiles) wait_vmcnt<kCopies>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // tile k visible to all; tile k-1 released by all
+    if (k + kNBuf - 1 < n_tiles) issue(k + kNBuf - 1, (k + kNBuf - 1) % kNBuf);
+#pragma unroll
+    for (int sub = 0; sub < kTK / 32; ++sub) {
+    const int key0 = kTK * k + 32 * sub;
+    MLA_LDS char* ktile = tiles + (k % kNBuf) * kBuf + sub * (32 * kKC * 16);
+    MLA_LDS char* vtile = tiles + (k % kNBuf) * kBuf + kKTile + sub * (32 * kVS * 16);
+    if (key0 <= q0 + 31) {  // some key of the sub-tile is visible to this wave
+      // two independent chains over the even and odd k-steps, added at the end
+      f32x16_t sa = f32x16_t{}, sb = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < kPD / 16; s += 2) {
+        const bf16x8_t ka = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + kq_off[s]);
+        const bf16x8_t kb = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + kq_off[s + 1]);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s + 1], sb, 0, 0, 0);
       }
-      // register r holds key 32k + 8(r/4) + 4hf + r%4
+      const f32x16_t sacc = sa + sb;
+      // register r holds key key0 + 8(r/4) + 4hf + r%4
       float sv[16];
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * k + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int key = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
         sv[r] = key <= my_q ? sacc[r] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, sv[r]);
       }
@@ -183,21 +210,24 @@ __global__ void __launch_bounds__(256) prefill_attention_kernel(PrefillParams p,
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
+      // the accumulators are rescaled only when some query's maximum grew
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] *= alpha;
+        for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] *= alpha;
+      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int ct = 0; ct < kPV / 32; ++ct) {
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<MLA_LDS i16x4_t*>((MLA_LDS char*)vtile + pv_off[ks][0][ct]));
+              reinterpret_cast<MLA_LDS i16x4_t*>(vtile + pv_off[ks][0][ct]));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<MLA_LDS i16x4_t*>((MLA_LDS char*)vtile + pv_off[ks][1][ct]));
+              reinterpret_cast<MLA_LDS i16x4_t*>(vtile + pv_off[ks][1][ct]));
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[ct], 0, 0, 0);
         }
     }
-    __syncthreads();  // every wave is done with the tile before the next is staged
+    }
   }
 
   // epilogue: normalise and store the rows of this wave's queries
@@ -237,7 +267,10 @@ hipError_t launch_prefill_attention(const PrefillArgs& a, hipStream_t st) {
   p.scale_log2 = a.scale * 1.4426950408889634f;
   RopeTable64 rope;
   for (int k = 0; k < 32; ++k) rope.inv[k] = std::pow(static_cast<double>(a.theta), -2.0 * k / kPR);
-  hipLaunchKernelGGL(prefill_attention_kernel, dim3((a.seq_len + 127) / 128, a.n_h), dim3(256), 0, st, p, rope);
+  // n_h heads x nqb query blocks, padded to a multiple of 8 heads (the extra workgroups exit at once)
+  const int nqb = (a.seq_len + kQB - 1) / kQB;
+  const int heads8 = (a.n_h + 7) / 8 * 8;
+  hipLaunchKernelGGL(prefill_attention_kernel, dim3(nqb, heads8), dim3(64 * kWaves), 0, st, p, rope);
   return hipGetLastError();
 }
 
