@@ -12,7 +12,8 @@
 // w owns queries 32w..32w+31 of the block.  The keys and values of each
 // 64-token tile are staged once in LDS and shared by the eight waves (a
 // workgroup of 128 queries fetched twice the bytes per flop and was bound by
-// them).  Per 32-key sub-tile, per wave (bf16 MFMA 32x32x16, fp32 accumulate):
+// them).  Per 64-key tile, per wave (bf16 MFMA 32x32x16, fp32 accumulate), as
+// two 32-key sub-tiles whose score chains run side by side:
 //   S^T[key, q] = sum_d K[key, d] Q[q, d]     A = K tile (ds_read_b128),
 //                                             B = Q^T, register resident
 //   (two chains over the even and odd k-steps), online softmax over the keys
@@ -171,43 +172,43 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // tile k visible to all; tile k-1 released by all
     if (k + kNBuf - 1 < n_tiles) issue(k + kNBuf - 1, (k + kNBuf - 1) % kNBuf);
+    MLA_LDS char* ktile = tiles + (k % kNBuf) * kBuf;
+    MLA_LDS char* vtile = ktile + kKTile;
+    const int key0 = kTK * k;
+    if (key0 <= q0 + 31) {  // some key of the tile is visible to this wave
+      // scores of the two 32-key sub-tiles: two independent MFMA chains
+      f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-    for (int sub = 0; sub < kTK / 32; ++sub) {
-    const int key0 = kTK * k + 32 * sub;
-    MLA_LDS char* ktile = tiles + (k % kNBuf) * kBuf + sub * (32 * kKC * 16);
-    MLA_LDS char* vtile = tiles + (k % kNBuf) * kBuf + kKTile + sub * (32 * kVS * 16);
-    if (key0 <= q0 + 31) {  // some key of the sub-tile is visible to this wave
-      // two independent chains over the even and odd k-steps, added at the end
-      f32x16_t sa = f32x16_t{}, sb = f32x16_t{};
+      for (int s = 0; s < kPD / 16; ++s)
 #pragma unroll
-      for (int s = 0; s < kPD / 16; s += 2) {
-        const bf16x8_t ka = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + kq_off[s]);
-        const bf16x8_t kb = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + kq_off[s + 1]);
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s + 1], sb, 0, 0, 0);
-      }
-      const f32x16_t sacc = sa + sb;
-      // register r holds key key0 + 8(r/4) + 4hf + r%4
-      float sv[16];
+        for (int sub = 0; sub < 2; ++sub) {
+          const bf16x8_t kf = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + sub * (32 * kKC * 16) + kq_off[s]);
+          sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[sub], 0, 0, 0);
+        }
+      // register r of sub-tile u holds key key0 + 32u + 8(r/4) + 4hf + r%4
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        sv[r] = key <= my_q ? sacc[r] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[r]);
-      }
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * sub + 8 * (r >> 2) + 4 * hf + (r & 3);
+          sc[sub][r] = key <= my_q ? sc[sub][r] * p.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, sc[sub][r]);
+        }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       // key 0 is visible to every query, so m_new is finite from the first tile on
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      bf16x8_t pf[2];
+      bf16x8_t pf[4];
       float psum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(sv[r] - m_new);
-        psum += pr;
-        pf[r >> 3][r & 7] = f32_to_bf16(pr);
-      }
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = __builtin_amdgcn_exp2f(sc[sub][r] - m_new);
+          psum += pr;
+          pf[2 * sub + (r >> 3)][r & 7] = f32_to_bf16(pr);
+        }
       l_run = l_run * alpha + psum;
       m_run = m_new;
       // the accumulators are rescaled only when some query's maximum grew
@@ -215,18 +216,19 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
 #pragma unroll
         for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] *= alpha;
       }
+      // k-steps 0, 1 sum the first sub-tile's values, 2, 3 the second's
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int ct = 0; ct < kPV / 32; ++ct) {
+          MLA_LDS char* vb = vtile + (ks >> 1) * (32 * kVS * 16);
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<MLA_LDS i16x4_t*>(vtile + pv_off[ks][0][ct]));
+              reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[ks & 1][0][ct]));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<MLA_LDS i16x4_t*>(vtile + pv_off[ks][1][ct]));
+              reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[ks & 1][1][ct]));
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[ct], 0, 0, 0);
         }
-    }
     }
   }
 
