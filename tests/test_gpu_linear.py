@@ -28,7 +28,8 @@ if torch.cuda.is_available():
 # (m, n, k): one token, ragged token tails, one and several k slices, the
 # V3 query path (W^DQ, W^UQ, W^QR) and output projection (W^O) at 64 tokens
 SHAPES = [(1, 128, 16), (5, 128, 48), (33, 256, 4096), (100, 384, 1024), (300, 128, 2048),
-          (64, 1536, 7168), (64, 16384, 1536), (64, 8192, 1536), (64, 7168, 16384)]
+          (64, 1536, 7168), (64, 16384, 1536), (64, 8192, 1536), (64, 7168, 16384),
+          (2100, 256, 512)]   # many tokens: each workgroup makes several token passes
 
 
 def _bf16(rng, shape, scale=1.0):
@@ -49,6 +50,18 @@ def test_linear_matches_definition(m, n, k):
     mla.linear(x, w, y)
     torch.cuda.synchronize()
     assert ov.rel_err(_host_bf16(y), x64 @ w64.T) <= ov.TOL["bf16"]
+
+
+def test_linear_strided_rows():
+    """x read from rows ldx elements apart (the latent part of cache rows)."""
+    rng = np.random.default_rng(6)
+    m, n, k, ldx = 1500, 384, 512, 576
+    rows, rows64 = _bf16(rng, (m, ldx))
+    w, w64 = _bf16(rng, (n, k), 1.0 / np.sqrt(k))
+    y = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    mla.linear(rows[:, :k], w, y, ldx=ldx)
+    torch.cuda.synchronize()
+    assert ov.rel_err(_host_bf16(y), rows64[:, :k] @ w64.T) <= ov.TOL["bf16"]
 
 
 def test_linear_repeat_is_bitwise_identical():
