@@ -25,6 +25,7 @@
 // workspace and linear_reduce_kernel sums them.
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace mla {
 namespace {
@@ -118,6 +119,78 @@ __global__ void __launch_bounds__(256) linear_kernel(const __bf16* __restrict__ 
   }
 }
 
+// Many tokens over a short contraction (the prefill's key and value
+// up-projections, k = d_c = 512): the weight rows stay in registers for the
+// whole call and only activation tiles move.  grid (N/256 row groups, Z
+// token groups), 8 waves: wave v holds rows 32v..32v+31 of its group (32
+// k-steps, 128 VGPRs).  Per pass of 64 tokens the workgroup copies the
+// activation tile (64 rows x 1 KB) straight into LDS, one pass ahead of the
+// one computed (two buffers); chunk c of row r sits at r * 64 + (c ^ (r % 16))
+// so the fragment reads are conflict-free.  Each wave then runs 64 MFMAs and
+// stores its 32 columns of the 64 rows.
+constexpr int kWsRows = 256, kWsK = 512, kWsWaves = 8;
+constexpr int kWsTile = 64 * kWsK * 2;              // 64 KB
+constexpr int kWsCopies = kWsTile / 1024 / kWsWaves;  // copies per wave per pass
+
+__global__ void __launch_bounds__(64 * kWsWaves) linear_ws_kernel(const __bf16* __restrict__ x, int ldx,
+                                                                  const __bf16* __restrict__ w, int M, int N,
+                                                                  __bf16* __restrict__ y) {
+  __shared__ __attribute__((aligned(1024))) char xs_raw[2 * kWsTile];
+  MLA_LDS char* xs = (MLA_LDS char*)xs_raw;
+  const uint32_t xs_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(xs));
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * kWsRows + 32 * wave;
+  bf16x8_t bw[kWsK / 16];
+  {
+    const __bf16* wrow = w + static_cast<int64_t>(n0 + l32) * kWsK + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < kWsK / 16; ++s) bw[s] = load8(wrow + 16 * s);
+    wait_vmcnt<0>();  // complete before the tile copies start counting
+  }
+  const int tiles = (M + 63) / 64;
+  const int np = (tiles - static_cast<int>(blockIdx.y) + gridDim.y - 1) / gridDim.y;
+  auto issue = [&](int pass, int buf) {
+    const int m0 = (blockIdx.y + gridDim.y * pass) * 64;
+#pragma unroll
+    for (int j = 0; j < kWsCopies; ++j) {
+      const int i = wave + kWsWaves * j, slot = 64 * i + lane;
+      const int r = slot >> 6, c = (slot & 63) ^ (r & 15);
+      const __bf16* g = x + static_cast<int64_t>(min(m0 + r, M - 1)) * ldx + 8 * c;
+      dma16(g, xs_addr + buf * kWsTile + i * 1024);
+    }
+  };
+  if (np > 0) issue(0, 0);
+  for (int pass = 0; pass < np; ++pass) {
+    if (pass + 1 < np) {
+      issue(pass + 1, (pass + 1) & 1);
+      wait_vmcnt<kWsCopies>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();  // every wave's copies of this pass have landed
+    MLA_LDS char* buf = xs + (pass & 1) * kWsTile;
+    const int m0 = (blockIdx.y + gridDim.y * pass) * 64;
+    f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int s = 0; s < kWsK / 16; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int r = 32 * mt + l32, c = 2 * s + hf;
+        const bf16x8_t a = *reinterpret_cast<MLA_LDS const bf16x8_t*>(buf + (r * 64 + (c ^ (r & 15))) * 16);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw[s], acc[mt], 0, 0, 0);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (m < M) y[static_cast<int64_t>(m) * N + n0 + l32] = f32_to_bf16(acc[mt][r]);
+      }
+    __builtin_amdgcn_s_barrier();  // every wave is done with this buffer before it is refilled
+  }
+}
+
 // y[m][4q..4q+3] = bf16(sum over slices of the partials); grid (column
 // quads / 256, M).  Every slice's quad is requested before any is summed
 // (MAXC >= n_chunks loads; the ones past n_chunks repeat the last slice).
@@ -148,7 +221,12 @@ __global__ void __launch_bounds__(256) linear_reduce_kernel(const float* __restr
 // bytes (measured on the V3 shapes at 64 tokens: W^DQ with 16 slices and
 // W^QR with 4 run 2-5 us faster than with twice as many, W^O with 8 runs 7 us
 // faster than with 16).
+// The weight-stationary form serves k = 512 with at least 256 tokens and
+// rows in groups of 256; it needs no workspace.
+bool linear_weight_stationary(int m, int n, int k) { return k == kWsK && m >= 256 && n % kWsRows == 0; }
+
 int linear_chunks(int m, int n, int k) {
+  if (linear_weight_stationary(m, n, k)) return 1;
   const int groups = n / kLinRows;
   int c = 1;
   while (2 * c <= kLinMaxChunks && groups * 2 * c <= 512) c *= 2;
@@ -163,6 +241,18 @@ size_t linear_workspace(int m, int n, int k) {
 }
 
 hipError_t launch_linear(const LinearArgs& a, hipStream_t st) {
+  if (linear_weight_stationary(a.m, a.n, a.k)) {
+    // one workgroup per CU (128 KB of LDS each): as many token groups as fill the GPU once
+    const int groups = a.n / kWsRows;
+    int z = 256 / groups;
+    z = z < 1 ? 1 : z;
+    const int tiles = (a.m + 63) / 64;
+    z = z > tiles ? tiles : z;
+    hipLaunchKernelGGL(linear_ws_kernel, dim3(groups, z), dim3(64 * kWsWaves), 0, st,
+                       static_cast<const __bf16*>(a.x), a.ldx, static_cast<const __bf16*>(a.w), a.m, a.n,
+                       static_cast<__bf16*>(a.y));
+    return hipGetLastError();
+  }
   const int chunks = linear_chunks(a.m, a.n, a.k);
   const int mt = a.m <= 32 ? 1 : 2;
   int groups = (a.m + 32 * mt - 1) / (32 * mt);

@@ -123,6 +123,8 @@ def test_linear_sizes_and_host_checks():
     assert mla.linear_workspace_size(64, 8192, 1536) == 4 * 64 * 8192 * 4
     # many tokens, few columns: the cap leaves one slice
     assert mla.linear_workspace_size(4096, 128, 4096) == 0
+    # many tokens over k = 512 (prefill up-projections): the weight-stationary form, no workspace
+    assert mla.linear_workspace_size(4096, 16384, 512) == 0
     # a large row count needs no slices
     assert mla.linear_workspace_size(64, 65536, 128) == 0
     assert mla.linear_workspace_size(64, 100, 128) == 0              # unsupported: 0

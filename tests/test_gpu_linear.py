@@ -55,7 +55,7 @@ def test_linear_matches_definition(m, n, k):
 def test_linear_strided_rows():
     """x read from rows ldx elements apart (the latent part of cache rows)."""
     rng = np.random.default_rng(6)
-    m, n, k, ldx = 1500, 384, 512, 576
+    m, n, k, ldx = 1500, 512, 512, 576
     rows, rows64 = _bf16(rng, (m, ldx))
     w, w64 = _bf16(rng, (n, k), 1.0 / np.sqrt(k))
     y = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
