@@ -48,7 +48,7 @@ constexpr int kTK = 64;                 // keys per staged tile (two 32-key MFMA
 constexpr int kKTile = kTK * kKC * 16;  // 24,576 B
 constexpr int kVTile = kTK * kVS * 16;  // 16,384 B
 constexpr int kBuf = kKTile + kVTile;   // one tile: 40 wave-wide 1 KB copies
-constexpr int kNBuf = 3;                // tiles in LDS: the one computed and two landing
+constexpr int kNBuf = 4;                // tiles in LDS (160 KB): the one computed and three landing
 constexpr int kCopies = kBuf / 1024 / kWaves;  // copies per wave per tile
 
 struct PrefillParams {
@@ -71,7 +71,7 @@ __device__ __forceinline__ bf16x8_t ld8(const __bf16* p) { return *reinterpret_c
 // r * 16 + (c ^ 2(r & 3)), so the four rows of a transposed read hit four
 // different 32-byte spans.  Tiles arrive by direct global->LDS copies (lane l of copy i fills
 // slot 64i + l, so the layout is chosen by which chunk each lane fetches),
-// up to two tiles ahead of the one being computed.
+// up to three tiles ahead of the one being computed.
 __device__ __forceinline__ int k_slot(int r, int c) { return r * kKC + (c ^ ((r >> 1) & 7)); }
 
 __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillParams p, RopeTable64 rope) {
@@ -168,8 +168,11 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
     if (k < n_tiles) issue(k, k);
   for (int k = 0; k < n_tiles; ++k) {
     // copies still allowed in flight: those of the tiles issued after tile k
-    if (k + 1 < n_tiles) wait_vmcnt<kCopies>();
-    else wait_vmcnt<0>();
+    switch (min(n_tiles - 1 - k, kNBuf - 2)) {  // copies of the tiles issued after tile k may be in flight
+      case 2: wait_vmcnt<2 * kCopies>(); break;
+      case 1: wait_vmcnt<kCopies>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
     __builtin_amdgcn_s_barrier();  // tile k visible to all; tile k-1 released by all
     if (k + kNBuf - 1 < n_tiles) issue(k + kNBuf - 1, (k + kNBuf - 1) % kNBuf);
     MLA_LDS char* ktile = tiles + (k % kNBuf) * kBuf;

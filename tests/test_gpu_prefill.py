@@ -74,3 +74,29 @@ def test_prefill_first_token_is_its_own_value():
     mla.prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out)
     torch.cuda.synchronize()
     assert np.array_equal(_host_bf16(out)[0], v64[0])
+
+
+def test_prefill_full_size_sampled():
+    """The size bench.py times (one 4096-token prompt, 128 heads, the
+    weight-stationary up-projections), checked on sampled queries and heads."""
+    rng = np.random.default_rng(4200)
+    n_h, T = 128, 4096
+    dims = mla.make_dims(n_h, D_C, D_H, D_R, D_V, 7168, 64, "bf16", "bf16")
+    rows, rows64 = _bf16(rng, (T, D_C + D_R))
+    w_uk, wuk64 = _bf16(rng, (n_h, D_H, D_C), 1.0 / np.sqrt(D_C))
+    w_uv, wuv64 = _bf16(rng, (n_h, D_V, D_C), 1.0 / np.sqrt(D_C))
+    q_nope, qn64 = _bf16(rng, (T, n_h, D_H))
+    q_pe, qp64 = _bf16(rng, (T, n_h, D_R))
+    k_nope = torch.empty(T, n_h, D_H, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty(T, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    mla.linear(rows[:, :D_C], w_uk.view(n_h * D_H, D_C), k_nope, ldx=D_C + D_R)
+    mla.linear(rows[:, :D_C], w_uv.view(n_h * D_V, D_C), v, ldx=D_C + D_R)
+    out = torch.empty(T, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    mla.prefill_attention(dims, q_nope, q_pe, k_nope, rows[:, D_C:], v, out)
+    torch.cuda.synchronize()
+    got = _host_bf16(out)
+    qs = np.array([0, 1, 255, 256, 2047, 4095])
+    heads = [0, 63, 127]
+    want = ref.attention_nonabsorbed(qn64[qs], qp64[qs], qs, rows64[:, :D_C], rows64[:, D_C:], wuk64, wuv64,
+                                     1.0 / np.sqrt(D_H + D_R), heads=heads)
+    assert ov.rel_err(got[qs][:, heads], want) <= ov.TOL["bf16"]
