@@ -204,11 +204,17 @@ def prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out, lse=None):
     k_rope is a [T, d_R] view whose rows may be strided (e.g. the RoPE part
     of contiguous cache rows)."""
     T = q_nope.shape[0]
-    if k_rope.dim() != 2 or k_rope.stride(1) != 1 or k_rope.shape[0] != T or not k_rope.is_cuda:
+    n_h, d_h, d_r, d_v = dims.num_heads, dims.qk_nope_head_dim, dims.qk_rope_head_dim, dims.v_head_dim
+    if (k_rope.dim() != 2 or k_rope.stride(1) != 1 or k_rope.shape[0] != T or k_rope.shape[1] != d_r
+            or not k_rope.is_cuda):
         raise ValueError("prefill_attention: k_rope must be a [T, d_R] device view with unit column stride")
-    for name, t in (("q_pe", q_pe), ("k_nope", k_nope), ("v", v), ("out", out)):
-        if t.shape[0] != T:
-            raise ValueError(f"prefill_attention: {name} has {t.shape[0]} rows, expected {T}")
+    for name, t, width in (("q_nope", q_nope, d_h), ("q_pe", q_pe, d_r), ("k_nope", k_nope, d_h), ("v", v, d_v),
+                           ("out", out, d_v)):
+        if t.shape[0] != T or t.numel() != T * n_h * width or t.dtype != torch.bfloat16:
+            raise ValueError(f"prefill_attention: {name} must be bf16 [{T}, {n_h}, {width}], got "
+                             f"{t.dtype} {tuple(t.shape)}")
+    if lse is not None and (lse.numel() != T * n_h or lse.dtype != torch.float32):
+        raise ValueError("prefill_attention: lse must be float32 [T, n_h]")
     _check(lib().mla_prefill_attention(ctypes.byref(dims), _ptr(q_nope), _ptr(q_pe), _ptr(k_nope),
                                        k_rope.data_ptr(), k_rope.stride(0), _ptr(v), T, _ptr(out), _ptr(lse),
                                        _stream(out.device)))

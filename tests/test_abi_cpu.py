@@ -136,3 +136,20 @@ def test_linear_sizes_and_host_checks():
     assert lib.mla_linear(P(1), 128, P(1), 0, 128, 128, P(1), None, 0, None) == 0     # nothing to do
     assert lib.mla_linear(P(1), 100, P(1), 4, 128, 128, P(1), None, 0, None) == 1   # ldx < k
     assert lib.mla_linear(P(1), 16384, P(1), 64, 7168, 16384, P(1), P(1), 16, None) == 3     # workspace too small
+
+
+def test_prefill_host_checks():
+    lib = mla.lib()
+    P = ctypes.c_void_p
+    d = v3_dims()
+
+    def call(dims=d, T=128, stride=576, q=P(1)):
+        return lib.mla_prefill_attention(ctypes.byref(dims), q, P(1), P(1), P(1), stride, P(1), T, P(1), None,
+                                         None)
+    assert call(T=0) == 0                                   # nothing to do
+    assert call(T=-1) == 1
+    assert call(q=None) == 1
+    assert call(stride=60) == 1                             # shorter than d_R
+    assert call(stride=100) == 1                            # rows not 16-byte aligned
+    assert call(dims=v3_dims(cache_dtype="fp8")) == 2       # bf16 cache and activations only
+    assert call(dims=mla.make_dims(4, 32, 16, 8, 16, 64, 64, "f32", "f32")) == 2
