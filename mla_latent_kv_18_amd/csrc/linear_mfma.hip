@@ -8,8 +8,12 @@
 // absorbed form sum_i B_i o_lat_i with B_i = W^O_i W^UV_i [MLA explainer,
 // value-side absorption eq.(11)].
 //
-// M is the step's token count (tens); N and K are thousands, so the weight
-// read bounds the call.  bf16 operands, fp32 accumulation on MFMA 32x32x16.
+// and, with many tokens over K = 512, for the prefill's key and value
+// up-projections W^UK_i c and W^UV_i c (linear_ws_kernel below).
+//
+// In the decode step M is the step's token count (tens); N and K are
+// thousands, so the weight read bounds the call.  bf16 operands, fp32
+// accumulation on MFMA 32x32x16.
 //
 // grid (N/128 row groups, n_chunks K slices, token groups), 4 waves: wave v
 // owns weight rows 32v..32v+31 of its group and reads the whole K slice, so
