@@ -153,3 +153,14 @@ def test_prefill_host_checks():
     assert call(stride=100) == 1                            # rows not 16-byte aligned
     assert call(dims=v3_dims(cache_dtype="fp8")) == 2       # bf16 cache and activations only
     assert call(dims=mla.make_dims(4, 32, 16, 8, 16, 64, 64, "f32", "f32")) == 2
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """No fallback: without libmla.so every call raises instead of computing
+    something else."""
+    monkeypatch.setattr(mla, "LIB_PATH", str(tmp_path / "absent" / "libmla.so"))
+    monkeypatch.setattr(mla, "_lib", None)
+    with pytest.raises(ImportError):
+        mla.lib()
+    with pytest.raises(ImportError):
+        mla.linear_workspace_size(64, 128, 128)
