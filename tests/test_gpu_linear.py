@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import mla_latent_kv_18_amd as mla
     from mla_latent_kv_18_amd.inputs import WORKLOADS, generate, generate_block_weights
-    from mla_latent_kv_18_amd.step import DeviceStep
+    from mla_latent_kv_18_amd.step import BlockStep
 
 # (m, n, k): one token, ragged token tails, one and several k slices, the
 # V3 query path (W^DQ, W^UQ, W^QR) and output projection (W^O) at 64 tokens
@@ -76,23 +76,19 @@ def test_linear_repeat_is_bitwise_identical():
     assert torch.equal(y1, y2)
 
 
-def test_attention_block_end_to_end():
-    w = WORKLOADS["v3_bs64_ctx4k"].scaled(name="block", batch=2, lens=(70, 129), seed=21)
+@pytest.mark.parametrize("base,tol", [("v3_bs64_ctx4k", "bf16"), ("v3_fp8_bs4_ctx128k_q2", "fp8")])
+def test_attention_block_end_to_end(base, tol):
+    """BlockStep (query path, the four calls, W^O) against the oracle fed the
+    raw inputs; then the pages' absorbed output form (B_i = W^O_i W^UV_i on
+    o_lat) against the two-step output of the same run (eq.(11))."""
+    w = WORKLOADS[base].scaled(name="block", batch=2, lens=(70, 129), seed=21)
     gen = generate(w)
     blk = generate_block_weights(w)
-    step = DeviceStep(gen)
+    step = BlockStep(gen, blk)
     N = w.batch * w.q_len
-    assert step.h.shape[0] == N             # every request appends its q_len query tokens
-    dev = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in blk.items() if k != "d_cq"}
-    c_q = torch.empty(N, blk["d_cq"], dtype=torch.bfloat16, device="cuda")
-    mla.linear(step.h, dev["w_dq"], c_q)
-    mla.linear(c_q, dev["w_uq"], step.q_nope)
-    mla.linear(c_q, dev["w_qr"], step.q_pe)
     step.run()
-    u = torch.empty(N, w.d_model, dtype=torch.bfloat16, device="cuda")
-    mla.linear(step.out, dev["w_o"], u)
     torch.cuda.synchronize()
-    got = _host_bf16(u)
+    got = _host_bf16(step.u)
 
     f = {k: codecs.bf16_decode(v) for k, v in blk.items() if k != "d_cq"}
     _, wuk, wuv, _ = ov.weights(gen)
@@ -105,4 +101,9 @@ def test_attention_block_end_to_end():
         o = ref.attention_nonabsorbed(q_nope[sl], q_pe[sl], gen["q_positions"][sl], rows[:, :w.d_c],
                                       rows[:, w.d_c:], wuk, wuv, w.softmax_scale)
         want[sl] = ref.output_projection(o, f["w_o"])
-    assert ov.rel_err(got, want) <= ov.TOL["bf16"]
+    assert ov.rel_err(got, want) <= ov.TOL[tol]
+
+    step.absorbed_output_weights()
+    step.o_proj_absorbed()
+    torch.cuda.synchronize()
+    assert ov.rel_err(_host_bf16(step.u), got) <= ov.TOL["bf16"]
