@@ -16,6 +16,9 @@ same workload.  `block` (skipped with --no-block) times the whole attention
 block around the step: the query path W^DQ, W^UQ, W^QR and the output
 projection W^O through mla_linear, with W^O against its weight-read bound
 and the pages' absorbed output form (B_i = W^O_i W^UV_i) beside it.
+`prefill` (default workload; skipped with --no-prefill) times the prefill
+side on one 4096-token prompt: the key and value up-projections and the
+causal attention, which is reported against the bf16 MFMA peak.
 """
 
 import argparse
