@@ -44,17 +44,17 @@ def rope_half(x, pos, base=10000.0):
     """Rotary embedding with half-split pairing.
 
     x: [..., d] (d even); pos: positions broadcastable to x.shape[:-1].
-    Pair k (k < d/2) is (x_k, x_{k+d/2}) rotated by theta_k = pos/base^(2k/d).
-    [MLA explainer, "RoPE breaks absorption" section: the rope() helper;
+    Element k of the first half and element k of the second half form one
+    plane, turned by the angle pos * base^(-2k/d).  Written here as complex
+    multiplication: z_k = x_k + i x_{k+d/2} becomes z_k e^{i angle}.
+    [MLA explainer, "RoPE breaks absorption" section (pairing and angles);
     decoupled-RoPE section eq.(15)]."""
     x = np.asarray(x, dtype=np.float64)
-    d = x.shape[-1]
-    half = d // 2
-    inv = base ** (-(2.0 * np.arange(half)) / d)
-    theta = np.asarray(pos, dtype=np.float64)[..., None] * inv
-    c, s = np.cos(theta), np.sin(theta)
-    x1, x2 = x[..., :half], x[..., half:]
-    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+    half = x.shape[-1] // 2
+    k = np.arange(half, dtype=np.float64)
+    angle = np.asarray(pos, dtype=np.float64)[..., None] * np.power(base, -2.0 * k / x.shape[-1])
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * angle)
+    return np.concatenate([z.real, z.imag], axis=-1)
 
 
 def rmsnorm(x, gamma, eps):
@@ -200,6 +200,26 @@ def query_from_hidden(h, w_dq, w_uq, w_qr, n_h):
     q_nope = (c_q @ np.asarray(w_uq, np.float64).T).reshape(h.shape[0], n_h, -1)
     q_pe = (c_q @ np.asarray(w_qr, np.float64).T).reshape(h.shape[0], n_h, -1)
     return c_q, q_nope, q_pe
+
+
+def absorbed_query_weights(w_uq, w_uk):
+    """Query-side absorption: the latent query of head i straight from the
+    query latent, q~_i = A_i c^Q with A_i = W^UK_i^T W^UQ_i (d_c x d'_c).
+    [MLA explainer, matrix absorption eq.(7)-(8) and query-compression
+    section (A_i becomes d'_c x d_c in the page's row-vector form)].
+    w_uq [n_h*d_h, d'_c] (head i's rows contiguous), w_uk [n_h, d_h, d_c]
+    -> A stacked by head, [n_h*d_c, d'_c] (an [out, in] weight)."""
+    w_uq = np.asarray(w_uq, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    n_h, d_h, _ = w_uk.shape
+    return np.concatenate([w_uk[i].T @ w_uq[i * d_h:(i + 1) * d_h] for i in range(n_h)], axis=0)
+
+
+def query_latent_absorbed(c_q, a, n_h):
+    """q~ [N, n_h, d_c] = A c^Q per head with A from absorbed_query_weights.
+    [MLA explainer eq.(8) with the query-compression form of q^C]."""
+    c_q = np.asarray(c_q, np.float64)
+    return (c_q @ np.asarray(a, np.float64).T).reshape(c_q.shape[0], n_h, -1)
 
 
 def output_projection(o, w_o):

@@ -25,32 +25,42 @@ def _golden(name):
 # The explainer page's seeded experiment, rebuilt from its stated shapes,
 # seed and draw order, evaluated through the oracle's own functions.
 # ---------------------------------------------------------------------------
+def _draw_schedule(setup):
+    """Draw the page's matrices from the schedule in the golden file: one
+    generator, in the listed order, each draw shaped and scaled as listed."""
+    rng = np.random.default_rng(setup["seed"])
+
+    def dim(expr):
+        return math.prod(setup[name] for name in expr.split("*"))
+
+    out = {}
+    for spec in setup["draws"]:
+        shape = tuple(dim(e) for e in spec["shape"])
+        if spec["dist"] == "normal":
+            x = rng.normal(size=shape)
+            fan_in = math.prod(setup[n] for n in spec["fan_in"])
+            out[spec["name"]] = x / np.sqrt(fan_in) if spec["fan_in"] else x
+        else:
+            x = rng.random(shape)
+            out[spec["name"]] = x / x.sum(axis=spec["normalise_axis"], keepdims=True)
+    return out
+
+
 @pytest.fixture(scope="module")
 def page_example():
     g = _golden("page_worked_example.json")
     s = g["setup"]
-    d, d_c, d_cq, d_h, n_h, T, d_r = (s[k] for k in ("d", "d_c", "d_cq", "d_h", "n_h", "T", "d_r"))
-    rng = np.random.default_rng(s["seed"])
-    H = rng.normal(size=(T, d))
-    W_DKV = rng.normal(size=(d, d_c)) / np.sqrt(d)
-    W_UK = rng.normal(size=(d_c, n_h * d_h)) / np.sqrt(d_c)
-    W_DQ = rng.normal(size=(d, d_cq)) / np.sqrt(d)
-    W_UQ = rng.normal(size=(d_cq, n_h * d_h)) / np.sqrt(d_cq)
-    W_UV = rng.normal(size=(d_c, n_h * d_h)) / np.sqrt(d_c)
-    W_O = rng.normal(size=(n_h * d_h, d)) / np.sqrt(n_h * d_h)
-    P = rng.random((T, T, n_h))
-    P /= P.sum(axis=1, keepdims=True)
-    W_QR = rng.normal(size=(d_cq, n_h * d_r)) / np.sqrt(d_cq)
-    W_KR = rng.normal(size=(d, d_r)) / np.sqrt(d)
+    d_c, d_h, n_h, T, d_r = (s[k] for k in ("d_c", "d_h", "n_h", "T", "d_r"))
+    m = _draw_schedule(s)
     # page layout (row vectors, head blocks of columns) -> oracle layout
-    w_uk = np.stack([W_UK[:, i * d_h:(i + 1) * d_h].T for i in range(n_h)])   # [n_h, d_h, d_c]
-    w_uv = np.stack([W_UV[:, i * d_h:(i + 1) * d_h].T for i in range(n_h)])   # [n_h, d_v, d_c]
-    C_kv = H @ W_DKV
-    C_q = H @ W_DQ
-    q_c = (C_q @ W_UQ).reshape(T, n_h, d_h)                                   # query content part
-    return dict(g=g, d_c=d_c, d_h=d_h, n_h=n_h, T=T, d_r=d_r, H=H, C_kv=C_kv, C_q=C_q,
-                q_c=q_c, w_uk=w_uk, w_uv=w_uv, W_O=W_O, P=P, W_QR=W_QR, W_KR=W_KR,
-                W_UQ=W_UQ, W_UK=W_UK)
+    w_uk = np.stack([m["W_UK"][:, i * d_h:(i + 1) * d_h].T for i in range(n_h)])   # [n_h, d_h, d_c]
+    w_uv = np.stack([m["W_UV"][:, i * d_h:(i + 1) * d_h].T for i in range(n_h)])   # [n_h, d_v, d_c]
+    C_kv = m["H"] @ m["W_DKV"]
+    C_q = m["H"] @ m["W_DQ"]
+    q_c = (C_q @ m["W_UQ"]).reshape(T, n_h, d_h)                                   # query content part
+    return dict(g=g, d_c=d_c, d_h=d_h, n_h=n_h, T=T, d_r=d_r, H=m["H"], C_kv=C_kv, C_q=C_q,
+                q_c=q_c, w_uk=w_uk, w_uv=w_uv, W_O=m["W_O"], P=m["P"], W_QR=m["W_QR"], W_KR=m["W_KR"],
+                W_UQ=m["W_UQ"], W_UK=m["W_UK"], W_DQ=m["W_DQ"])
 
 
 def _expanded_keys(e):
@@ -529,13 +539,7 @@ def test_page_query_path_value(page_example):
     e = page_example
     g = e["g"]["key_absorption"]
     n_h, d_h, d_r = e["n_h"], e["d_h"], e["d_r"]
-    s = e["g"]["setup"]
-    rng = np.random.default_rng(s["seed"])
-    rng.normal(size=(e["T"], s["d"]))                      # H, W_DKV, W_UK are redrawn in page order
-    rng.normal(size=(s["d"], e["d_c"]))
-    rng.normal(size=(e["d_c"], n_h * d_h))
-    W_DQ = rng.normal(size=(s["d"], s["d_cq"])) / np.sqrt(s["d"])
-    W_UQ = rng.normal(size=(s["d_cq"], n_h * d_h)) / np.sqrt(s["d_cq"])
+    W_DQ, W_UQ = e["W_DQ"], e["W_UQ"]
     # page layout (row vectors) -> [out, in]
     c_q, q_nope, q_pe = ref.query_from_hidden(e["H"], W_DQ.T, W_UQ.T, e["W_QR"].T, n_h)
     assert q_nope.shape == (e["T"], n_h, d_h) and q_pe.shape == (e["T"], n_h, d_r)
@@ -585,3 +589,114 @@ def test_absorbed_output_weights_equal_the_two_step_path():
     assert b.shape == (d, n_h * d_c)
     absorbed = ref.output_projection_absorbed(o_lat, b)
     assert np.max(np.abs(two_step - absorbed)) <= 1e-12 * np.max(np.abs(two_step))
+
+
+def test_query_rope_part_brute_force():
+    """The RoPE half of the query path, W^QR c^Q with head i's d_R rows
+    contiguous, against plain loops over the page's draws (a transposed or
+    mis-sliced W^QR fails here); and the page's decoupled-RoPE equality
+    with q^R taken from the oracle's query path."""
+    rng = np.random.default_rng(41)
+    n_h, d_r, d_h, d_cq, d, N = 3, 4, 2, 5, 6, 2
+    h = rng.normal(size=(N, d))
+    w_dq = rng.normal(size=(d_cq, d))
+    w_uq = rng.normal(size=(n_h * d_h, d_cq))
+    w_qr = rng.normal(size=(n_h * d_r, d_cq))
+    _, q_nope, q_pe = ref.query_from_hidden(h, w_dq, w_uq, w_qr, n_h)
+    for t in range(N):
+        c_q = [sum(w_dq[a, m] * h[t, m] for m in range(d)) for a in range(d_cq)]
+        for i in range(n_h):
+            for r in range(d_r):
+                want = sum(w_qr[i * d_r + r, a] * c_q[a] for a in range(d_cq))
+                assert abs(q_pe[t, i, r] - want) < 1e-12
+            for k in range(d_h):
+                want = sum(w_uq[i * d_h + k, a] * c_q[a] for a in range(d_cq))
+                assert abs(q_nope[t, i, k] - want) < 1e-12
+
+
+def test_page_decoupled_rope_through_query_path(page_example):
+    """The page's decoupled-RoPE check with q^R from query_from_hidden: the
+    scores of the expanded keys equal the absorbed scores over [c ; k^R]."""
+    e = page_example
+    n_h, T = e["n_h"], e["T"]
+    pos = np.arange(T)
+    _, q_nope, q_pe = ref.query_from_hidden(e["H"], e["W_DQ"].T, e["W_UQ"].T, e["W_QR"].T, n_h)
+    # the page's own layout: q^R = (C_q W_QR) split into head blocks of d_R columns
+    q_pe_page = (e["C_q"] @ e["W_QR"]).reshape(T, n_h, e["d_r"])
+    assert np.max(np.abs(q_pe - q_pe_page)) < 1e-12
+    KR = ref.rope_half(e["H"] @ e["W_KR"], pos)
+    QR = ref.rope_half(q_pe, pos[:, None])
+    S_naive = np.einsum("tih,jih->tji", q_nope, _expanded_keys(e)) + np.einsum("tir,jr->tji", QR, KR)
+    q_lat = ref.absorb_q(q_nope, q_pe, pos, e["w_uk"])
+    S_abs = np.einsum("tic,jc->tji", q_lat, np.concatenate([e["C_kv"], KR], axis=1))
+    assert np.max(np.abs(S_naive - S_abs)) < 1e-12
+
+
+def test_append_from_projection_matches_hidden_path_and_loops():
+    """The append step fed the down-projection output: equal to latent_rows
+    fed h, and to plain loops (norm over the latent only, RoPE on the rest)."""
+    rng = np.random.default_rng(42)
+    d_c, d_r, d, N = 6, 4, 9, 5
+    h = rng.normal(size=(N, d))
+    w = rng.normal(size=(d_c + d_r, d)) / np.sqrt(d)
+    gamma = rng.uniform(0.5, 1.5, size=d_c)
+    pos = np.array([0, 3, 17, 4095, 131071])
+    kv = h @ w.T
+    c, kr = ref.append_from_projection(kv, gamma, pos, d_c, 1e-6)
+    c2, kr2 = ref.latent_rows(h, w, gamma, pos, d_c, 1e-6)
+    assert np.max(np.abs(c - c2)) < 1e-12 and np.max(np.abs(kr - kr2)) < 1e-12
+    for j in range(N):
+        ms = sum(kv[j, r] ** 2 for r in range(d_c)) / d_c
+        for r in range(d_c):
+            assert abs(c[j, r] - kv[j, r] / math.sqrt(ms + 1e-6) * gamma[r]) < 1e-12
+        assert np.allclose(kr[j], _bf_rope(list(kv[j, d_c:]), float(pos[j])), rtol=0, atol=1e-9)
+    # the RoPE part is not normalised: scaling it scales k^R alone
+    c3, kr3 = ref.append_from_projection(np.concatenate([kv[:, :d_c], 3 * kv[:, d_c:]], 1), gamma, pos, d_c, 1e-6)
+    assert np.max(np.abs(c3 - c)) < 1e-12 and np.max(np.abs(kr3 - 3 * kr)) < 1e-12
+
+
+def test_page_query_absorbed_weights(page_example):
+    """A_i = W^UK_i^T W^UQ_i: the page's shape and rank (printed), and the
+    same latent query as the two-step path (c^Q -> q^C -> W^UK_i^T q^C)."""
+    e = page_example
+    g = e["g"]["key_absorption"]
+    n_h, d_c, d_h = e["n_h"], e["d_c"], e["d_h"]
+    a = ref.absorbed_query_weights(e["W_UQ"].T, e["w_uk"])
+    d_cq = e["g"]["setup"]["d_cq"]
+    assert a.shape == (n_h * d_c, d_cq)
+    # the page prints A as [n_h, d'_c, d_c] (row-vector form): the transpose of each block
+    blocks = np.stack([a[i * d_c:(i + 1) * d_c].T for i in range(n_h)])
+    assert list(blocks.shape) == g["A_shape"]
+    assert np.linalg.matrix_rank(blocks[0]) == g["A0_rank"] == d_h
+    q_lat = ref.query_latent_absorbed(e["C_q"], a, n_h)
+    two_step = ref.absorb_q(e["q_c"], np.zeros((e["T"], n_h, 0)), np.arange(e["T"]), e["w_uk"])
+    assert np.max(np.abs(q_lat - two_step)) < 1e-12
+    # and the page's printed score through it
+    S = np.einsum("tic,jc->tji", q_lat, e["C_kv"])
+    assert abs(S[3, 1, 0] - g["S_naive_t3_j1_h0"]) < 1e-12
+
+
+def test_absorbed_query_weights_brute_force():
+    rng = np.random.default_rng(43)
+    n_h, d_h, d_c, d_cq = 2, 3, 4, 5
+    w_uq = rng.normal(size=(n_h * d_h, d_cq))
+    w_uk = rng.normal(size=(n_h, d_h, d_c))
+    a = ref.absorbed_query_weights(w_uq, w_uk)
+    for i in range(n_h):
+        for c in range(d_c):
+            for m in range(d_cq):
+                want = sum(w_uk[i, k, c] * w_uq[i * d_h + k, m] for k in range(d_h))
+                assert abs(a[i * d_c + c, m] - want) < 1e-12
+
+
+def test_absorbed_output_weights_brute_force():
+    rng = np.random.default_rng(44)
+    n_h, d_v, d_c, d = 2, 3, 4, 5
+    w_o = rng.normal(size=(d, n_h * d_v))
+    w_uv = rng.normal(size=(n_h, d_v, d_c))
+    b = ref.absorbed_output_weights(w_o, w_uv)
+    for m in range(d):
+        for i in range(n_h):
+            for c in range(d_c):
+                want = sum(w_o[m, i * d_v + k] * w_uv[i, k, c] for k in range(d_v))
+                assert abs(b[m, i * d_c + c] - want) < 1e-12
