@@ -15,7 +15,9 @@
  *                      RoPE on k^R -> write the row into a paged cache
  *   mla_absorb_q       q~_i = W^UK_i^T q^C_i (latent query), RoPE on q^R
  *   mla_decode         scores over [c^KV ; k^R], softmax, latent-weighted sum
- *                      (split over the context, then a combine kernel)
+ *                      (split over the context, then a combine kernel), after
+ *                      mla_decode_plan has balanced the chunks; or
+ *                      mla_decode_uniform with one chunk length for all
  *   mla_out_proj       o_i = W^UV_i o_lat_i
  *   mla_linear         the dense projections around them (query path
  *                      W^DQ, W^UQ, W^QR; output W^O or the absorbed B_i;
@@ -29,7 +31,8 @@
  *     including the workspaces; libmla never allocates or frees device
  *     memory and keeps no mutable global state.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- *     stream) and never synchronise the host.
+ *     stream) and never synchronise the host, except mla_decode_plan, which
+ *     reads host lengths and waits for the copy of its work list.
  *   - Errors: every entry point checks its arguments on the host before any
  *     launch and returns a status; nothing is thrown across the ABI.  The
  *     text of the last error of the calling thread is returned by
@@ -70,7 +73,9 @@ typedef enum {
   MLA_ERR_INVALID_ARGUMENT = 1,
   MLA_ERR_UNSUPPORTED = 2,
   MLA_ERR_WORKSPACE_TOO_SMALL = 3,
-  MLA_ERR_HIP = 4
+  MLA_ERR_PLAN_MISMATCH = 4, /* a decode plan used with other dims, another
+                                workspace, or a modified plan struct */
+  MLA_ERR_HIP = 5
 } mla_status_t;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype_t;
@@ -102,6 +107,12 @@ typedef struct {
  * Returns 0 for invalid dims.  [MLA explainer, cache comparison section;
  * variants, MLA section: per-token elements = d_c + d_R per layer.] */
 size_t mla_cache_row_bytes(const mla_dims_t* dims);
+
+/* HBM bytes one cached token occupies in one layer: the row plus, for fp8,
+ * its fp32 scale ((d_c + d_R) * element size, + 4 for fp8).  Returns 0 for
+ * invalid dims.  [MLA explainer, cache comparison section: per-token cache
+ * of d_c + d_R elements per layer; variants, MLA section.] */
+size_t mla_cache_bytes_per_token(const mla_dims_t* dims);
 
 /* Bytes of one latent-query row q_lat[n, i] as mla_absorb_q writes it and
  * mla_decode reads it: (d_c + d_R) * element size for fp32 / bf16; for an
@@ -163,34 +174,121 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void
  *   s_j   = (q_lat . cache_j) * softmax_scale        j <= query position
  *   o_lat = sum_j softmax(s)_j cache_j[:d_c]         [eq.(9)-(10)]
  *   lse   = log sum_j exp(s_j)  (natural log)
- * The context of each request is cut into chunks of split_tokens rows;
- * each chunk writes a partial (o, lse) to the workspace and a combine kernel
- * merges them; with one chunk per request the partial step writes o_lat
- * directly.  split_tokens = 0 picks a size from the shapes; otherwise it
- * must be a positive multiple of 64 (bf16/fp8) and only changes rounding.
+ * The context of a request is cut into chunks; each chunk writes a partial
+ * (o, lse) to the workspace and a combine kernel merges them by the
+ * log-sum-exp rule; a request with one chunk writes o_lat directly.  The
+ * chunking only changes rounding.
+ *
+ * Two ways to launch it:
+ *   planned  mla_decode_plan (host, once per batch composition) turns the
+ *            host copy of the sequence lengths into a balanced work list in
+ *            the workspace; mla_decode then runs it.  Ragged batches get
+ *            chunks sized for the whole batch and placed across the eight
+ *            XCDs by load, and no workgroup is launched for nothing.
+ *   uniform  mla_decode_uniform cuts every request into chunks of one
+ *            length sized from max_seq_len alone; it needs no host copy of
+ *            the lengths, so a captured graph can replay it as they change.
+ *
+ * Common arguments:
  * q_lat: [batch*q_len, n_h] rows as mla_absorb_q writes them; q_scale as
- *   above.
+ *   there (fp8 only, else NULL).
  * cache: pool [num_blocks, block_size, d_c + d_R]; cache_scale [num_blocks,
  *   block_size] for fp8 else NULL.
  * block_table: [batch, max_blocks_per_seq] int32 physical block ids, each
  *   in [0, num_blocks) (out-of-range ids are clamped into the pool).
  * seq_lens: [batch] int32 device, T_b = rows cached for request b including
- *   this step's q_len rows; values are clamped to [0, max_seq_len].  A query
- *   with no visible key gets o_lat = 0 and lse = -inf.
- * max_seq_len (host): upper bound of seq_lens, <= max_blocks_per_seq *
- *   block_size; it sizes the grid and the workspace.
+ *   this step's q_len rows.  A query with no visible key gets o_lat = 0 and
+ *   lse = -inf.
  * o_lat: [batch*q_len, n_h, d_c] act_dtype.  lse: [batch*q_len, n_h] fp32
  *   (may be NULL). */
-size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
-                                 int32_t max_seq_len, int32_t split_tokens);
-mla_status_t mla_decode(const mla_dims_t* dims, const void* q_lat, const float* q_scale,
-                        const void* cache, const float* cache_scale,
-                        const int32_t* block_table, int32_t max_blocks_per_seq,
-                        int32_t num_blocks, const int32_t* seq_lens, int32_t batch, int32_t q_len,
-                        int32_t max_seq_len, int32_t split_tokens, void* workspace,
-                        size_t workspace_bytes, void* o_lat, float* lse, mla_stream_t stream);
 
-/* The chunk length mla_decode uses for split_tokens = 0 (host helper). */
+/* Decode plan: filled by mla_decode_plan, read by mla_decode.  Plain data
+ * owned by the caller; the work list it describes lives at the start of the
+ * workspace given to mla_decode_plan, which must be passed unchanged to
+ * mla_decode. */
+typedef struct {
+  int32_t batch;          /* requests */
+  int32_t q_len;          /* queries per request */
+  int32_t num_items;      /* context chunks over all requests */
+  int32_t max_splits;     /* most chunks of one request */
+  uint64_t hash;          /* digest of the dims, the fields below and the
+                             lengths planned for */
+  size_t workspace_bytes; /* workspace bytes mla_decode needs for this plan */
+  size_t image_bytes;     /* bytes at the start of the workspace that hold
+                             the work list (header, launch list, part_ptr) */
+  int32_t split_tokens;   /* chunk length, a multiple of 64 */
+  int32_t max_seq_len;    /* longest request planned for */
+  int32_t num_slots;      /* workgroups mla_decode launches */
+  int32_t num_partials;   /* chunks that write a partial (requests with >1 chunk) */
+  uint64_t seq_digest;    /* digest of the lengths planned for */
+  uint64_t workspace;     /* device address of the workspace planned into */
+} mla_plan_t;
+
+/* Workspace bytes a plan for these lengths needs (host seq_lens [batch]).
+ * Returns 0 for invalid arguments. */
+size_t mla_decode_plan_workspace_size(const mla_dims_t* dims, const int32_t* seq_lens_host,
+                                      int32_t batch, int32_t q_len, int32_t split_tokens_hint);
+
+/* Plans a decode over requests of the given lengths [V2 summary, "推論方法"
+ * (inference) section: one step over a batch of cached requests; MLA
+ * explainer, opening section: contexts up to 128k tokens].
+ * seq_lens_host: [batch] int32 host memory, the lengths the device array
+ *   passed to mla_decode will hold (each >= 0).
+ * split_tokens_hint: 0 picks the chunk length from the lengths (balanced
+ *   over the GPU's workgroup slots); otherwise a positive multiple of 64.
+ * plan: filled on success.  workspace: device memory of at least
+ *   mla_decode_plan_workspace_size() bytes; the work list is copied into it
+ *   on `stream`, and this call waits for that copy (the one synchronising
+ *   call of the library), so the plan can be reused for any number of
+ *   mla_decode calls (e.g. every layer of a step) while the lengths stay
+ *   the same. */
+mla_status_t mla_decode_plan(const mla_dims_t* dims, const int32_t* seq_lens_host, int32_t batch,
+                             int32_t q_len, int32_t split_tokens_hint, mla_plan_t* plan,
+                             void* workspace, size_t workspace_bytes, mla_stream_t stream);
+
+/* The host half of mla_decode_plan, for callers that copy the work list
+ * themselves (e.g. asynchronously from pinned memory): fills `plan` and
+ * writes the work-list image (plan->image_bytes bytes) to host memory.
+ * workspace: the device address the image will be copied to (recorded in
+ * the plan, never accessed).  host_image may be NULL to fill the plan only;
+ * otherwise host_image_bytes >= plan->image_bytes.  Image layout (all
+ * little-endian int32 unless noted): bytes 0-7 "MLAPLAN1", 8-15 the hash
+ * (uint64); from byte 256 the launch list, num_slots entries of four:
+ * {b | row_group << 24 (b = -1: idle slot), first row, end row, partial
+ * block (-1: the request's only chunk, written to o_lat directly)}; then,
+ * at the next multiple of 256, part_ptr [batch + 1] (the partial blocks of
+ * request b are part_ptr[b] .. part_ptr[b+1] - 1).  Launch slot s runs on
+ * XCD s % 8.  No device work. */
+mla_status_t mla_decode_plan_host(const mla_dims_t* dims, const int32_t* seq_lens_host, int32_t batch,
+                                  int32_t q_len, int32_t split_tokens_hint, const void* workspace,
+                                  mla_plan_t* plan, void* host_image, size_t host_image_bytes);
+
+/* Runs a plan.  Returns MLA_ERR_PLAN_MISMATCH if the plan was made for other
+ * dims, was planned into another workspace, or was modified.  The device
+ * seq_lens must hold the lengths planned for (kernels clamp each chunk to
+ * the device value, so a shorter length stays in bounds). */
+mla_status_t mla_decode(const mla_dims_t* dims, const mla_plan_t* plan, const void* q_lat,
+                        const float* q_scale, const void* cache, const float* cache_scale,
+                        const int32_t* block_table, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+                        void* o_lat, float* lse, mla_stream_t stream);
+
+/* Uniform split.  max_seq_len (host): upper bound of seq_lens, <=
+ * max_blocks_per_seq * block_size; device lengths are clamped to
+ * [0, max_seq_len].  split_tokens = 0 picks a length from the shapes;
+ * otherwise a positive multiple of 64 (bf16/fp8).  workspace: at least
+ * mla_decode_uniform_workspace_size() bytes. */
+size_t mla_decode_uniform_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                         int32_t max_seq_len, int32_t split_tokens);
+mla_status_t mla_decode_uniform(const mla_dims_t* dims, const void* q_lat, const float* q_scale,
+                                const void* cache, const float* cache_scale,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                int32_t num_blocks, const int32_t* seq_lens, int32_t batch,
+                                int32_t q_len, int32_t max_seq_len, int32_t split_tokens,
+                                void* workspace, size_t workspace_bytes, void* o_lat, float* lse,
+                                mla_stream_t stream);
+
+/* The chunk length mla_decode_uniform uses for split_tokens = 0 (host helper). */
 int32_t mla_decode_default_split(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                                  int32_t max_seq_len);
 
@@ -247,6 +345,26 @@ mla_status_t mla_prefill_attention(const mla_dims_t* dims, const void* q_nope, c
 size_t mla_linear_workspace_size(int32_t m, int32_t n, int32_t k);
 mla_status_t mla_linear(const void* x, int32_t ldx, const void* w, int32_t m, int32_t n, int32_t k,
                         void* y, void* workspace, size_t workspace_bytes, mla_stream_t stream);
+
+/* ------------------------------------------------------- absorbed weights
+ * Formed once when a model is loaded, not per step.  act_dtype buffers
+ * (bf16 or fp32), caller-owned device memory; fp32 accumulation.
+ *
+ * Output side [MLA explainer, value-side absorption eq.(11)]: B_i = W^O_i
+ * W^UV_i, so that u = sum_i B_i o_lat_i.
+ *   w_o [hidden_size, n_h * d_v] (W^O_i = column block i), w_uv [n_h, d_v,
+ *   d_c] -> b [hidden_size, n_h * d_c] (B_i = column block i); mla_linear
+ *   with x = o_lat viewed as [m, n_h * d_c] and w = b gives u.
+ * Query side [MLA explainer, matrix absorption eqs.(7)-(8), query-compression
+ * section]: A_i = W^UK_i^T W^UQ_i (d_c x d'_c), so that q~_i = A_i c^Q.
+ *   w_uq [n_h * d_h, d_cq] (head i's rows contiguous), w_uk [n_h, d_h, d_c]
+ *   -> a [n_h * d_c, d_cq]; mla_linear with x = c^Q and w = a gives the
+ *   latent queries [m, n_h * d_c].
+ * d_cq > 0.  Nothing is launched on an argument error. */
+mla_status_t mla_absorb_output_weights(const mla_dims_t* dims, const void* w_o, const void* w_uv,
+                                       void* b, mla_stream_t stream);
+mla_status_t mla_absorb_query_weights(const mla_dims_t* dims, int32_t d_cq, const void* w_uq,
+                                      const void* w_uk, void* a, mla_stream_t stream);
 
 /* ------------------------------------------------------------ diagnostics */
 const char* mla_status_string(mla_status_t status);

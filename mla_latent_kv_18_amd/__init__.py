@@ -18,14 +18,16 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 _DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
-          3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_HIP"}
+          3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_PLAN_MISMATCH", 5: "MLA_ERR_HIP"}
 
 # every entry point declared in include/mla.h
-EXPORTS = ("mla_cache_row_bytes", "mla_q_lat_row_bytes", "mla_append_workspace_size", "mla_append_latent",
-           "mla_absorb_workspace_size", "mla_absorb_q", "mla_decode_workspace_size",
-           "mla_decode", "mla_decode_default_split", "mla_out_proj", "mla_linear_workspace_size",
-           "mla_linear", "mla_prefill_attention", "mla_status_string", "mla_last_error_message",
-           "mla_version")
+EXPORTS = ("mla_cache_row_bytes", "mla_cache_bytes_per_token", "mla_q_lat_row_bytes",
+           "mla_append_workspace_size", "mla_append_latent", "mla_absorb_workspace_size", "mla_absorb_q",
+           "mla_decode_plan_workspace_size", "mla_decode_plan", "mla_decode_plan_host", "mla_decode",
+           "mla_decode_uniform_workspace_size", "mla_decode_uniform", "mla_decode_default_split",
+           "mla_out_proj", "mla_linear_workspace_size", "mla_linear", "mla_prefill_attention",
+           "mla_absorb_output_weights", "mla_absorb_query_weights",
+           "mla_status_string", "mla_last_error_message", "mla_version")
 
 
 class MlaError(RuntimeError):
@@ -41,6 +43,16 @@ class Dims(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("cache_dtype", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+class Plan(ctypes.Structure):
+    """mla_plan_t: filled by decode_plan, read by decode."""
+    _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_items", ctypes.c_int32),
+                ("max_splits", ctypes.c_int32), ("hash", ctypes.c_uint64), ("workspace_bytes", ctypes.c_size_t),
+                ("image_bytes", ctypes.c_size_t),
+                ("split_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32), ("num_partials", ctypes.c_int32),
+                ("seq_digest", ctypes.c_uint64), ("workspace", ctypes.c_uint64)]
 
 
 def make_dims(n_h, d_c, d_h, d_r, d_v, d_model, block_size, cache_dtype, act_dtype,
@@ -61,15 +73,23 @@ def lib():
         raise ImportError(f"libmla.so not found at {LIB_PATH}; run python -m mla_latent_kv_18_amd.build")
     L = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, DP = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.POINTER(Dims)
+    PP = ctypes.POINTER(Plan)
     sig = {
         "mla_cache_row_bytes": (SZ, [DP]),
+        "mla_cache_bytes_per_token": (SZ, [DP]),
         "mla_q_lat_row_bytes": (SZ, [DP]),
         "mla_append_workspace_size": (SZ, [DP, I32]),
         "mla_append_latent": (I32, [DP, P, P, P, P, P, I32, I64, P, P, P, SZ, P]),
         "mla_absorb_workspace_size": (SZ, [DP, I32]),
         "mla_absorb_q": (I32, [DP, P, P, P, P, I32, P, P, P, SZ, P]),
-        "mla_decode_workspace_size": (SZ, [DP, I32, I32, I32, I32]),
-        "mla_decode": (I32, [DP, P, P, P, P, P, I32, I32, P, I32, I32, I32, I32, P, SZ, P, P, P]),
+        "mla_decode_plan_workspace_size": (SZ, [DP, P, I32, I32, I32]),
+        "mla_decode_plan": (I32, [DP, P, I32, I32, I32, PP, P, SZ, P]),
+        "mla_decode_plan_host": (I32, [DP, P, I32, I32, I32, P, PP, P, SZ]),
+        "mla_decode": (I32, [DP, PP, P, P, P, P, P, I32, I32, P, P, SZ, P, P, P]),
+        "mla_decode_uniform_workspace_size": (SZ, [DP, I32, I32, I32, I32]),
+        "mla_decode_uniform": (I32, [DP, P, P, P, P, P, I32, I32, P, I32, I32, I32, I32, P, SZ, P, P, P]),
+        "mla_absorb_output_weights": (I32, [DP, P, P, P, P]),
+        "mla_absorb_query_weights": (I32, [DP, I32, P, P, P, P]),
         "mla_decode_default_split": (I32, [DP, I32, I32, I32]),
         "mla_out_proj": (I32, [DP, P, P, I32, P, P]),
         "mla_linear_workspace_size": (SZ, [I32, I32, I32]),
@@ -141,26 +161,68 @@ def absorb_q(dims, q_nope, q_pe, w_uk, positions, q_lat, q_scale=None, workspace
                               nbytes, _stream(q_lat.device)))
 
 
-def decode_workspace_size(dims, batch, q_len, max_seq_len, split_tokens=0):
-    return lib().mla_decode_workspace_size(ctypes.byref(dims), batch, q_len, max_seq_len, split_tokens)
+def _host_lens(seq_lens):
+    import numpy as np
+    if isinstance(seq_lens, torch.Tensor):
+        seq_lens = seq_lens.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+
+
+def decode_plan_workspace_size(dims, seq_lens_host, q_len, split_tokens=0):
+    lens = _host_lens(seq_lens_host)
+    return lib().mla_decode_plan_workspace_size(ctypes.byref(dims), lens.ctypes.data, len(lens), q_len,
+                                                split_tokens)
+
+
+def decode_plan(dims, seq_lens_host, q_len, device, split_tokens=0, workspace=None):
+    """mla_decode_plan: plans a decode over requests of the given host
+    lengths.  Returns (plan, workspace); pass both to decode()."""
+    lens = _host_lens(seq_lens_host)
+    need = lib().mla_decode_plan_workspace_size(ctypes.byref(dims), lens.ctypes.data, len(lens), q_len,
+                                                split_tokens)
+    if need == 0:
+        raise MlaError(1, lib().mla_last_error_message().decode())
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    plan = Plan()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode_plan(ctypes.byref(dims), lens.ctypes.data, len(lens), q_len, split_tokens,
+                                 ctypes.byref(plan), _ptr(workspace), nbytes, _stream(workspace.device)))
+    return plan, workspace
+
+
+def decode(dims, plan, workspace, q_lat, cache, block_table, seq_lens, o_lat, lse=None, q_scale=None,
+           cache_scale=None):
+    """mla_decode: runs a plan made by decode_plan over the paged latent
+    cache; writes o_lat [B*q_len, n_h, d_c] (and lse)."""
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().mla_decode(ctypes.byref(dims), ctypes.byref(plan), _ptr(q_lat), _ptr(q_scale), _ptr(cache),
+                            _ptr(cache_scale), _ptr(block_table), block_table.shape[1], cache.shape[0],
+                            _ptr(seq_lens), _ptr(workspace), nbytes, _ptr(o_lat), _ptr(lse),
+                            _stream(q_lat.device)))
+
+
+def decode_uniform_workspace_size(dims, batch, q_len, max_seq_len, split_tokens=0):
+    return lib().mla_decode_uniform_workspace_size(ctypes.byref(dims), batch, q_len, max_seq_len, split_tokens)
 
 
 def default_split(dims, batch, q_len, max_seq_len):
     return lib().mla_decode_default_split(ctypes.byref(dims), batch, q_len, max_seq_len)
 
 
-def decode(dims, q_lat, cache, block_table, seq_lens, max_seq_len, o_lat, lse=None, q_scale=None,
-           cache_scale=None, q_len=1, split_tokens=0, workspace=None):
-    """mla_decode over the paged latent cache; writes o_lat [B*q_len, n_h, d_c]."""
+def decode_uniform(dims, q_lat, cache, block_table, seq_lens, max_seq_len, o_lat, lse=None, q_scale=None,
+                   cache_scale=None, q_len=1, split_tokens=0, workspace=None):
+    """mla_decode_uniform: one chunk length for every request, sized from
+    max_seq_len; writes o_lat [B*q_len, n_h, d_c]."""
     batch = block_table.shape[0]
-    need = decode_workspace_size(dims, batch, q_len, max_seq_len, split_tokens)
+    need = decode_uniform_workspace_size(dims, batch, q_len, max_seq_len, split_tokens)
     if workspace is None:
         workspace, _ = _workspace(need, q_lat.device)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().mla_decode(ctypes.byref(dims), _ptr(q_lat), _ptr(q_scale), _ptr(cache),
-                            _ptr(cache_scale), _ptr(block_table), block_table.shape[1],
-                            cache.shape[0], _ptr(seq_lens), batch, q_len, max_seq_len, split_tokens,
-                            _ptr(workspace), nbytes, _ptr(o_lat), _ptr(lse), _stream(q_lat.device)))
+    _check(lib().mla_decode_uniform(ctypes.byref(dims), _ptr(q_lat), _ptr(q_scale), _ptr(cache),
+                                    _ptr(cache_scale), _ptr(block_table), block_table.shape[1],
+                                    cache.shape[0], _ptr(seq_lens), batch, q_len, max_seq_len, split_tokens,
+                                    _ptr(workspace), nbytes, _ptr(o_lat), _ptr(lse), _stream(q_lat.device)))
 
 
 def out_proj(dims, o_lat, w_uv, out):
@@ -218,6 +280,22 @@ def prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out, lse=None):
     _check(lib().mla_prefill_attention(ctypes.byref(dims), _ptr(q_nope), _ptr(q_pe), _ptr(k_nope),
                                        k_rope.data_ptr(), k_rope.stride(0), _ptr(v), T, _ptr(out), _ptr(lse),
                                        _stream(out.device)))
+
+
+def absorb_output_weights(dims, w_o, w_uv, b):
+    """mla_absorb_output_weights: b [d_model, n_h*d_c] with B_i = W^O_i W^UV_i."""
+    _check(lib().mla_absorb_output_weights(ctypes.byref(dims), _ptr(w_o), _ptr(w_uv), _ptr(b), _stream(b.device)))
+
+
+def absorb_query_weights(dims, w_uq, w_uk, a):
+    """mla_absorb_query_weights: a [n_h*d_c, d_cq] with A_i = W^UK_i^T W^UQ_i."""
+    d_cq = w_uq.shape[-1]
+    _check(lib().mla_absorb_query_weights(ctypes.byref(dims), d_cq, _ptr(w_uq), _ptr(w_uk), _ptr(a),
+                                          _stream(a.device)))
+
+
+def cache_bytes_per_token(dims):
+    return lib().mla_cache_bytes_per_token(ctypes.byref(dims))
 
 
 def version():

@@ -3,9 +3,13 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
+
+#include <vector>
 
 #include "../../include/mla.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace {
 
@@ -83,6 +87,64 @@ int32_t default_split(const Resolved& r, int32_t batch, int32_t q_len, int32_t m
   return static_cast<int32_t>(len);
 }
 
+mla::PlanShape plan_shape(const Resolved& r, int32_t q_len) {
+  mla::PlanShape sh;
+  if (!r.mfma) {
+    sh.row_groups = 1;
+    sh.resident_per_xcd = 32;
+    return sh;
+  }
+  const int waves = mla::decode_waves_per_group(r.n_h, q_len);
+  sh.row_groups = q_len * r.n_h / (32 * waves);
+  sh.resident_per_xcd = 32 * (4 / waves);  // one wave per SIMD: 1 or 2 workgroups per CU
+  return sh;
+}
+
+int64_t partial_bytes(const Resolved& r, int32_t q_len, int64_t num_partials) {
+  if (!r.mfma) return 0;
+  const int64_t rows = num_partials * q_len * r.n_h;
+  return rows * 512 * 2 + rows * 4;  // bf16 partial rows, fp32 lse
+}
+
+// Everything a plan stands for, except the hash itself.
+uint64_t plan_hash(const mla_dims_t* d, const mla_plan_t* p) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  h = mla::fnv1a(h, d, sizeof(*d));
+  const int32_t f[] = {p->batch, p->q_len, p->num_items, p->max_splits, p->split_tokens, p->max_seq_len,
+                       p->num_slots, p->num_partials};
+  h = mla::fnv1a(h, f, sizeof(f));
+  const uint64_t g[] = {static_cast<uint64_t>(p->workspace_bytes), static_cast<uint64_t>(p->image_bytes),
+                        p->seq_digest, p->workspace};
+  return mla::fnv1a(h, g, sizeof(g));
+}
+
+// Validates a plan request and builds it on the host.
+mla_status_t make_plan(const mla_dims_t* dims, const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
+                       int32_t hint, Resolved* r, mla::PlanResult* res, mla::PlanLayout* lay) {
+  mla_status_t st = resolve(dims, r);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || q_len <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "bad sizes (batch %d q_len %d)", batch, q_len);
+  if (batch > 0 && seq_lens_host == nullptr) return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens_host is NULL");
+  if (batch >= (1 << 24)) return fail(MLA_ERR_UNSUPPORTED, "batch must be below 2^24");
+  if (r->mfma && q_len > 2) return fail(MLA_ERR_UNSUPPORTED, "bf16/fp8 decode supports q_len <= 2");
+  if (hint < 0 || (hint > 0 && hint % 64 != 0))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "split_tokens_hint must be 0 or a positive multiple of 64");
+  for (int32_t b = 0; b < batch; ++b)
+    if (seq_lens_host[b] < 0) return fail(MLA_ERR_INVALID_ARGUMENT, "seq_lens_host[%d] = %d < 0", b, seq_lens_host[b]);
+  const mla::PlanShape sh = plan_shape(*r, q_len);
+  int32_t L = hint;
+  if (!r->mfma) {  // the fp32 kernel makes one pass per request
+    int32_t mx = 64;
+    for (int32_t b = 0; b < batch; ++b) mx = seq_lens_host[b] > mx ? seq_lens_host[b] : mx;
+    L = (mx + 63) / 64 * 64;
+  } else if (L == 0) {
+    L = mla::choose_split(seq_lens_host, batch, sh);
+  }
+  if (!mla::build_plan(seq_lens_host, batch, sh, L, res)) return fail(MLA_ERR_INVALID_ARGUMENT, "planning failed");
+  *lay = mla::plan_layout(batch, res->num_slots, partial_bytes(*r, q_len, res->num_partials));
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +154,11 @@ size_t mla_cache_row_bytes(const mla_dims_t* dims) {
   if (dims == nullptr || dims->kv_lora_rank <= 0 || dims->qk_rope_head_dim < 0) return 0;
   if (dims->cache_dtype < MLA_F32 || dims->cache_dtype > MLA_FP8_E4M3) return 0;
   return static_cast<size_t>(dims->kv_lora_rank + dims->qk_rope_head_dim) * elem_size(dims->cache_dtype);
+}
+
+size_t mla_cache_bytes_per_token(const mla_dims_t* dims) {
+  const size_t row = mla_cache_row_bytes(dims);
+  return row > 0 && dims->cache_dtype == MLA_FP8_E4M3 ? row + sizeof(float) : row;
 }
 
 size_t mla_q_lat_row_bytes(const mla_dims_t* dims) {
@@ -156,8 +223,8 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void
   return hip_status(r.mfma ? mla::launch_absorb_q_mfma(a, s) : mla::launch_absorb_q_f32(a, s), "mla_absorb_q");
 }
 
-size_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
-                                 int32_t max_seq_len, int32_t split_tokens) {
+size_t mla_decode_uniform_workspace_size(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                         int32_t max_seq_len, int32_t split_tokens) {
   Resolved r;
   if (resolve(dims, &r) != MLA_OK || batch <= 0 || q_len <= 0 || max_seq_len < 0) return 0;
   if (!r.mfma) return 0;
@@ -172,12 +239,12 @@ int32_t mla_decode_default_split(const mla_dims_t* dims, int32_t batch, int32_t 
   return default_split(r, batch, q_len, max_seq_len);
 }
 
-mla_status_t mla_decode(const mla_dims_t* dims, const void* q_lat, const float* q_scale,
-                        const void* cache, const float* cache_scale, const int32_t* block_table,
-                        int32_t max_blocks_per_seq, int32_t num_blocks, const int32_t* seq_lens,
-                        int32_t batch, int32_t q_len, int32_t max_seq_len, int32_t split_tokens,
-                        void* workspace, size_t workspace_bytes, void* o_lat, float* lse,
-                        mla_stream_t stream) {
+mla_status_t mla_decode_uniform(const mla_dims_t* dims, const void* q_lat, const float* q_scale,
+                                const void* cache, const float* cache_scale, const int32_t* block_table,
+                                int32_t max_blocks_per_seq, int32_t num_blocks, const int32_t* seq_lens,
+                                int32_t batch, int32_t q_len, int32_t max_seq_len, int32_t split_tokens,
+                                void* workspace, size_t workspace_bytes, void* o_lat, float* lse,
+                                mla_stream_t stream) {
   Resolved r;
   mla_status_t st = resolve(dims, &r);
   if (st != MLA_OK) return st;
@@ -222,6 +289,137 @@ mla_status_t mla_decode(const mla_dims_t* dims, const void* q_lat, const float* 
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
   a.workspace = workspace;
+  return hip_status(r.cache_dtype == MLA_FP8_E4M3 ? mla::launch_decode_fp8(a, s) : mla::launch_decode_mfma(a, s),
+                    "mla_decode_uniform");
+}
+
+size_t mla_decode_plan_workspace_size(const mla_dims_t* dims, const int32_t* seq_lens_host, int32_t batch,
+                                      int32_t q_len, int32_t split_tokens_hint) {
+  Resolved r;
+  mla::PlanResult res;
+  mla::PlanLayout lay;
+  if (make_plan(dims, seq_lens_host, batch, q_len, split_tokens_hint, &r, &res, &lay) != MLA_OK) return 0;
+  return lay.total;
+}
+
+mla_status_t mla_decode_plan_host(const mla_dims_t* dims, const int32_t* seq_lens_host, int32_t batch,
+                                  int32_t q_len, int32_t split_tokens_hint, const void* workspace,
+                                  mla_plan_t* plan, void* host_image, size_t host_image_bytes) {
+  if (plan == nullptr) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  Resolved r;
+  mla::PlanResult res;
+  mla::PlanLayout lay;
+  mla_status_t st = make_plan(dims, seq_lens_host, batch, q_len, split_tokens_hint, &r, &res, &lay);
+  if (st != MLA_OK) return st;
+  mla_plan_t p{};
+  p.batch = batch;
+  p.q_len = q_len;
+  p.num_items = res.num_items;
+  p.max_splits = res.max_splits;
+  p.workspace_bytes = lay.total;
+  p.image_bytes = lay.partials;
+  p.split_tokens = res.split_tokens;
+  p.max_seq_len = res.max_seq_len;
+  p.num_slots = res.num_slots;
+  p.num_partials = res.num_partials;
+  p.seq_digest = mla::fnv1a(0xcbf29ce484222325ull, seq_lens_host, sizeof(int32_t) * static_cast<size_t>(batch));
+  p.workspace = static_cast<uint64_t>(reinterpret_cast<uintptr_t>(workspace));
+  p.hash = plan_hash(dims, &p);
+  if (host_image != nullptr) {
+    if (host_image_bytes < lay.partials)
+      return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "the work-list image needs %zu bytes, got %zu", lay.partials,
+                  host_image_bytes);
+    unsigned char* img = static_cast<unsigned char*>(host_image);
+    memset(img, 0, lay.partials);
+    memcpy(img, "MLAPLAN1", 8);
+    memcpy(img + 8, &p.hash, 8);
+    if (!res.list.empty()) memcpy(img + lay.list, res.list.data(), res.list.size() * 4);
+    memcpy(img + lay.part_ptr, res.part_ptr.data(), res.part_ptr.size() * 4);
+  }
+  *plan = p;
+  g_err[0] = '\0';
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_plan(const mla_dims_t* dims, const int32_t* seq_lens_host, int32_t batch, int32_t q_len,
+                             int32_t split_tokens_hint, mla_plan_t* plan, void* workspace, size_t workspace_bytes,
+                             mla_stream_t stream) {
+  if (plan == nullptr) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  mla_plan_t p{};
+  mla_status_t st = mla_decode_plan_host(dims, seq_lens_host, batch, q_len, split_tokens_hint, workspace, &p,
+                                         nullptr, 0);
+  if (st != MLA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < p.workspace_bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode plan needs %zu workspace bytes, got %zu", p.workspace_bytes,
+                workspace_bytes);
+  std::vector<unsigned char> host(p.image_bytes);
+  st = mla_decode_plan_host(dims, seq_lens_host, batch, q_len, split_tokens_hint, workspace, &p, host.data(),
+                            host.size());
+  if (st != MLA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(workspace, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host image is freed on return
+  st = hip_status(e, "mla_decode_plan");
+  if (st == MLA_OK) *plan = p;
+  return st;
+}
+
+mla_status_t mla_decode(const mla_dims_t* dims, const mla_plan_t* plan, const void* q_lat, const float* q_scale,
+                        const void* cache, const float* cache_scale, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, int32_t num_blocks, const int32_t* seq_lens, void* workspace,
+                        size_t workspace_bytes, void* o_lat, float* lse, mla_stream_t stream) {
+  Resolved r;
+  mla_status_t st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (plan == nullptr) return fail(MLA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (plan_hash(dims, plan) != plan->hash)
+    return fail(MLA_ERR_PLAN_MISMATCH, "the plan was made for other dims or has been modified");
+  if (static_cast<uint64_t>(reinterpret_cast<uintptr_t>(workspace)) != plan->workspace)
+    return fail(MLA_ERR_PLAN_MISMATCH, "the plan's work list is in another workspace");
+  if (workspace_bytes < plan->workspace_bytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", plan->workspace_bytes,
+                workspace_bytes);
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "bad sizes (max_blocks %d num_blocks %d)", max_blocks_per_seq, num_blocks);
+  if (plan->batch == 0) return hip_status(hipSuccess, "");
+  if (static_cast<int64_t>(plan->max_seq_len) > static_cast<int64_t>(max_blocks_per_seq) * r.bs)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "planned length %d exceeds max_blocks_per_seq*block_size", plan->max_seq_len);
+  if (!q_lat || !cache || !block_table || !seq_lens || !o_lat)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (r.cache_dtype == MLA_FP8_E4M3 && (!q_scale || !cache_scale))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "fp8 decode needs q_scale and cache_scale");
+  const mla::PlanLayout lay = mla::plan_layout(plan->batch, plan->num_slots,
+                                               partial_bytes(r, plan->q_len, plan->num_partials));
+  char* ws = static_cast<char*>(workspace);
+  mla::DecodeArgs a{};
+  a.q_lat = q_lat;
+  a.q_scale = q_scale;
+  a.cache = cache;
+  a.cache_scale = cache_scale;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.seq_lens = seq_lens;
+  a.batch = plan->batch;
+  a.q_len = plan->q_len;
+  a.n_h = r.n_h;
+  a.d_c = r.d_c;
+  a.d_r = r.d_r;
+  a.block_size = r.bs;
+  a.max_seq_len = plan->max_seq_len;
+  a.scale = r.scale;
+  a.o_lat = o_lat;
+  a.lse = lse;
+  a.cache_dtype = r.cache_dtype;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!r.mfma) return hip_status(mla::launch_decode_f32(a, s), "mla_decode");
+  a.split_tokens = plan->split_tokens;
+  a.num_splits = plan->max_splits;
+  a.items = reinterpret_cast<const int32_t*>(ws + lay.list);
+  a.part_ptr = reinterpret_cast<const int32_t*>(ws + lay.part_ptr);
+  a.num_slots = plan->num_slots;
+  a.num_partials = plan->num_partials;
+  a.workspace = ws + lay.partials;
   return hip_status(r.cache_dtype == MLA_FP8_E4M3 ? mla::launch_decode_fp8(a, s) : mla::launch_decode_mfma(a, s),
                     "mla_decode");
 }
@@ -277,12 +475,44 @@ mla_status_t mla_linear(const void* x, int32_t ldx, const void* w, int32_t m, in
   return hip_status(mla::launch_linear(a, static_cast<hipStream_t>(stream)), "mla_linear");
 }
 
+mla_status_t mla_absorb_output_weights(const mla_dims_t* dims, const void* w_o, const void* w_uv, void* b,
+                                       mla_stream_t stream) {
+  Resolved r;
+  mla_status_t st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (!w_o || !w_uv || !b) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  // B_i[m, c] = sum_k W^O[m, i*d_v + k] W^UV[i, k, c]
+  mla::FoldArgs a{w_o, w_uv, b, r.n_h, r.d_model, r.d_c, r.d_v,
+                  r.d_v, static_cast<int64_t>(r.n_h) * r.d_v, 1,
+                  static_cast<int64_t>(r.d_v) * r.d_c, r.d_c, 1,
+                  r.d_c, static_cast<int64_t>(r.n_h) * r.d_c, 1};
+  return hip_status(mla::launch_fold(a, r.act_dtype == MLA_BF16, static_cast<hipStream_t>(stream)),
+                    "mla_absorb_output_weights");
+}
+
+mla_status_t mla_absorb_query_weights(const mla_dims_t* dims, int32_t d_cq, const void* w_uq, const void* w_uk,
+                                      void* a_out, mla_stream_t stream) {
+  Resolved r;
+  mla_status_t st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (d_cq <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "d_cq must be positive");
+  if (!w_uq || !w_uk || !a_out) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  // A_i[c, m] = sum_k W^UK[i, k, c] W^UQ[i*d_h + k, m]
+  mla::FoldArgs a{w_uk, w_uq, a_out, r.n_h, r.d_c, d_cq, r.d_h,
+                  static_cast<int64_t>(r.d_h) * r.d_c, 1, r.d_c,
+                  static_cast<int64_t>(r.d_h) * d_cq, d_cq, 1,
+                  static_cast<int64_t>(r.d_c) * d_cq, d_cq, 1};
+  return hip_status(mla::launch_fold(a, r.act_dtype == MLA_BF16, static_cast<hipStream_t>(stream)),
+                    "mla_absorb_query_weights");
+}
+
 const char* mla_status_string(mla_status_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_PLAN_MISMATCH: return "MLA_ERR_PLAN_MISMATCH";
     case MLA_ERR_HIP: return "MLA_ERR_HIP";
   }
   return "MLA_ERR_UNKNOWN";
@@ -290,6 +520,6 @@ const char* mla_status_string(mla_status_t status) {
 
 const char* mla_last_error_message(void) { return g_err; }
 
-int32_t mla_version(void) { return 200; }
+int32_t mla_version(void) { return 300; }
 
 }  // extern "C"

@@ -49,6 +49,7 @@
 // copies of a wave), the 16-lane b128 key reads touch 16 consecutive
 // positions, and the two 16-lane halves of a transposed value read land in
 // disjoint banks.
+#include "decode_unit.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -77,6 +78,7 @@ struct Fp8Params {
   int split_tokens, num_splits, row_groups;
   int xcd_pack;  // row groups of one chunk placed 8 workgroups apart (same XCD)
   float scale_log2;
+  const int32_t* items;  // planned launch list, or null for the uniform split
 };
 
 // buffer layout: [tile 36864 B][per-wave token scales, 256 B each]
@@ -95,25 +97,27 @@ decode_fp8_kernel(Fp8Params p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;
-  const int b = blockIdx.y;
-  int split, rg;
-  if (p.xcd_pack) {
-    const int x8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
-    rg = rest % p.row_groups;
-    split = (rest / p.row_groups) * 8 + x8;
+  DecodeUnit u;
+  if (p.items != nullptr) {
+    if (!unit_from_list(p.items, p.seq_lens, p.max_seq_len, blockIdx.x, u)) return;
   } else {
-    rg = blockIdx.x % p.row_groups;
-    split = blockIdx.x / p.row_groups;
+    int split, rgu;
+    if (p.xcd_pack) {
+      const int x8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
+      rgu = rest % p.row_groups;
+      split = (rest / p.row_groups) * 8 + x8;
+    } else {
+      rgu = blockIdx.x % p.row_groups;
+      split = blockIdx.x / p.row_groups;
+    }
+    if (split >= p.num_splits) return;
+    if (!unit_uniform(p.seq_lens, p.max_seq_len, p.split_tokens, p.num_splits, blockIdx.y, rgu, split, u))
+      return;  // empty chunk: the combine step skips it
   }
-  if (split >= p.num_splits) return;
+  const int b = u.b, rg = u.rg, T = u.T, j0 = u.j0, j1 = u.j1;
+  const bool direct = u.part < 0;
 
   const MLA_CONST int32_t* block_table = (const MLA_CONST int32_t*)(p.block_table);
-  int T = ((const MLA_CONST int32_t*)(p.seq_lens))[b];
-  T = T < 0 ? 0 : (T > p.max_seq_len ? p.max_seq_len : T);
-  const int j0 = split * p.split_tokens;
-  const bool direct = p.num_splits == 1;
-  if (!direct && j0 >= T) return;
-  const int j1 = min(j0 + p.split_tokens, T);
   const int n_tiles = j1 > j0 ? (j1 - j0 + kTileT - 1) / kTileT : 0;
 
   const int rows_per_req = p.q_len * p.n_h;
@@ -340,7 +344,7 @@ decode_fp8_kernel(Fp8Params p) {
     orow = p.o_lat + (static_cast<int64_t>(n_tok) * p.n_h + my_h) * kDc;
     lrow = p.lse != nullptr ? p.lse + static_cast<int64_t>(n_tok) * p.n_h + my_h : nullptr;
   } else {
-    const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
+    const int64_t pr = static_cast<int64_t>(u.part) * rows_per_req + my_row;
     orow = p.o_part + pr * kDc;
     lrow = p.lse_part + pr;
   }
@@ -412,25 +416,27 @@ decode_fp8_pipe_kernel(Fp8Params p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;
-  const int b = blockIdx.y;
-  int split, rg;
-  if (p.xcd_pack) {
-    const int x8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
-    rg = rest % p.row_groups;
-    split = (rest / p.row_groups) * 8 + x8;
+  DecodeUnit u;
+  if (p.items != nullptr) {
+    if (!unit_from_list(p.items, p.seq_lens, p.max_seq_len, blockIdx.x, u)) return;
   } else {
-    rg = blockIdx.x % p.row_groups;
-    split = blockIdx.x / p.row_groups;
+    int split, rgu;
+    if (p.xcd_pack) {
+      const int x8 = blockIdx.x & 7, rest = blockIdx.x >> 3;
+      rgu = rest % p.row_groups;
+      split = (rest / p.row_groups) * 8 + x8;
+    } else {
+      rgu = blockIdx.x % p.row_groups;
+      split = blockIdx.x / p.row_groups;
+    }
+    if (split >= p.num_splits) return;
+    if (!unit_uniform(p.seq_lens, p.max_seq_len, p.split_tokens, p.num_splits, blockIdx.y, rgu, split, u))
+      return;  // empty chunk: the combine step skips it
   }
-  if (split >= p.num_splits) return;
+  const int b = u.b, rg = u.rg, T = u.T, j0 = u.j0, j1 = u.j1;
+  const bool direct = u.part < 0;
 
   const MLA_CONST int32_t* block_table = (const MLA_CONST int32_t*)(p.block_table);
-  int T = ((const MLA_CONST int32_t*)(p.seq_lens))[b];
-  T = T < 0 ? 0 : (T > p.max_seq_len ? p.max_seq_len : T);
-  const int j0 = split * p.split_tokens;
-  const bool direct = p.num_splits == 1;
-  if (!direct && j0 >= T) return;
-  const int j1 = min(j0 + p.split_tokens, T);
   const int n_tiles = j1 > j0 ? (j1 - j0 + kTileT - 1) / kTileT : 0;
 
   const int rows_per_req = p.q_len * p.n_h;
@@ -637,7 +643,7 @@ decode_fp8_pipe_kernel(Fp8Params p) {
   if (direct) {
     row_base = static_cast<int64_t>(n_tok) * p.n_h + h0;
   } else {
-    row_base = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + row0;
+    row_base = static_cast<int64_t>(u.part) * rows_per_req + row0;
   }
   __bf16* obase = direct ? p.o_lat : p.o_part;
 #pragma unroll 4
@@ -659,9 +665,9 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t st) {
   p.cache_scale = a.cache_scale;
   p.block_table = a.block_table;
   p.seq_lens = a.seq_lens;
-  const size_t rows = static_cast<size_t>(a.batch) * a.num_splits * a.q_len * a.n_h;
+  const int64_t rows = partial_units(a) * a.q_len * a.n_h;
   p.o_part = static_cast<__bf16*>(a.workspace);
-  p.lse_part = a.num_splits > 1 ? reinterpret_cast<float*>(p.o_part + rows * kDc) : nullptr;
+  p.lse_part = rows > 0 ? reinterpret_cast<float*>(p.o_part + rows * kDc) : nullptr;
   p.o_lat = static_cast<__bf16*>(a.o_lat);
   p.lse = a.lse;
   p.max_blocks = a.max_blocks;
@@ -673,11 +679,13 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t st) {
   p.split_tokens = a.split_tokens;
   p.num_splits = a.num_splits;
   p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.items = a.items;
   const int waves = decode_waves_per_group(a.n_h, a.q_len);
   p.row_groups = a.q_len * a.n_h / (32 * waves);
-  p.xcd_pack = a.num_splits > 1 && p.row_groups > 1;
+  p.xcd_pack = a.items == nullptr && a.num_splits > 1 && p.row_groups > 1;
   const int grid_splits = p.xcd_pack ? (a.num_splits + 7) / 8 * 8 : a.num_splits;
-  const dim3 grid(grid_splits * p.row_groups, a.batch);
+  const dim3 grid = a.items != nullptr ? dim3(a.num_slots) : dim3(grid_splits * p.row_groups, a.batch);
+  if (a.items != nullptr && a.num_slots == 0) return hipSuccess;
   if (waves == 4 && a.q_len <= 32)
     hipLaunchKernelGGL(decode_fp8_pipe_kernel, grid, dim3(256), 0, st, p);
   else if (waves == 4)
@@ -685,7 +693,7 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((decode_fp8_kernel<2, 2>), grid, dim3(128), 0, st, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_splits == 1) return e;
+  if (e != hipSuccess || rows == 0) return e;
   return launch_combine(a, st);
 }
 

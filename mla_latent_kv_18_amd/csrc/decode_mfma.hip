@@ -27,6 +27,7 @@
 // (global_load_lds_dwordx4), NBUF tiles in flight.
 #include <type_traits>
 
+#include "decode_unit.h"
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -54,6 +55,7 @@ struct DecodeParams {
   int split_tokens, num_splits, row_groups;
   int xcd_group;  // 1: the workgroups of one request share an XCD (see xcd_slot)
   float scale_log2;
+  const int32_t* items;  // planned launch list, or null for the uniform split
 };
 
 __device__ __forceinline__ int swz(int t) {
@@ -86,18 +88,18 @@ decode_bf16_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;          // which 4-token half of each 8-token group
-  const int b = blockIdx.y;
-  const int rg = blockIdx.x % p.row_groups;
-  const int split = blockIdx.x / p.row_groups;
+  DecodeUnit u;
+  if (p.items != nullptr) {
+    if (!unit_from_list(p.items, p.seq_lens, p.max_seq_len, blockIdx.x, u)) return;
+  } else if (!unit_uniform(p.seq_lens, p.max_seq_len, p.split_tokens, p.num_splits, blockIdx.y,
+                           blockIdx.x % p.row_groups, blockIdx.x / p.row_groups, u)) {
+    return;  // empty chunk: the combine step skips it
+  }
+  const int b = u.b, rg = u.rg, T = u.T, j0 = u.j0, j1 = u.j1;
+  const bool direct = u.part < 0;
 
   // block table and lengths are read through the scalar path (uniform per workgroup)
   const MLA_CONST int32_t* block_table = (const MLA_CONST int32_t*)(p.block_table);
-  int T = ((const MLA_CONST int32_t*)(p.seq_lens))[b];
-  T = T < 0 ? 0 : (T > p.max_seq_len ? p.max_seq_len : T);
-  const int j0 = split * p.split_tokens;
-  const bool direct = p.num_splits == 1;
-  if (!direct && j0 >= T) return;  // empty chunk: the combine step skips it
-  const int j1 = min(j0 + p.split_tokens, T);
   const int n_tiles = j1 > j0 ? (j1 - j0 + kTileT - 1) / kTileT : 0;
 
   const int rows_per_req = p.q_len * p.n_h;
@@ -272,7 +274,7 @@ decode_bf16_kernel(DecodeParams p) {
       }
     if (p.lse != nullptr && hf == 0) p.lse[static_cast<int64_t>(n_tok) * p.n_h + my_h] = lse_v;
   } else {
-    const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
+    const int64_t pr = static_cast<int64_t>(u.part) * rows_per_req + my_row;
     __bf16* orow = p.o_part + pr * kDc;
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct)
@@ -360,18 +362,20 @@ decode_bf16_pipe_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;
-  int b = blockIdx.y, unit = blockIdx.x;
-  if (p.xcd_group) xcd_slot(b, unit);
-  const int rg = unit % p.row_groups;
-  const int split = unit / p.row_groups;
+  DecodeUnit u;
+  if (p.items != nullptr) {
+    if (!unit_from_list(p.items, p.seq_lens, p.max_seq_len, blockIdx.x, u)) return;
+  } else {
+    int bu = blockIdx.y, unit = blockIdx.x;
+    if (p.xcd_group) xcd_slot(bu, unit);
+    if (!unit_uniform(p.seq_lens, p.max_seq_len, p.split_tokens, p.num_splits, bu, unit % p.row_groups,
+                      unit / p.row_groups, u))
+      return;  // empty chunk: the combine step skips it
+  }
+  const int b = u.b, rg = u.rg, T = u.T, j0 = u.j0, j1 = u.j1;
+  const bool direct = u.part < 0;
 
   const MLA_CONST int32_t* block_table = (const MLA_CONST int32_t*)(p.block_table);
-  int T = ((const MLA_CONST int32_t*)(p.seq_lens))[b];
-  T = T < 0 ? 0 : (T > p.max_seq_len ? p.max_seq_len : T);
-  const int j0 = split * p.split_tokens;
-  const bool direct = p.num_splits == 1;
-  if (!direct && j0 >= T) return;  // empty chunk: the combine step skips it
-  const int j1 = min(j0 + p.split_tokens, T);
   const int n_tiles = j1 > j0 ? (j1 - j0 + kTileT - 1) / kTileT : 0;
 
   const int rows_per_req = p.q_len * p.n_h;
@@ -584,7 +588,7 @@ decode_bf16_pipe_kernel(DecodeParams p) {
   if (direct) {
     if (p.lse != nullptr && hf == 0) p.lse[static_cast<int64_t>(n_tok) * p.n_h + my_h] = lse_v;
   } else {
-    const int64_t pr = (static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + my_row;
+    const int64_t pr = static_cast<int64_t>(u.part) * rows_per_req + my_row;
     if (hf == 0) p.lse_part[pr] = lse_v;
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -618,7 +622,7 @@ decode_bf16_pipe_kernel(DecodeParams p) {
     if (direct) {
       orow = p.o_lat + (static_cast<int64_t>(b * p.q_len + row / p.n_h) * p.n_h + row % p.n_h) * kDc;
     } else {
-      orow = p.o_part + ((static_cast<int64_t>(b) * p.num_splits + split) * rows_per_req + row) * kDc;
+      orow = p.o_part + (static_cast<int64_t>(u.part) * rows_per_req + row) * kDc;
     }
     *reinterpret_cast<bf16x8_t*>(orow + 128 * wave + 8 * c) = v;
   }
@@ -637,6 +641,7 @@ template <typename OutT>
 __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ o_part,
                                                      const float* __restrict__ lse_part,
                                                      const int32_t* __restrict__ seq_lens,
+                                                     const int32_t* __restrict__ part_ptr,
                                                      int num_splits, int split_tokens, int q_len,
                                                      int n_h, int max_seq_len, OutT* __restrict__ o_lat,
                                                      float* __restrict__ lse, int xcd_group) {
@@ -644,7 +649,19 @@ __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ 
   if (xcd_group) xcd_slot(b, row);  // the XCD whose L2 took the request's partials
   const int lane = threadIdx.x;
   const int rows = q_len * n_h;
-  const int64_t base = static_cast<int64_t>(b) * num_splits * rows + row;
+  // Planned launch: the request's partial blocks are part_ptr[b] .. part_ptr[b+1]-1
+  // (none: its one chunk wrote o_lat).  Uniform split: b * num_splits + s for
+  // the chunks that start before the request's end.
+  int64_t first = static_cast<int64_t>(b) * num_splits;
+  int last = num_splits - 1, ns_planned = 0;
+  if (part_ptr != nullptr) {
+    const int p0 = part_ptr[b];
+    ns_planned = part_ptr[b + 1] - p0;
+    if (ns_planned <= 0) return;
+    first = p0;
+    last = ns_planned - 1;
+  }
+  const int64_t base = first * rows + row;
   auto lse_of = [&](int s) { return lse_part[base + static_cast<int64_t>(s) * rows]; };
   auto part_of = [&](int s) {
     return *reinterpret_cast<const bf16x8_t*>(o_part + (base + static_cast<int64_t>(s) * rows) * kDc + lane * 8);
@@ -652,13 +669,12 @@ __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ 
   // Indices are clamped rather than branched on, so that every load issues
   // before the first wait.
   int T = seq_lens[b];
-  const int last = num_splits - 1;
   const float lse_lane = lse_of(min(lane, last));
   bf16x8_t x0[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) x0[j] = part_of(min(j, last));
   T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
-  const int ns = (T + split_tokens - 1) / split_tokens;
+  const int ns = part_ptr != nullptr ? ns_planned : (T + split_tokens - 1) / split_tokens;
   const float v0 = lane < ns ? lse_lane : -INFINITY;  // splits 0..63
   float mx = v0;
   for (int s = 64 + lane; s < ns; s += 64) mx = fmaxf(mx, lse_of(s));
@@ -725,15 +741,24 @@ size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits) {
   return rows * kDc * sizeof(__bf16) + rows * sizeof(float);  // bf16 partials, fp32 lse
 }
 
+// Partial rows: bf16 [units, q_len * n_h, 512] at the start of a.workspace,
+// then fp32 lse [units, q_len * n_h]; units = planned partial blocks, or
+// batch * num_splits for the uniform split
+// (0: every request has one chunk and no combine runs).
+int64_t partial_units(const DecodeArgs& a) {
+  if (a.items != nullptr) return a.num_partials;
+  return a.num_splits > 1 ? static_cast<int64_t>(a.batch) * a.num_splits : 0;
+}
+
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   DecodeParams p;
   p.q_lat = static_cast<const __bf16*>(a.q_lat);
   p.cache = static_cast<const __bf16*>(a.cache);
   p.block_table = a.block_table;
   p.seq_lens = a.seq_lens;
-  const size_t rows = static_cast<size_t>(a.batch) * a.num_splits * a.q_len * a.n_h;
+  const int64_t rows = partial_units(a) * a.q_len * a.n_h;
   p.o_part = static_cast<__bf16*>(a.workspace);
-  p.lse_part = a.num_splits > 1 ? reinterpret_cast<float*>(p.o_part + rows * kDc) : nullptr;
+  p.lse_part = rows > 0 ? reinterpret_cast<float*>(p.o_part + rows * kDc) : nullptr;
   p.o_lat = static_cast<__bf16*>(a.o_lat);
   p.lse = a.lse;
   p.max_blocks = a.max_blocks;
@@ -745,11 +770,13 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   p.split_tokens = a.split_tokens;
   p.num_splits = a.num_splits;
   p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.items = a.items;
   const int waves = decode_waves_per_group(a.n_h, a.q_len);
   p.row_groups = a.q_len * a.n_h / (32 * waves);
   const bool pipe = waves == 4 && a.q_len <= 32;
-  p.xcd_group = pipe && a.batch % 8 == 0;
-  const dim3 grid(a.num_splits * p.row_groups, a.batch);
+  p.xcd_group = a.items == nullptr && pipe && a.batch % 8 == 0;
+  const dim3 grid = a.items != nullptr ? dim3(a.num_slots) : dim3(a.num_splits * p.row_groups, a.batch);
+  if (a.items != nullptr && a.num_slots == 0) return hipSuccess;
   if (pipe)
     hipLaunchKernelGGL(decode_bf16_pipe_kernel, grid, dim3(256), 0, st, p);
   else if (waves == 4)
@@ -757,18 +784,19 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((decode_bf16_kernel<2, 2>), grid, dim3(128), 0, st, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.num_splits == 1) return e;
+  if (e != hipSuccess || rows == 0) return e;
   return launch_combine(a, st, p.xcd_group != 0);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st, bool xcd_group) {
-  const size_t rows = static_cast<size_t>(a.batch) * a.num_splits * a.q_len * a.n_h;
+  const int64_t rows = partial_units(a) * a.q_len * a.n_h;
   const __bf16* o_part = static_cast<const __bf16*>(a.workspace);
   const float* lse_part = reinterpret_cast<const float*>(o_part + rows * kDc);
   const dim3 cgrid(a.q_len * a.n_h, a.batch);
   hipLaunchKernelGGL((combine_kernel<__bf16>), cgrid, dim3(64), 0, st, o_part, lse_part, a.seq_lens,
-                     a.num_splits, a.split_tokens, a.q_len, a.n_h, a.max_seq_len,
-                     static_cast<__bf16*>(a.o_lat), a.lse, xcd_group && a.batch % 8 == 0 ? 1 : 0);
+                     a.items != nullptr ? a.part_ptr : nullptr, a.num_splits, a.split_tokens, a.q_len,
+                     a.n_h, a.max_seq_len, static_cast<__bf16*>(a.o_lat), a.lse,
+                     xcd_group && a.batch % 8 == 0 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -46,10 +46,16 @@ struct DecodeArgs {
   int batch, q_len, n_h, d_c, d_r, block_size, max_seq_len;
   int split_tokens, num_splits;
   float scale;
-  void* workspace;
+  void* workspace;  // partials: bf16 [units, rows, 512] then fp32 lse [units, rows]
   void* o_lat;
   float* lse;
   int cache_dtype;
+  // planned launch (null items: uniform split): launch list of num_slots
+  // int32 x 4 entries and the partial blocks of request b, part_ptr[b] ..
+  // part_ptr[b + 1] - 1, out of num_partials
+  const int32_t* items;
+  const int32_t* part_ptr;
+  int num_slots, num_partials;
 };
 
 struct OutProjArgs {
@@ -67,6 +73,17 @@ struct LinearArgs {
   void* y;
   void* workspace;
 };
+
+// C_i = X_i Y_i for i < batch: C_i[r, c] = sum_k X_i[r, k] Y_i[k, c] with
+// every operand addressed through element strides (absorbed weights)
+struct FoldArgs {
+  const void* x;
+  const void* y;
+  void* out;
+  int batch, rows, cols, k;
+  int64_t xs_i, xs_r, xs_k, ys_i, ys_k, ys_c, os_i, os_r, os_c;
+};
+hipError_t launch_fold(const FoldArgs&, bool bf16, hipStream_t);
 
 // fp32, any dims
 hipError_t launch_append_f32(const AppendArgs&, hipStream_t);
@@ -110,5 +127,7 @@ hipError_t launch_linear(const LinearArgs&, hipStream_t);
 // merge of the chunk partials that a split decode left in the workspace
 // (xcd_group: the partials of request b were written on XCD b % 8, batch % 8 == 0)
 hipError_t launch_combine(const DecodeArgs&, hipStream_t, bool xcd_group = false);
+// partial row blocks the decode of `a` writes (0: no combine)
+int64_t partial_units(const DecodeArgs& a);
 
 }  // namespace mla

@@ -1,16 +1,19 @@
 """One MLA decode step on the GPU: upload a generated workload and run the
 four libmla calls (append -> absorb q -> decode -> out proj).  Plumbing
 only: torch allocates device memory and streams, libmla does every
-computation.  capture() records a whole step (or the decode call alone)
-into a HIP graph for callers that replay steps from a graph."""
+computation.  The decode is planned once from the host copy of the
+lengths (mla_decode_plan) and run with mla_decode; mode="uniform" runs
+mla_decode_uniform instead.  capture() records a whole step (or the decode
+call alone) into a HIP graph for callers that replay steps from a graph."""
 
 import ctypes
 
 import numpy as np
 import torch
 
-from . import (absorb_q, append_latent, decode, decode_workspace_size, lib, linear, linear_workspace_size,
-               make_dims, out_proj)
+from . import (absorb_output_weights, absorb_q, absorb_query_weights, append_latent, decode, decode_plan,
+               decode_uniform, decode_uniform_workspace_size, lib, linear, linear_workspace_size, make_dims,
+               out_proj)
 
 
 def _dev(a, device, fmt):
@@ -21,7 +24,7 @@ def _dev(a, device, fmt):
 
 
 class DeviceStep:
-    def __init__(self, gen, device="cuda:0", split_tokens=0):
+    def __init__(self, gen, device="cuda:0", split_tokens=0, mode="planned"):
         w = gen["workload"]
         self.w = w
         self.device = device
@@ -53,7 +56,10 @@ class DeviceStep:
         self.lse = torch.empty(N, w.n_h, dtype=torch.float32, device=device)
         self.out = torch.empty(N, w.n_h, w.d_v, dtype=out_dtype, device=device)
         self.split_tokens = split_tokens
-        nws = decode_workspace_size(self.dims, w.batch, w.q_len, self.max_seq_len, split_tokens)
+        self.mode = mode
+        self.seq_lens_host = np.asarray(gen["seq_lens"], dtype=np.int32)
+        self.plan, self.plan_ws = decode_plan(self.dims, self.seq_lens_host, w.q_len, device, split_tokens)
+        nws = decode_uniform_workspace_size(self.dims, w.batch, w.q_len, self.max_seq_len, split_tokens)
         self.decode_ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
         n_new = len(gen["new_positions"])
         self.append_ws = torch.empty(max(lib().mla_append_workspace_size(ctypes.byref(self.dims), n_new), 1),
@@ -69,15 +75,23 @@ class DeviceStep:
         absorb_q(self.dims, self.q_nope, self.q_pe, self.w_uk, self.q_pos, self.q_lat, self.q_scale,
                  workspace=self.absorb_ws)
 
-    def decode(self, split_tokens=None):
+    def decode(self, split_tokens=None, mode=None):
+        mode = self.mode if mode is None else mode
         st = self.split_tokens if split_tokens is None else split_tokens
+        if mode == "planned":
+            plan, ws = self.plan, self.plan_ws
+            if st != self.split_tokens:
+                plan, ws = decode_plan(self.dims, self.seq_lens_host, self.w.q_len, self.device, st)
+            decode(self.dims, plan, ws, self.q_lat, self.cache, self.block_table, self.seq_lens, self.o_lat,
+                   self.lse, q_scale=self.q_scale, cache_scale=self.cache_scale)
+            return
         ws = self.decode_ws
-        need = decode_workspace_size(self.dims, self.w.batch, self.w.q_len, self.max_seq_len, st)
+        need = decode_uniform_workspace_size(self.dims, self.w.batch, self.w.q_len, self.max_seq_len, st)
         if need > ws.numel():
             ws = torch.empty(need, dtype=torch.uint8, device=self.device)
-        decode(self.dims, self.q_lat, self.cache, self.block_table, self.seq_lens, self.max_seq_len,
-               self.o_lat, self.lse, q_scale=self.q_scale, cache_scale=self.cache_scale,
-               q_len=self.w.q_len, split_tokens=st, workspace=ws)
+        decode_uniform(self.dims, self.q_lat, self.cache, self.block_table, self.seq_lens, self.max_seq_len,
+                       self.o_lat, self.lse, q_scale=self.q_scale, cache_scale=self.cache_scale,
+                       q_len=self.w.q_len, split_tokens=st, workspace=ws)
 
     def out_proj(self):
         out_proj(self.dims, self.o_lat, self.w_uv, self.out)
@@ -143,16 +157,31 @@ class BlockStep(DeviceStep):
         self.o_proj()
 
     def absorbed_output_weights(self):
-        """B_i = W^O_i W^UV_i side by side [d_model, n_h * d_c], formed once
-        (as at model load) with torch in float32 and stored in bf16."""
+        """B_i = W^O_i W^UV_i side by side [d_model, n_h * d_c], formed once (as
+        at model load) by mla_absorb_output_weights."""
         w = self.w
-        b = torch.empty(w.d_model, w.n_h * w.d_c, dtype=torch.bfloat16, device=self.device)
-        for i in range(w.n_h):
-            wo_i = self.w_o[:, i * w.d_v:(i + 1) * w.d_v].float().contiguous()
-            b[:, i * w.d_c:(i + 1) * w.d_c] = (wo_i @ self.w_uv[i].float().contiguous()).bfloat16()
-        self.b = b
-        return b
+        self.b = torch.empty(w.d_model, w.n_h * w.d_c, dtype=torch.bfloat16, device=self.device)
+        absorb_output_weights(self.dims, self.w_o, self.w_uv, self.b)
+        return self.b
 
     def o_proj_absorbed(self):
         """u = sum_i B_i o_lat_i straight from the latent output."""
         linear(self.o_lat, self.b, self.u, workspace=self.linear_ws)
+
+    def absorbed_query_weights(self):
+        """A_i = W^UK_i^T W^UQ_i stacked [n_h * d_c, d'_c], formed once by
+        mla_absorb_query_weights; q_lat_absorbed() then gives the latent
+        queries from c^Q in one projection."""
+        w = self.w
+        self.a = torch.empty(w.n_h * w.d_c, self.d_cq, dtype=torch.bfloat16, device=self.device)
+        absorb_query_weights(self.dims, self.w_uq, self.w_uk, self.a)
+        N = w.batch * w.q_len
+        self.q_lat_a = torch.empty(N, w.n_h * w.d_c, dtype=torch.bfloat16, device=self.device)
+        need = linear_workspace_size(N, w.n_h * w.d_c, self.d_cq)
+        if need > self.linear_ws.numel():
+            self.linear_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self.a
+
+    def q_lat_absorbed(self):
+        """q~ [N, n_h * d_c] = A c^Q (the RoPE part still comes from W^QR)."""
+        linear(self.c_q, self.a, self.q_lat_a, workspace=self.linear_ws)

@@ -45,11 +45,19 @@ def test_sizes_and_status_strings():
     f32 = mla.make_dims(4, 32, 16, 8, 16, 64, 64, "f32", "f32")
     assert lib.mla_cache_row_bytes(ctypes.byref(f32)) == 40 * 4
     assert lib.mla_status_string(0) == b"MLA_OK"
-    assert lib.mla_version() >= 100
+    assert lib.mla_status_string(4) == b"MLA_ERR_PLAN_MISMATCH"
+    assert lib.mla_status_string(5) == b"MLA_ERR_HIP"
+    assert lib.mla_version() >= 300
+    # bytes per cached token and layer: the row, plus the fp32 scale for fp8
+    assert mla.cache_bytes_per_token(d) == 1152
+    assert mla.cache_bytes_per_token(v3_dims(cache_dtype="fp8")) == 576 + 4
+    assert mla.cache_bytes_per_token(f32) == 160
+    # x 61 layers: the V3 per-token cache of 35,136 elements (2 B each in bf16)
+    assert 61 * mla.cache_bytes_per_token(d) == 35136 * 2
     # default split: one resident wave of workgroups for the 64 x 4096 decode
     assert mla.default_split(d, 64, 1, 4096) == 1024
-    assert mla.decode_workspace_size(d, 64, 1, 4096) == 64 * 4 * 128 * (512 * 2 + 4)   # bf16 partials + fp32 lse
-    assert mla.decode_workspace_size(d, 64, 1, 256) == 0          # one chunk: no partials
+    assert mla.decode_uniform_workspace_size(d, 64, 1, 4096) == 64 * 4 * 128 * (512 * 2 + 4)   # bf16 partials + lse
+    assert mla.decode_uniform_workspace_size(d, 64, 1, 256) == 0          # one chunk: no partials
 
 
 def call_decode(d, **over):
@@ -58,10 +66,10 @@ def call_decode(d, **over):
              num_blocks=64, seq_lens=1, batch=64, q_len=1, max_seq_len=4096, split=0, ws=1,
              ws_bytes=1 << 30, o_lat=1, lse=None, stream=None)
     a.update(over)
-    return lib.mla_decode(ctypes.byref(d), a["q_lat"], a["q_scale"], a["cache"], a["cache_scale"],
-                          a["block_table"], a["max_blocks"], a["num_blocks"], a["seq_lens"], a["batch"],
-                          a["q_len"], a["max_seq_len"], a["split"], a["ws"], a["ws_bytes"], a["o_lat"],
-                          a["lse"], a["stream"])
+    return lib.mla_decode_uniform(ctypes.byref(d), a["q_lat"], a["q_scale"], a["cache"], a["cache_scale"],
+                                  a["block_table"], a["max_blocks"], a["num_blocks"], a["seq_lens"], a["batch"],
+                                  a["q_len"], a["max_seq_len"], a["split"], a["ws"], a["ws_bytes"], a["o_lat"],
+                                  a["lse"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -164,3 +172,169 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         mla.lib()
     with pytest.raises(ImportError):
         mla.linear_workspace_size(64, 128, 128)
+
+
+# ---------------------------------------------------------------------------
+# The split-KV planner (host half): coverage, no overlap, placement, balance,
+# and the plan checks mla_decode makes before any launch.
+# ---------------------------------------------------------------------------
+def plan_host(d, lens, q_len=1, hint=0, ws=0x7f0000000000):
+    import numpy as np
+    lib = mla.lib()
+    lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    plan = mla.Plan()
+    st = lib.mla_decode_plan_host(ctypes.byref(d), lens.ctypes.data, len(lens), q_len, hint, ctypes.c_void_p(ws),
+                                  ctypes.byref(plan), None, 0)
+    assert st == 0, lib.mla_last_error_message()
+    img = np.zeros(plan.image_bytes, dtype=np.uint8)
+    assert lib.mla_decode_plan_host(ctypes.byref(d), lens.ctypes.data, len(lens), q_len, hint, ctypes.c_void_p(ws),
+                                    ctypes.byref(plan), img.ctypes.data, img.nbytes) == 0
+    assert bytes(img[:8]) == b"MLAPLAN1"
+    assert int(img[8:16].view(np.uint64)[0]) == plan.hash
+    words = img.view(np.int32)
+    entries = words[64:64 + 4 * plan.num_slots].reshape(-1, 4)
+    pp_off = (256 + ((plan.num_slots * 16 + 255) // 256) * 256) // 4
+    part_ptr = words[pp_off:pp_off + len(lens) + 1]
+    return plan, entries, part_ptr
+
+
+def check_plan(d, lens, q_len, plan, entries, part_ptr, row_groups):
+    import numpy as np
+    lens = np.asarray(lens)
+    B = len(lens)
+    assert plan.batch == B and plan.q_len == q_len
+    assert plan.split_tokens % 64 == 0 and plan.split_tokens > 0
+    assert plan.num_slots % 8 == 0 and plan.num_slots == len(entries)
+    live = entries[entries[:, 0] >= 0]
+    b = live[:, 0] & 0xFFFFFF
+    rg = live[:, 0] >> 24
+    slot_xcd = (np.nonzero(entries[:, 0] >= 0)[0]) % 8
+    # every (item, row group) exactly once; the row groups of an item on one XCD
+    seen = {}
+    for (bb, r, j0, j1, part), x in zip(zip(b, rg, live[:, 1], live[:, 2], live[:, 3]), slot_xcd):
+        key = (int(bb), int(j0), int(j1), int(part))
+        assert 0 <= r < row_groups
+        seen.setdefault(key, {})
+        assert r not in seen[key], "row group launched twice"
+        seen[key][int(r)] = int(x)
+    for key, groups in seen.items():
+        assert sorted(groups) == list(range(row_groups))
+        assert len(set(groups.values())) == 1, "row groups of one chunk on different XCDs"
+    # per request: the chunks tile [0, T) without gaps or overlap (one empty chunk for T = 0)
+    assert plan.num_items == len(seen)
+    parts = []
+    for r_ in range(B):
+        chunks = sorted((j0, j1, part) for (bb, j0, j1, part) in seen if bb == r_)
+        T = int(lens[r_])
+        if T == 0:
+            assert chunks == [(0, 0, -1)]
+        else:
+            assert chunks[0][0] == 0 and chunks[-1][1] == T
+            for (a0, a1, _), (c0, c1, _) in zip(chunks, chunks[1:]):
+                assert a1 == c0
+            assert all(j1 - j0 <= plan.split_tokens and j1 > j0 for j0, j1, _ in chunks)
+        # partial blocks: none for a one-chunk request, else exactly part_ptr[b] .. part_ptr[b+1]-1
+        ps = sorted(p for _, _, p in chunks)
+        if len(chunks) == 1:
+            assert ps == [-1] and part_ptr[r_ + 1] == part_ptr[r_]
+        else:
+            assert ps == list(range(part_ptr[r_], part_ptr[r_ + 1]))
+        parts += [p for p in ps if p >= 0]
+        assert plan.max_splits >= len(chunks)
+    assert sorted(parts) == list(range(plan.num_partials))
+    assert part_ptr[0] == 0 and part_ptr[B] == plan.num_partials
+    # balance: per-XCD rows (plus a fixed per-chunk cost) within one chunk of the mean
+    load = np.zeros(8)
+    for (bb, j0, j1, part), groups in seen.items():
+        load[next(iter(groups.values()))] += (j1 - j0 + 256) * row_groups
+    assert load.max() - load.mean() <= (plan.split_tokens + 256) * row_groups + 1e-9
+    return seen
+
+
+def test_plan_v3_bs64_matches_uniform_and_groups_requests():
+    d = v3_dims()
+    lens = [4096] * 64
+    plan, entries, part_ptr = plan_host(d, lens)
+    seen = check_plan(d, lens, 1, plan, entries, part_ptr, 1)
+    assert plan.split_tokens == 1024 and plan.num_items == 256 and plan.num_slots == 256
+    # each request's four chunks run on one XCD (its queries and partials share that L2)
+    by_req = {}
+    for (bb, _, _, _), groups in seen.items():
+        by_req.setdefault(bb, set()).update(groups.values())
+    assert all(len(x) == 1 for x in by_req.values())
+    ws = plan.workspace_bytes
+    assert ws >= 256 * 128 * (512 * 2 + 4)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_plan_ragged_kimi_like(seed):
+    import numpy as np
+    d = v3_dims(n_h=64)
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1024, 131072, size=32, endpoint=True)
+    plan, entries, part_ptr = plan_host(d, lens)
+    check_plan(d, lens, 1, plan, entries, part_ptr, 1)
+    # about one resident wave (two 64-head workgroups per CU): no launch of mostly idle workgroups
+    assert plan.num_slots <= 2 * 512
+    assert (entries[:, 0] >= 0).sum() == plan.num_items
+
+
+def test_plan_fp8_two_queries_pairs_row_groups():
+    d = v3_dims(cache_dtype="fp8")
+    lens = [131072] * 4
+    plan, entries, part_ptr = plan_host(d, lens, q_len=2)
+    check_plan(d, lens, 2, plan, entries, part_ptr, 2)
+    assert plan.split_tokens == 4096 and plan.num_slots == 256
+
+
+@pytest.mark.parametrize("lens", [[0], [0, 50, 0, 1, 100, 0, 64, 65], [1, 2, 63, 64, 65, 500, 1000, 2048],
+                                  [5000] + [10] * 40, [131072], list(range(0, 3000, 97))])
+@pytest.mark.parametrize("hint", [0, 64, 256])
+def test_plan_edge_lengths(lens, hint):
+    d = v3_dims()
+    plan, entries, part_ptr = plan_host(d, lens, hint=hint)
+    check_plan(d, lens, 1, plan, entries, part_ptr, 1)
+    if hint:
+        assert plan.split_tokens == hint
+
+
+def test_plan_is_checked_before_any_launch():
+    import numpy as np
+    lib = mla.lib()
+    d = v3_dims()
+    ws = 0x7f0000000000
+    plan, _, _ = plan_host(d, [300, 5000], ws=ws)
+    P = ctypes.c_void_p
+
+    def call(dims=d, p=plan, w=ws, nbytes=None):
+        return lib.mla_decode(ctypes.byref(dims), ctypes.byref(p), P(1), None, P(1), None, P(1), 128, 256, P(1),
+                              P(w), plan.workspace_bytes if nbytes is None else nbytes, P(1), None, None)
+    assert call(dims=v3_dims(n_h=64)) == 4                     # planned for other dims
+    assert call(w=ws + 256) == 4                               # another workspace
+    assert call(nbytes=plan.workspace_bytes - 1) == 3
+    tampered = mla.Plan.from_buffer_copy(plan)
+    tampered.num_slots += 8
+    assert call(p=tampered) == 4                               # modified plan
+    assert call(dims=v3_dims(cache_dtype="fp8")) == 4
+    assert lib.mla_last_error_message()
+    # bad planning arguments
+    lens = np.array([10, -1], dtype=np.int32)
+    p2 = mla.Plan()
+    assert lib.mla_decode_plan_host(ctypes.byref(d), lens.ctypes.data, 2, 1, 0, None, ctypes.byref(p2), None, 0) == 1
+    ok = np.array([10, 20], dtype=np.int32)
+    assert lib.mla_decode_plan_host(ctypes.byref(d), ok.ctypes.data, 2, 1, 100, None, ctypes.byref(p2), None, 0) == 1
+    assert lib.mla_decode_plan_host(ctypes.byref(d), ok.ctypes.data, 2, 3, 0, None, ctypes.byref(p2), None, 0) == 2
+    small = np.zeros(16, dtype=np.uint8)
+    assert lib.mla_decode_plan_host(ctypes.byref(d), ok.ctypes.data, 2, 1, 0, None, ctypes.byref(p2),
+                                    small.ctypes.data, 16) == 3
+    assert lib.mla_decode_plan(ctypes.byref(d), ok.ctypes.data, 2, 1, 0, ctypes.byref(p2), None, 0, None) == 3
+    assert mla.decode_plan_workspace_size(d, [4096] * 64, 1) >= 256 * 128 * 1028
+
+
+def test_fold_weights_host_checks():
+    lib = mla.lib()
+    P = ctypes.c_void_p
+    d = v3_dims()
+    assert lib.mla_absorb_output_weights(ctypes.byref(d), None, P(1), P(1), None) == 1
+    assert lib.mla_absorb_query_weights(ctypes.byref(d), 0, P(1), P(1), P(1), None) == 1
+    assert lib.mla_absorb_query_weights(ctypes.byref(d), 1536, P(1), None, P(1), None) == 1

@@ -103,7 +103,39 @@ def test_attention_block_end_to_end(base, tol):
         want[sl] = ref.output_projection(o, f["w_o"])
     assert ov.rel_err(got, want) <= ov.TOL[tol]
 
-    step.absorbed_output_weights()
+    # eq.(11), absorbed: B_i = W^O_i W^UV_i formed by libmla, u = sum_i B_i o_lat_i
+    b = step.absorbed_output_weights()
     step.o_proj_absorbed()
     torch.cuda.synchronize()
-    assert ov.rel_err(_host_bf16(step.u), got) <= ov.TOL["bf16"]
+    b_ref = ref.absorbed_output_weights(f["w_o"], wuv)
+    assert ov.rel_err(_host_bf16(b), b_ref) <= 2.0 ** -8, "B_i (one bf16 rounding of an fp32 sum)"
+    o_lat = _host_bf16(step.o_lat)
+    u_abs = _host_bf16(step.u)
+    assert ov.rel_err(u_abs, ref.output_projection_absorbed(o_lat, b_ref)) <= ov.TOL["bf16"], "u from o_lat"
+    assert ov.rel_err(u_abs, want) <= ov.TOL[tol], "absorbed output end to end"
+
+
+@pytest.mark.parametrize("d_model,d_cq,n_h", [(7168, 1536, 128), (1024, 384, 64)])
+def test_query_side_absorbed_weights(d_model, d_cq, n_h):
+    """A_i = W^UK_i^T W^UQ_i formed by libmla; q~ = A c^Q through mla_linear
+    equals the oracle's latent query from c^Q, and the two-step form."""
+    w = WORKLOADS["v3_bs64_ctx4k"].scaled(name="qabs", batch=3, lens=(70, 129, 5), seed=22, n_h=n_h,
+                                           d_model=d_model)
+    gen = generate(w)
+    blk = generate_block_weights(w, d_cq=d_cq)
+    step = BlockStep(gen, blk)
+    step.query()
+    a = step.absorbed_query_weights()
+    step.q_lat_absorbed()
+    torch.cuda.synchronize()
+    f = {k: codecs.bf16_decode(v) for k, v in blk.items() if k != "d_cq"}
+    _, wuk, _, _ = ov.weights(gen)
+    a_ref = ref.absorbed_query_weights(f["w_uq"], wuk)
+    assert ov.rel_err(_host_bf16(a), a_ref) <= 2.0 ** -8, "A_i (one bf16 rounding of an fp32 sum)"
+    c_q = _host_bf16(step.c_q)
+    got = _host_bf16(step.q_lat_a).reshape(c_q.shape[0], n_h, w.d_c)
+    assert ov.rel_err(got, ref.query_latent_absorbed(c_q, a_ref, n_h)) <= ov.TOL["bf16"]
+    h64 = ov.f64(gen["h"], w.act_dtype)
+    _, q_nope, _ = ref.query_from_hidden(h64, f["w_dq"], f["w_uq"], f["w_qr"], n_h)
+    two_step = ref.absorb_q(q_nope, np.zeros(q_nope.shape[:2] + (0,)), np.zeros(q_nope.shape[0]), wuk)
+    assert ov.rel_err(got, two_step) <= ov.TOL["bf16"]

@@ -91,9 +91,9 @@ def check_request(step, gen, b, heads, tol, lse_tol):
     assert ov.rel_err(out[:, heads], want) <= tol, "end to end"
 
 
-def _run(w, split_tokens=0):
-    gen = generate(w)
-    step = DeviceStep(gen, split_tokens=split_tokens)
+def _run(w, split_tokens=0, mode="planned", gen=None):
+    gen = generate(w) if gen is None else gen
+    step = DeviceStep(gen, split_tokens=split_tokens, mode=mode)
     step.run()
     torch.cuda.synchronize()
     return gen, step
@@ -115,13 +115,21 @@ SMALL_BF16 = {
 }
 
 
+@pytest.mark.parametrize("mode", ["planned", "uniform"])
 @pytest.mark.parametrize("name", sorted(SMALL_BF16))
 @pytest.mark.parametrize("split_tokens", [0, 64, 128])
-def test_small_bf16_all_heads(name, split_tokens):
+def test_small_bf16_all_heads(name, split_tokens, mode):
     w = WORKLOADS["v3_bs64_ctx4k"].scaled(name=name, seed=7, **SMALL_BF16[name])
-    gen, step = _run(w, split_tokens)
+    gen, step = _run(w, split_tokens, mode)
     for b in range(w.batch):
         check_request(step, gen, b, list(range(w.n_h)), ov.TOL["bf16"], 2e-2)
+
+
+# Split invariance bar: two results that differ only in where the context
+# is cut each carry one bf16 rounding of o_lat (2^-9 relative), of the bf16
+# partials (2^-9) and of the bf16 softmax numerators P taken against a
+# different reference point (2^-9): 4 x 2^-9 = 2^-7 of max|o_lat|.
+INVARIANCE = 2.0 ** -7
 
 
 def test_split_and_paging_invariance_and_determinism():
@@ -131,11 +139,13 @@ def test_split_and_paging_invariance_and_determinism():
     step.decode()
     torch.cuda.synchronize()
     assert torch.equal(step.o_lat, base), "decode is not bitwise deterministic"
-    for st in (64, 256, 512):
-        step.decode(split_tokens=st)
-        torch.cuda.synchronize()
-        d = (step.o_lat.float() - base.float()).abs().max().item()
-        assert d <= 2e-2 * base.float().abs().max().item(), f"split {st} changes o_lat by {d}"
+    bound = INVARIANCE * base.float().abs().max().item()
+    for mode in ("planned", "uniform"):
+        for st in (0, 64, 256, 512):
+            step.decode(split_tokens=st, mode=mode)
+            torch.cuda.synchronize()
+            d = (step.o_lat.float() - base.float()).abs().max().item()
+            assert d <= bound, f"{mode} split {st} changes o_lat by {d}"
     # same rows under a permuted block table
     ws = w.scaled(shuffle=True)
     gen2 = generate(ws)
@@ -146,12 +156,13 @@ def test_split_and_paging_invariance_and_determinism():
     assert d <= 1e-6, f"block-table permutation changes o_lat by {d}"
 
 
+@pytest.mark.parametrize("mode", ["planned", "uniform"])
 @pytest.mark.parametrize("lens", [(0, 50), (0, 50, 0, 1, 100, 0, 64, 65)])
-def test_empty_request_gives_zero_and_neg_inf(lens):
+def test_empty_request_gives_zero_and_neg_inf(lens, mode):
     # the batch of 8 runs with each request's chunks and merge rows on one XCD
     w = WORKLOADS["v3_bs64_ctx4k"].scaled(name="empty", batch=len(lens), lens=lens, seed=9)
     for st in (0, 64):
-        gen, step = _run(w, st)
+        gen, step = _run(w, st, mode)
         for b, T in enumerate(lens):
             if T == 0:
                 assert torch.all(step.o_lat[b].float() == 0).item()
@@ -169,11 +180,12 @@ SMALL_FP8 = {
 }
 
 
+@pytest.mark.parametrize("mode", ["planned", "uniform"])
 @pytest.mark.parametrize("name", sorted(SMALL_FP8))
 @pytest.mark.parametrize("split_tokens", [0, 64, 128])
-def test_small_fp8_all_heads(name, split_tokens):
+def test_small_fp8_all_heads(name, split_tokens, mode):
     w = WORKLOADS["v3_fp8_bs4_ctx128k_q2"].scaled(name=name, seed=11, **SMALL_FP8[name])
-    gen, step = _run(w, split_tokens)
+    gen, step = _run(w, split_tokens, mode)
     for b in range(w.batch):
         check_request(step, gen, b, list(range(w.n_h)), ov.TOL["fp8"], 2e-2)
 
@@ -183,6 +195,7 @@ FULL = ["v3_bs64_ctx4k", "v3_paged_bs16_ctx32k", "kimi_k2_ragged_bs32", "v3_fp8_
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
+    """In the launch configuration bench.py times (planned decode)."""
     w = WORKLOADS[name]
     gen, step = _run(w)
     rng = np.random.default_rng(100)
@@ -218,3 +231,106 @@ def test_graph_replay_matches_eager():
     gd.replay()
     torch.cuda.synchronize()
     assert torch.equal(step.o_lat, ref[1])
+
+
+def test_planned_equals_uniform_on_full_ragged_workload():
+    """The balanced plan and the uniform split cut the Kimi-like ragged
+    context differently; both agree to the invariance bar on every row."""
+    w = WORKLOADS["kimi_k2_ragged_bs32"]
+    gen, step = _run(w)
+    planned = step.o_lat.float().clone()
+    step.decode(mode="uniform")
+    torch.cuda.synchronize()
+    d = (step.o_lat.float() - planned).abs().max().item()
+    assert d <= INVARIANCE * planned.abs().max().item()
+
+
+# ---------------------------------------------------------------------------
+# Peaked attention: keys planted after the first tile of a chunk whose score
+# exceeds that tile's maximum by more than 2^64 (and 2^128) in the exponent.
+# Every decode kernel then redoes the chunk with the exact chunk maximum as
+# its softmax reference.  Checked per call: o_lat and lse against the
+# absorbed oracle fed the GPU's latent queries and cache rows (with logits
+# this large, the rounding of q_lat itself moves the softmax weights, so the
+# end-to-end comparison is not the meaningful one here).
+# ---------------------------------------------------------------------------
+def plant_peaks(gen, plants, seed):
+    """plants: (request, position, query t, head, score) -> overwrite the
+    pre-filled row at `position` so that (query t, head) scores about
+    `score` (natural log units) against it: row = score/scale * q / |q|^2
+    plus N(0, 1) noise, with q the oracle's latent query."""
+    w = gen["workload"]
+    rng = np.random.default_rng(seed)
+    _, wuk, _, _ = ov.weights(gen)
+    q_nope = ov.f64(gen["q_nope"], w.act_dtype)
+    q_pe = ov.f64(gen["q_pe"], w.act_dtype)
+    q_lat = ref.absorb_q(q_nope, q_pe, gen["q_positions"], wuk)
+    from mla_latent_kv_18_amd.inputs import to_bf16_bits, to_fp8_rows
+    for b, pos, t, h, score in plants:
+        assert pos < int(gen["seq_lens"][b]) - w.q_len, "plant a pre-filled row"
+        q = q_lat[b * w.q_len + t, h]
+        row = score / w.softmax_scale * q / (q @ q) + rng.standard_normal(q.shape)
+        blk = gen["block_table"][b, pos // w.block_size]
+        if w.dtype == "bf16":
+            gen["pool"][blk, pos % w.block_size] = to_bf16_bits(row[None])[0]
+        else:
+            codes, sc = to_fp8_rows(row[None].astype(np.float32))
+            gen["pool"][blk, pos % w.block_size] = codes[0]
+            gen["pool_scale"][blk, pos % w.block_size] = sc[0]
+    return gen
+
+
+def check_decode_call(step, gen, b, tol, lse_tol=2e-2):
+    w = step.w
+    T = int(gen["seq_lens"][b])
+    sl = slice(b * w.q_len, (b + 1) * w.q_len)
+    rows = _gpu_rows(step, b, T)
+    if w.dtype == "fp8":
+        planes = _host(step.q_lat[sl], "fp8")
+        D = w.row_dim
+        q_lat = (planes[..., :D] + planes[..., D:] / 16.0) * \
+            step.q_scale[sl].cpu().numpy().astype(np.float64)[..., None]
+    else:
+        q_lat = _host(step.q_lat[sl], w.dtype)
+    o_ref, lse_ref = ref.decode_absorbed(q_lat, gen["q_positions"][sl], rows[:, :w.d_c], rows[:, w.d_c:],
+                                         w.softmax_scale)
+    o_lat = _host(step.o_lat[sl], w.act_dtype)
+    lse = step.lse[sl].cpu().numpy().astype(np.float64)
+    assert ov.rel_err(o_lat, o_ref) <= tol, "decode o_lat"
+    assert np.max(np.abs(lse - lse_ref)) <= lse_tol, "decode lse"
+    return float(np.max(lse_ref))
+
+
+PEAK_CASES = {   # base workload, overrides: the four decode kernels
+    "bf16_pipelined_h128": ("v3_bs64_ctx4k", dict(batch=2, lens=(400, 700))),
+    "bf16_pipelined_h128_q2": ("v3_bs64_ctx4k", dict(batch=2, lens=(400, 700), q_len=2)),
+    "bf16_plain_h64": ("v3_bs64_ctx4k", dict(n_h=64, batch=2, lens=(400, 700))),
+    "fp8_pipelined_h128_q2": ("v3_fp8_bs4_ctx128k_q2", dict(batch=2, lens=(400, 700))),
+    "fp8_plain_h64_q1": ("v3_fp8_bs4_ctx128k_q2", dict(n_h=64, batch=2, lens=(400, 700), q_len=1)),
+}
+
+
+@pytest.mark.parametrize("mode", ["planned", "uniform"])
+@pytest.mark.parametrize("split_tokens", [0, 64, 128])
+@pytest.mark.parametrize("score", [60.0, 120.0])
+@pytest.mark.parametrize("case", sorted(PEAK_CASES))
+def test_peaked_logits_take_the_second_pass(case, score, split_tokens, mode):
+    base, over = PEAK_CASES[case]
+    w = WORKLOADS[base].scaled(name="peak", seed=13, **over)
+    gen = generate(w)
+    last = w.q_len - 1
+    # position % 64 = 36 and % 128 = 100: a later tile of its chunk for 32- and
+    # 64-token tiles and chunks of 64, 128, 256 or more rows.  A few keys at
+    # nearly the same height keep the softmax from being one-hot; heads in
+    # different waves and both queries get their own peaks.
+    plants = []
+    for b in range(w.batch):
+        for k, (t, h) in enumerate([(0, 5), (last, w.n_h - 3), (0, w.n_h // 2 + 1)]):
+            p0 = 100 + 256 * k
+            if p0 + 2 < int(gen["seq_lens"][b]) - w.q_len:
+                plants += [(b, p0, t, h, score), (b, p0 + 1, t, h, score - 1.0), (b, p0 + 2, t, h, score + 0.5)]
+    plant_peaks(gen, plants, seed=14)
+    gen, step = _run(w, split_tokens, mode, gen=gen)
+    top = max(check_decode_call(step, gen, b, ov.TOL[w.dtype]) for b in range(w.batch))
+    # the planted keys dominate: far above the unit-variance logits of the rest
+    assert top > 0.9 * score

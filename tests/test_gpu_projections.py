@@ -121,3 +121,56 @@ def test_out_proj_rows(n):
     mla.out_proj(dims, o_lat, w_uv, out)
     torch.cuda.synchronize()
     assert _rel_err(_host_bf16(out), ref.out_proj(o64, wuv64)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cache_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("n", (1, 33, 100))
+def test_append_from_given_projection(n, cache_dtype):
+    """mla_append_latent with w_dkv_kr = NULL: hidden is the down-projection
+    output itself ([n, d_c + d_R] fp32); the call normalises, rotates and
+    writes it.  Checked against the oracle's append_from_projection,
+    including a padding token (slot -1) that writes nothing."""
+    rng = np.random.default_rng(4000 + n)
+    if cache_dtype == "f32":
+        d_c, d_r, n_h, d_h = 32, 8, 4, 16
+        dims = mla.make_dims(n_h, d_c, d_h, d_r, d_h, 64, 64, "f32", "f32")
+    else:
+        d_c, d_r = D_C, D_R
+        dims = mla.make_dims(N_H, D_C, D_H, D_R, D_V, 1024, 64, cache_dtype, "bf16")
+    D = d_c + d_r
+    kv64 = rng.standard_normal((n, D)).astype(np.float32).astype(np.float64)
+    kv = torch.from_numpy(kv64.astype(np.float32)).cuda()
+    gamma64 = rng.uniform(0.5, 1.5, size=d_c).astype(np.float32).astype(np.float64)
+    gamma = torch.from_numpy(gamma64.astype(np.float32)).cuda()
+    pos64 = rng.integers(0, 131072, n)
+    pos = torch.from_numpy(pos64.astype(np.int32)).cuda()
+    n_blocks = (2 * n + 63) // 64
+    slots64 = rng.permutation(n_blocks * 64)[:n]
+    if n > 1:
+        slots64[n // 2] = -1
+    slots = torch.from_numpy(slots64.astype(np.int64)).cuda()
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[cache_dtype]
+    cache = torch.zeros(n_blocks, 64, D, dtype=tdt, device="cuda")
+    scale = torch.zeros(n_blocks * 64, dtype=torch.float32, device="cuda") if cache_dtype == "fp8" else None
+    mla.append_latent(dims, kv, None, gamma, pos, slots, cache, scale)
+    torch.cuda.synchronize()
+    c_ref, kr_ref = ref.append_from_projection(kv64, gamma64, pos64, d_c, 1e-6, 10000.0)
+    want = np.concatenate([c_ref, kr_ref], axis=-1)
+    flat = cache.reshape(-1, D).cpu()
+    if cache_dtype == "fp8":
+        rows = codecs.e4m3_dequantize_rows(flat.numpy(), scale.cpu().numpy().astype(np.float64))
+    elif cache_dtype == "bf16":
+        rows = _host_bf16(flat)
+    else:
+        rows = flat.numpy().astype(np.float64)
+    keep = slots64 >= 0
+    tol = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}[cache_dtype]
+    got = rows[slots64[keep]]
+    assert _rel_err(got[:, :d_c], want[keep, :d_c]) <= tol, "latent"
+    assert _rel_err(got[:, d_c:], want[keep, d_c:]) <= tol, "rope key"
+    untouched = np.setdiff1d(np.arange(flat.shape[0]), slots64[keep])
+    assert not np.any(rows[untouched]), "rows outside the slot mapping were written"
+    if cache_dtype == "fp8":   # one scale per written row: max|row| / 448
+        sc = scale.cpu().numpy().astype(np.float64)[slots64[keep]]
+        amax = np.max(np.abs(rows[slots64[keep]]), axis=1)
+        assert np.allclose(amax, 448.0 * sc, rtol=0.07)
