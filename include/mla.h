@@ -288,6 +288,27 @@ mla_status_t mla_decode_uniform(const mla_dims_t* dims, const void* q_lat, const
                                 void* workspace, size_t workspace_bytes, void* o_lat, float* lse,
                                 mla_stream_t stream);
 
+/* For callers that cannot allocate (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation): mla_decode_uniform with
+ * its split partials in a static scratch array of the library instead of a
+ * workspace.  No allocation of any kind happens in this call.  The scratch
+ * holds MLA_NOALLOC_SCRATCH_BYTES (48 MiB) on each GPU the library runs on,
+ * from the library's load until the process ends; a decode whose
+ * mla_decode_uniform_workspace_size() exceeds it is rejected with
+ * MLA_ERR_WORKSPACE_TOO_SMALL before anything is launched.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (e.g. on two streams without ordering) race and may return wrong
+ * results.  Nothing in it needs clearing between calls (each call writes
+ * every partial it reads).  Other arguments and errors as for
+ * mla_decode_uniform. */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+mla_status_t mla_decode_uniform_noalloc(const mla_dims_t* dims, const void* q_lat, const float* q_scale,
+                                        const void* cache, const float* cache_scale,
+                                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                                        int32_t num_blocks, const int32_t* seq_lens, int32_t batch,
+                                        int32_t q_len, int32_t max_seq_len, int32_t split_tokens,
+                                        void* o_lat, float* lse, mla_stream_t stream);
+
 /* The chunk length mla_decode_uniform uses for split_tokens = 0 (host helper). */
 int32_t mla_decode_default_split(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                                  int32_t max_seq_len);

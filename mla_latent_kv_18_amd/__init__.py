@@ -24,7 +24,8 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
 EXPORTS = ("mla_cache_row_bytes", "mla_cache_bytes_per_token", "mla_q_lat_row_bytes",
            "mla_append_workspace_size", "mla_append_latent", "mla_absorb_workspace_size", "mla_absorb_q",
            "mla_decode_plan_workspace_size", "mla_decode_plan", "mla_decode_plan_host", "mla_decode",
-           "mla_decode_uniform_workspace_size", "mla_decode_uniform", "mla_decode_default_split",
+           "mla_decode_uniform_workspace_size", "mla_decode_uniform", "mla_decode_uniform_noalloc",
+           "mla_decode_default_split",
            "mla_out_proj", "mla_linear_workspace_size", "mla_linear", "mla_prefill_attention",
            "mla_absorb_output_weights", "mla_absorb_query_weights",
            "mla_status_string", "mla_last_error_message", "mla_version")
@@ -88,6 +89,7 @@ def lib():
         "mla_decode": (I32, [DP, PP, P, P, P, P, P, I32, I32, P, P, SZ, P, P, P]),
         "mla_decode_uniform_workspace_size": (SZ, [DP, I32, I32, I32, I32]),
         "mla_decode_uniform": (I32, [DP, P, P, P, P, P, I32, I32, P, I32, I32, I32, I32, P, SZ, P, P, P]),
+        "mla_decode_uniform_noalloc": (I32, [DP, P, P, P, P, P, I32, I32, P, I32, I32, I32, I32, P, P, P]),
         "mla_absorb_output_weights": (I32, [DP, P, P, P, P]),
         "mla_absorb_query_weights": (I32, [DP, I32, P, P, P, P]),
         "mla_decode_default_split": (I32, [DP, I32, I32, I32]),
@@ -280,6 +282,20 @@ def prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out, lse=None):
     _check(lib().mla_prefill_attention(ctypes.byref(dims), _ptr(q_nope), _ptr(q_pe), _ptr(k_nope),
                                        k_rope.data_ptr(), k_rope.stride(0), _ptr(v), T, _ptr(out), _ptr(lse),
                                        _stream(out.device)))
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def decode_uniform_noalloc(dims, q_lat, cache, block_table, seq_lens, max_seq_len, o_lat, lse=None,
+                           q_scale=None, cache_scale=None, q_len=1, split_tokens=0):
+    """mla_decode_uniform_noalloc: decode_uniform with the split partials in
+    the library's static scratch (no workspace, no allocation)."""
+    batch = block_table.shape[0]
+    _check(lib().mla_decode_uniform_noalloc(ctypes.byref(dims), _ptr(q_lat), _ptr(q_scale), _ptr(cache),
+                                            _ptr(cache_scale), _ptr(block_table), block_table.shape[1],
+                                            cache.shape[0], _ptr(seq_lens), batch, q_len, max_seq_len,
+                                            split_tokens, _ptr(o_lat), _ptr(lse), _stream(q_lat.device)))
 
 
 def absorb_output_weights(dims, w_o, w_uv, b):

@@ -5,15 +5,46 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/mla.h"
 #include "kernels.h"
 #include "plan.h"
 
+// Scratch of mla_decode_uniform_noalloc: the split partials of a decode,
+// for callers that cannot allocate.  One copy per GPU, held until the
+// process ends.  Host code never uses the array's name as an address (it is
+// a host-side stand-in); it uses the per-device address from
+// hipGetSymbolAddress below.
+constexpr size_t kStaticScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 mla_status_t fail(mla_status_t st, const char* fmt, ...) {
   va_list ap;
@@ -291,6 +322,30 @@ mla_status_t mla_decode_uniform(const mla_dims_t* dims, const void* q_lat, const
   a.workspace = workspace;
   return hip_status(r.cache_dtype == MLA_FP8_E4M3 ? mla::launch_decode_fp8(a, s) : mla::launch_decode_mfma(a, s),
                     "mla_decode_uniform");
+}
+
+mla_status_t mla_decode_uniform_noalloc(const mla_dims_t* dims, const void* q_lat, const float* q_scale,
+                                        const void* cache, const float* cache_scale, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, int32_t num_blocks, const int32_t* seq_lens,
+                                        int32_t batch, int32_t q_len, int32_t max_seq_len, int32_t split_tokens,
+                                        void* o_lat, float* lse, mla_stream_t stream) {
+  // the sizes first, so that an oversized call fails before any HIP call
+  Resolved r;
+  mla_status_t st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  const size_t need = mla_decode_uniform_workspace_size(dims, batch, q_len, max_seq_len, split_tokens);
+  if (need > kStaticScratchBytes)
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL,
+                "the decode needs %zu bytes of split partials; the static scratch of "
+                "mla_decode_uniform_noalloc holds %zu (use mla_decode_uniform with a workspace)",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = hip_status(static_scratch(&ws), "mla_decode_uniform_noalloc (scratch address)");
+    if (st != MLA_OK) return st;
+  }
+  return mla_decode_uniform(dims, q_lat, q_scale, cache, cache_scale, block_table, max_blocks_per_seq, num_blocks,
+                            seq_lens, batch, q_len, max_seq_len, split_tokens, ws, need, o_lat, lse, stream);
 }
 
 size_t mla_decode_plan_workspace_size(const mla_dims_t* dims, const int32_t* seq_lens_host, int32_t batch,
