@@ -9,8 +9,10 @@ request, bf16 latent cache, on one MI355X.
 
 Prints one JSON line.  `value` is latent-cache GB/s of the whole step
 (cache bytes read per step / step time, inputs resident in HBM); the
-`roofline` object covers the decode call (its algorithmic cache bytes per
-launch / its average launch time from HIP events on the launch stream);
+`roofline` object covers the decode call (its algorithmic cache bytes, or
+flops when MFMA bound, per launch / its average launch time from HIP events
+on the launch stream, with the last-level caches flushed before each
+launch; the unflushed rate is beside it as achieved_warm);
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the
 same workload.  `block` (skipped with --no-block) times the whole attention
 block around the step: the query path W^DQ, W^UQ, W^QR and the output
@@ -18,7 +20,8 @@ projection W^O through mla_linear, with W^O against its weight-read bound
 and the pages' absorbed output form (B_i = W^O_i W^UV_i) beside it.
 `prefill` (default workload; skipped with --no-prefill) times the prefill
 side on one 4096-token prompt: the key and value up-projections and the
-causal attention, which is reported against the bf16 MFMA peak.
+causal attention, which is reported against the bf16 MFMA peak, and the
+prompt's second half as a chunk continuing after its cached first half.
 """
 
 import argparse
@@ -102,11 +105,26 @@ def cpu_baseline(gen, min_seconds=10.0, max_units=64):
         if time.perf_counter() - t0 >= min_seconds:
             break
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    info = threadpool_info()
+    threads = max([p.get("num_threads", 1) for p in info] + [1])
+    blas = sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip() for p in info
+                   if p.get("user_api") == "blas"}) or ["none found"]
     what = (f"{n} of {w.batch} requests of {w.name} (all {w.n_h} heads)" if whole else
             f"{8 * n} head evaluations of request 0 of {w.name} ({T0} tokens, q_len {w.q_len})")
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "sample": f"{what}, non-absorbed float64 MLA, {dt:.1f} s"}
+            "kind": "oracle", "sample": f"{what}, non-absorbed float64 MLA, {dt:.1f} s",
+            "cpu_model": cpu_model(), "blas": ", ".join(blas)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _event_us(fn, reps=50, warmup=5):
@@ -154,6 +172,16 @@ def block_measurements(w, gen, steps, warmup):
     t_uv = _event_us(blk.out_proj)
     blk.absorbed_output_weights()
     t_b = _event_us(blk.o_proj_absorbed)
+    # query side: q~ = W^UK_i^T (W^UQ_i c^Q) in two steps, or A_i c^Q in one
+    from mla_latent_kv_18_amd import linear
+
+    def uq_then_absorb():
+        linear(blk.c_q, blk.w_uq, blk.q_nope, workspace=blk.linear_ws)
+        blk.absorb()
+    t_uq_absorb = _event_us(uq_then_absorb)
+    blk.absorbed_query_weights()
+    t_a = _event_us(blk.q_lat_absorbed)
+    del blk.a
     gbs = wo_bytes / (t_wo * 1e-6) / 1e9
     return {
         "ms_per_step": round(ms, 5),
@@ -168,6 +196,10 @@ def block_measurements(w, gen, steps, warmup):
         "out_proj_then_w_o_us": round(t_uv + t_wo, 2),
         "absorbed_b_us": round(t_b, 2),
         "absorbed_b_weight_bytes": w.d_model * w.n_h * w.d_c * elem,
+        "w_uq_then_absorb_us": round(t_uq_absorb, 2),
+        "w_uq_w_uk_weight_bytes": (w.n_h * w.d_h * blk.d_cq + w.n_h * w.d_h * w.d_c) * elem,
+        "absorbed_a_us": round(t_a, 2),
+        "absorbed_a_weight_bytes": w.n_h * w.d_c * blk.d_cq * elem,
     }
 
 
@@ -212,6 +244,21 @@ def prefill_measurements(w, seq_len=4096):
     kv_flops = 2 * T * w.d_c * n_h * (w.d_h + w.d_v)
     tf = flops / (t_attn * 1e-6) / 1e12
     peak = MFMA_PEAK_TFLOPS["bf16"]
+
+    # chunked prefill: the prompt's last `new` tokens continue after its first
+    # T - new tokens, already cached (keys: all T rows; queries: the new ones)
+    new = T // 2
+    cu_q = torch.tensor([0, new], dtype=torch.int32, device="cuda:0")
+    cu_k = torch.tensor([0, T], dtype=torch.int32, device="cuda:0")
+    out_c = torch.empty(new, n_h, w.d_v, dtype=torch.bfloat16, device="cuda:0")
+
+    def chunk():
+        mla.prefill_attention_varlen(dims, q_nope[T - new:], q_pe[T - new:], k_nope, rows[:, w.d_c:], v, cu_q, cu_k,
+                                     new, out_c)
+    t_chunk = _event_us(chunk, reps=20)
+    ctx = T - new
+    chunk_flops = sum(ctx + t + 1 for t in range(new)) * n_h * 2 * (w.d_h + w.d_r + w.d_v)
+    tfc = chunk_flops / (t_chunk * 1e-6) / 1e12
     return {
         "seq_len": T, "num_heads": n_h,
         "kv_up_projection_us": round(t_kv, 2),
@@ -220,6 +267,9 @@ def prefill_measurements(w, seq_len=4096):
         "attention": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                       "frac": round(tf / peak, 4), "flops_per_launch": flops},
         "tokens_per_s": round(T / ((t_kv + t_attn) * 1e-6), 1),
+        "chunked": {"cached_tokens": ctx, "new_tokens": new, "attention_us": round(t_chunk, 2),
+                    "achieved": round(tfc, 2), "unit": "TFLOP/s", "frac": round(tfc / peak, 4),
+                    "flops_per_launch": chunk_flops},
     }
 
 
@@ -286,11 +336,14 @@ def main():
         torch.cuda.synchronize()
     decode_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
 
-    # decode alone with the last-level caches flushed before each launch: a
-    # 1 GiB read (a write would leave dirty lines whose write-back competes)
+    # The roofline's launches: the decode call with the last-level caches
+    # flushed before each one (a 1 GiB read; a write would leave dirty lines
+    # whose write-back competes), so that no part of the latent cache is
+    # still in the 256 MB Infinity Cache.  K launches, each between its own
+    # pair of HIP events on the launch stream, averaged.
     scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
     cold = []
-    for _ in range(10):
+    for _ in range(args.steps):
         scratch.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -299,19 +352,25 @@ def main():
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
     del scratch
-    cold_ms = sorted(cold)[len(cold) // 2]
+    cold_ms = sum(cold) / len(cold)
+    cold_median_ms = sorted(cold)[len(cold) // 2]
 
-    gbs = cache_bytes / (decode_ms * 1e-3) / 1e9
-    tflops = flops / (decode_ms * 1e-3) / 1e12
+    gbs = cache_bytes / (cold_ms * 1e-3) / 1e9
+    tflops = flops / (cold_ms * 1e-3) / 1e12
+    warm_gbs = cache_bytes / (decode_ms * 1e-3) / 1e9
+    warm_tflops = flops / (decode_ms * 1e-3) / 1e12
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic() if args.workload == WORKLOAD else None,
-                "bytes_per_launch": cache_bytes}
+                "bytes_per_launch": cache_bytes,
+                "achieved_warm": round(warm_gbs, 2), "frac_warm": round(warm_gbs / HBM_PEAK_GBS, 4)}
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak, "unit": "TFLOP/s",
-                "frac": round(tflops / mfma_peak, 4), "traffic": None, "flops_per_launch": flops}
-    roof["kernel"] = "mla_decode (chunk partials + combine)"
+                "frac": round(tflops / mfma_peak, 4), "traffic": None, "flops_per_launch": flops,
+                "achieved_warm": round(warm_tflops, 2), "frac_warm": round(warm_tflops / mfma_peak, 4)}
+    roof["kernel"] = "mla_decode (chunk partials + combine), caches flushed before each launch"
+    roof["launch_us"] = round(cold_ms * 1e3, 2)
     out = {
         "metric": METRIC if args.workload == WORKLOAD else f"MLA decode latent-cache GB/s ({args.workload})",
         "value": round(cache_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -335,10 +394,13 @@ def main():
         "tokens_per_s": round(w.batch * w.q_len / (ms_step * 1e-3), 1),
         "decode_ms": round(decode_ms, 5),
         "decode_cold_ms": round(cold_ms, 5),
+        "decode_cold_median_ms": round(cold_median_ms, 5),
         "decode_gbs": round(gbs, 2),
         "decode_hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "decode_tflops": round(tflops, 2),
         "decode_mfma_frac": round(tflops / mfma_peak, 4),
+        "decode_plan": {"split_tokens": step.plan.split_tokens, "items": step.plan.num_items,
+                        "workgroups": step.plan.num_slots},
         "roofline": roof,
     }
     if not args.no_block:

@@ -342,6 +342,31 @@ mla_status_t mla_prefill_attention(const mla_dims_t* dims, const void* q_nope, c
                                    const void* v, int32_t seq_len, void* out, float* lse,
                                    mla_stream_t stream);
 
+/* Chunked and multi-sequence prefill: the same attention over a table of
+ * num_seqs sequences [MLA explainer, trade-offs section (prefill is
+ * processed without absorption); decoupled RoPE eqs.(14)-(16)].  Sequence s
+ * has keys cu_k[s] .. cu_k[s+1]-1 (rows of k_nope, v and k_rope): its cached
+ * context of ctx_s tokens followed by its new tokens, and queries cu_q[s] ..
+ * cu_q[s+1]-1 (rows of q_nope, q_pe, out, lse), the new tokens, with
+ * Tq_s = cu_q[s+1] - cu_q[s] <= Tk_s = cu_k[s+1] - cu_k[s] and ctx_s =
+ * Tk_s - Tq_s.  Query t of sequence s sits at position ctx_s + t (its RoPE
+ * angle) and attends to keys 0 .. ctx_s + t of its sequence; ctx_s = 0 is a
+ * whole prompt, ctx_s > 0 continues one after ctx_s cached tokens.
+ * cu_q, cu_k: [num_seqs + 1] int32 device arrays, non-decreasing, cu_q[0] =
+ * cu_k[0] = 0 (a sequence with Tk_s < Tq_s is computed as if ctx_s = 0 and
+ * only its first Tk_s keys existed; out-of-order offsets are the caller's
+ * error).  max_q (host): at least every Tq_s; it sizes the grid.
+ * total_q (host): cu_q[num_seqs], rows of the query-side arrays.  Keys are
+ * per head and already up-projected (k_nope = W^UK_i c, v = W^UV_i c, e.g.
+ * by mla_linear over the sequences' latent rows); k_rope rows as above.
+ * Same dims, dtypes and errors as mla_prefill_attention; num_seqs = 0 or
+ * max_q = 0 returns MLA_OK and launches nothing. */
+mla_status_t mla_prefill_attention_varlen(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
+                                          const void* k_nope, const void* k_rope, int32_t k_rope_stride,
+                                          const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                                          int32_t num_seqs, int32_t max_q, int32_t total_q, void* out,
+                                          float* lse, mla_stream_t stream);
+
 /* --------------------------------------------------------------- linear
  * The dense projections on either side of the four calls above, as one
  * skinny bf16 GEMM (fp32 accumulation):

@@ -26,7 +26,7 @@ EXPORTS = ("mla_cache_row_bytes", "mla_cache_bytes_per_token", "mla_q_lat_row_by
            "mla_decode_plan_workspace_size", "mla_decode_plan", "mla_decode_plan_host", "mla_decode",
            "mla_decode_uniform_workspace_size", "mla_decode_uniform", "mla_decode_uniform_noalloc",
            "mla_decode_default_split",
-           "mla_out_proj", "mla_linear_workspace_size", "mla_linear", "mla_prefill_attention",
+           "mla_out_proj", "mla_linear_workspace_size", "mla_linear", "mla_prefill_attention", "mla_prefill_attention_varlen",
            "mla_absorb_output_weights", "mla_absorb_query_weights",
            "mla_status_string", "mla_last_error_message", "mla_version")
 
@@ -96,6 +96,7 @@ def lib():
         "mla_out_proj": (I32, [DP, P, P, I32, P, P]),
         "mla_linear_workspace_size": (SZ, [I32, I32, I32]),
         "mla_prefill_attention": (I32, [DP, P, P, P, P, I32, P, I32, P, P, P]),
+        "mla_prefill_attention_varlen": (I32, [DP, P, P, P, P, I32, P, P, P, I32, I32, I32, P, P, P]),
         "mla_linear": (I32, [P, I32, P, I32, I32, I32, P, P, SZ, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error_message": (ctypes.c_char_p, []),
@@ -312,6 +313,29 @@ def absorb_query_weights(dims, w_uq, w_uk, a):
 
 def cache_bytes_per_token(dims):
     return lib().mla_cache_bytes_per_token(ctypes.byref(dims))
+
+
+def prefill_attention_varlen(dims, q_nope, q_pe, k_nope, k_rope, v, cu_q, cu_k, max_q, out, lse=None):
+    """mla_prefill_attention_varlen: sequences whose new tokens (queries,
+    rows cu_q[s]..cu_q[s+1]-1) follow their cached context (keys, rows
+    cu_k[s]..cu_k[s+1]-1).  cu_q, cu_k: int32 device tensors [num_seqs + 1];
+    max_q: the most queries of one sequence (host int)."""
+    n_h, d_h, d_r, d_v = dims.num_heads, dims.qk_nope_head_dim, dims.qk_rope_head_dim, dims.v_head_dim
+    S = cu_q.numel() - 1
+    Tq, Tk = q_nope.shape[0], k_nope.shape[0]
+    if cu_k.numel() != S + 1 or cu_q.dtype != torch.int32 or cu_k.dtype != torch.int32:
+        raise ValueError("prefill_attention_varlen: cu_q and cu_k must be int32 [num_seqs + 1]")
+    if k_rope.dim() != 2 or k_rope.stride(1) != 1 or k_rope.shape[0] != Tk or k_rope.shape[1] != d_r:
+        raise ValueError("prefill_attention_varlen: k_rope must be a [total keys, d_R] view with unit column stride")
+    for name, t, rows, width in (("q_nope", q_nope, Tq, d_h), ("q_pe", q_pe, Tq, d_r), ("k_nope", k_nope, Tk, d_h),
+                                 ("v", v, Tk, d_v), ("out", out, Tq, d_v)):
+        if t.shape[0] != rows or t.numel() != rows * n_h * width or t.dtype != torch.bfloat16:
+            raise ValueError(f"prefill_attention_varlen: {name} must be bf16 [{rows}, {n_h}, {width}]")
+    if lse is not None and (lse.numel() != Tq * n_h or lse.dtype != torch.float32):
+        raise ValueError("prefill_attention_varlen: lse must be float32 [total queries, n_h]")
+    _check(lib().mla_prefill_attention_varlen(ctypes.byref(dims), _ptr(q_nope), _ptr(q_pe), _ptr(k_nope),
+                                              k_rope.data_ptr(), k_rope.stride(0), _ptr(v), _ptr(cu_q), _ptr(cu_k),
+                                              S, max_q, Tq, _ptr(out), _ptr(lse), _stream(out.device)))
 
 
 def version():

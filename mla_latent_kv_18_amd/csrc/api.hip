@@ -506,8 +506,33 @@ mla_status_t mla_prefill_attention(const mla_dims_t* dims, const void* q_nope, c
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if (k_rope_stride < r.d_r || k_rope_stride % 8 != 0)
     return fail(MLA_ERR_INVALID_ARGUMENT, "k_rope_stride must be >= d_R and a multiple of 8 (got %d)", k_rope_stride);
-  mla::PrefillArgs a{q_nope, q_pe, k_nope, k_rope, k_rope_stride, v, seq_len, r.n_h, r.scale, r.theta, out, lse};
+  mla::PrefillArgs a{q_nope, q_pe, k_nope, k_rope, k_rope_stride, v, seq_len, r.n_h, r.scale, r.theta, out, lse,
+                     nullptr, nullptr, 1, seq_len};
   return hip_status(mla::launch_prefill_attention(a, static_cast<hipStream_t>(stream)), "mla_prefill_attention");
+}
+
+mla_status_t mla_prefill_attention_varlen(const mla_dims_t* dims, const void* q_nope, const void* q_pe,
+                                          const void* k_nope, const void* k_rope, int32_t k_rope_stride,
+                                          const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                                          int32_t num_seqs, int32_t max_q, int32_t total_q, void* out,
+                                          float* lse, mla_stream_t stream) {
+  Resolved r;
+  mla_status_t st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  if (!r.mfma || r.act_dtype != MLA_BF16 || r.cache_dtype != MLA_BF16)
+    return fail(MLA_ERR_UNSUPPORTED, "prefill attention needs the bf16 MFMA dims (d_h = d_v = 128, d_R = 64)");
+  if (num_seqs < 0 || max_q < 0 || total_q < 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "num_seqs, max_q and total_q must be >= 0");
+  if (num_seqs >= 65536) return fail(MLA_ERR_UNSUPPORTED, "num_seqs must be below 65536");
+  if (num_seqs == 0 || max_q == 0) return hip_status(hipSuccess, "");
+  if (!q_nope || !q_pe || !k_nope || !k_rope || !v || !out || !cu_q || !cu_k)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (k_rope_stride < r.d_r || k_rope_stride % 8 != 0)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "k_rope_stride must be >= d_R and a multiple of 8 (got %d)", k_rope_stride);
+  mla::PrefillArgs a{q_nope, q_pe, k_nope, k_rope, k_rope_stride, v, total_q, r.n_h, r.scale, r.theta, out, lse,
+                     cu_q, cu_k, num_seqs, max_q};
+  return hip_status(mla::launch_prefill_attention(a, static_cast<hipStream_t>(stream)),
+                    "mla_prefill_attention_varlen");
 }
 
 size_t mla_linear_workspace_size(int32_t m, int32_t n, int32_t k) {

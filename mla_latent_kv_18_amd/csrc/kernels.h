@@ -116,6 +116,10 @@ struct PrefillArgs {
   float scale, theta;
   void* out;
   float* lse;
+  // several sequences (null cu_q: one sequence of seq_len queries and keys)
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int num_seqs, max_q;
 };
 hipError_t launch_prefill_attention(const PrefillArgs&, hipStream_t);
 

@@ -6,7 +6,12 @@
 // eq.(16) (the score is the sum of both blocks); trade-offs section (the
 // prompt is processed without absorption)].
 //
-// One sequence of T tokens at positions 0..T-1; query t sees keys 0..t.
+// Sequences: sequence s has Tk_s keys (its cached context followed by its
+// new tokens) and Tq_s <= Tk_s new tokens, the queries; query t sits at
+// position ctx_s + t with ctx_s = Tk_s - Tq_s and sees keys 0..ctx_s + t
+// (chunked prefill continues a prompt after ctx_s cached tokens; ctx_s = 0 is
+// a whole prompt).  Queries and outputs of sequence s are rows cu_q[s] ..
+// cu_q[s+1]-1, its keys and values rows cu_k[s] .. cu_k[s+1]-1.
 //
 // Work decomposition: workgroup = (block of 256 queries, head), 8 waves; wave
 // w owns queries 32w..32w+31 of the block.  The keys and values of each
@@ -61,6 +66,9 @@ struct PrefillParams {
   float* lse;            // [T, n_h] natural log, or null
   int T, n_h, k_rope_stride;
   float scale_log2;
+  const int32_t* cu_q;   // [num_seqs + 1] query row offsets, or null: one sequence of T queries and T keys
+  const int32_t* cu_k;   // [num_seqs + 1] key row offsets
+  int max_q;             // most queries of one sequence (sizes the grid)
 };
 
 __device__ __forceinline__ bf16x8_t ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
@@ -84,23 +92,38 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
   // workgroup on XCD x takes head x + 8(n / nqb) and query block n % nqb
   // (longest first), so the query blocks of one head run together on one XCD
   // and read that head's keys and values through its L2.
-  const int nqb = (p.T + kQB - 1) / kQB;
-  const int id = blockIdx.x + gridDim.x * blockIdx.y;
+  const int nqb = (p.max_q + kQB - 1) / kQB;
+  const int id = blockIdx.x + gridDim.x * blockIdx.y;   // gridDim.y is a multiple of 8
   const int xcd = id & 7, n = id >> 3;
   const int head = xcd + 8 * (n / nqb);
   const int qb = nqb - 1 - n % nqb;
   if (head >= p.n_h) return;
+  // this workgroup's sequence: query rows q_row0 + [0, Tq), key rows k_row0 + [0, Tk)
+  int Tq = p.T, Tk = p.T, q_row0 = 0, k_row0 = 0;
+  if (p.cu_q != nullptr) {
+    const MLA_CONST int32_t* cq = (const MLA_CONST int32_t*)(p.cu_q);
+    const MLA_CONST int32_t* ck = (const MLA_CONST int32_t*)(p.cu_k);
+    q_row0 = cq[blockIdx.z];
+    Tq = cq[blockIdx.z + 1] - q_row0;
+    k_row0 = ck[blockIdx.z];
+    Tk = ck[blockIdx.z + 1] - k_row0;
+  }
+  if (qb * kQB >= Tq || Tk <= 0) return;
+  const int ctx = max(Tk - Tq, 0);                        // cached keys before the first query
   const int q0 = qb * kQB + 32 * wave;                   // this wave's first query
   const int my_q = q0 + l32;
-  const int qc = min(my_q, p.T - 1);
+  const int qc = min(my_q, Tq - 1);
+  const int vis = min(ctx + my_q, Tk - 1);               // last key this query sees
 
   // Q^T fragments: qf[s] = Q[q][16s + 8hf .. +7]; s < 8 content, s >= 8 RoPE part
   bf16x8_t qf[kPD / 16];
   {
-    const __bf16* qn = p.q_nope + (static_cast<int64_t>(qc) * p.n_h + head) * kPH + 8 * hf;
+    const int64_t qrow = q_row0 + qc;
+    const int qpos = ctx + qc;
+    const __bf16* qn = p.q_nope + (qrow * p.n_h + head) * kPH + 8 * hf;
 #pragma unroll
     for (int s = 0; s < kPH / 16; ++s) qf[s] = ld8(qn + 16 * s);
-    const __bf16* qr = p.q_pe + (static_cast<int64_t>(qc) * p.n_h + head) * kPR + 8 * hf;
+    const __bf16* qr = p.q_pe + (qrow * p.n_h + head) * kPR + 8 * hf;
     bf16x8_t x[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) x[s] = ld8(qr + 16 * s);
@@ -110,7 +133,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float cs, sn;
-        rope_cos_sin_inv(qc, rope.inv[16 * s + 8 * hf + e], &cs, &sn);
+        rope_cos_sin_inv(qpos, rope.inv[16 * s + 8 * hf + e], &cs, &sn);
         const float a = static_cast<float>(x[s][e]), b = static_cast<float>(x[s + 2][e]);
         qf[8 + s][e] = f32_to_bf16(a * cs - b * sn);
         qf[10 + s][e] = f32_to_bf16(a * sn + b * cs);
@@ -145,13 +168,13 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
       const __bf16* g;
       if (i < kKTile / 1024) {
         const int r = slot / kKC, c = (slot - r * kKC) ^ ((r >> 1) & 7);
-        const int key = min(kTK * k + r, p.T - 1);
-        g = c < 16 ? p.k_nope + (static_cast<int64_t>(key) * p.n_h + head) * kPH + 8 * c
-                   : p.k_rope + static_cast<int64_t>(key) * p.k_rope_stride + 8 * (c - 16);
+        const int64_t key = k_row0 + min(kTK * k + r, Tk - 1);
+        g = c < 16 ? p.k_nope + (key * p.n_h + head) * kPH + 8 * c
+                   : p.k_rope + key * p.k_rope_stride + 8 * (c - 16);
       } else {
         const int s2 = slot - kKTile / 16, r = s2 / kVS, c = (s2 - r * kVS) ^ (2 * (r & 3));
-        const int key = min(kTK * k + r, p.T - 1);
-        g = p.v + (static_cast<int64_t>(key) * p.n_h + head) * kPV + 8 * c;
+        const int64_t key = k_row0 + min(kTK * k + r, Tk - 1);
+        g = p.v + (key * p.n_h + head) * kPV + 8 * c;
       }
       dma16(g, tiles_addr + bi * kBuf + i * 1024);
     }
@@ -161,7 +184,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
 #pragma unroll
   for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int last_key = min(qb * kQB + kQB - 1, p.T - 1);
+  const int last_key = min(ctx + qb * kQB + kQB - 1, Tk - 1);
   const int n_tiles = last_key / kTK + 1;
 #pragma unroll
   for (int k = 0; k < kNBuf - 1; ++k)
@@ -178,7 +201,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
     MLA_LDS char* ktile = tiles + (k % kNBuf) * kBuf;
     MLA_LDS char* vtile = ktile + kKTile;
     const int key0 = kTK * k;
-    if (key0 <= q0 + 31) {  // some key of the tile is visible to this wave
+    if (key0 <= ctx + q0 + 31) {  // some key of the tile is visible to this wave
       // scores of the two 32-key sub-tiles: two independent MFMA chains
       f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
@@ -195,7 +218,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * sub + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sc[sub][r] = key <= my_q ? sc[sub][r] * p.scale_log2 : -INFINITY;
+          sc[sub][r] = key <= vis ? sc[sub][r] * p.scale_log2 : -INFINITY;
           mx = fmaxf(mx, sc[sub][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -238,8 +261,9 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
   // epilogue: normalise and store the rows of this wave's queries
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (my_q < p.T) {
-    __bf16* orow = p.out + (static_cast<int64_t>(my_q) * p.n_h + head) * kPV;
+  if (my_q < Tq) {
+    const int64_t out_row = q_row0 + my_q;
+    __bf16* orow = p.out + (out_row * p.n_h + head) * kPV;
 #pragma unroll
     for (int ct = 0; ct < kPV / 32; ++ct)
 #pragma unroll
@@ -250,7 +274,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
         *reinterpret_cast<bf16x4_t*>(orow + 32 * ct + 8 * j + 4 * hf) = o;
       }
     if (p.lse != nullptr && hf == 0)
-      p.lse[static_cast<int64_t>(my_q) * p.n_h + head] =
+      p.lse[out_row * p.n_h + head] =
           (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
@@ -270,12 +294,17 @@ hipError_t launch_prefill_attention(const PrefillArgs& a, hipStream_t st) {
   p.n_h = a.n_h;
   p.k_rope_stride = a.k_rope_stride;
   p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.max_q = a.cu_q != nullptr ? a.max_q : a.seq_len;
   RopeTable64 rope;
   for (int k = 0; k < 32; ++k) rope.inv[k] = std::pow(static_cast<double>(a.theta), -2.0 * k / kPR);
-  // n_h heads x nqb query blocks, padded to a multiple of 8 heads (the extra workgroups exit at once)
-  const int nqb = (a.seq_len + kQB - 1) / kQB;
+  // (nqb query blocks x n_h heads, padded to a multiple of 8 heads: the
+  // extra workgroups exit at once) per sequence
+  const int nqb = (p.max_q + kQB - 1) / kQB;
   const int heads8 = (a.n_h + 7) / 8 * 8;
-  hipLaunchKernelGGL(prefill_attention_kernel, dim3(nqb, heads8), dim3(64 * kWaves), 0, st, p, rope);
+  const int seqs = a.cu_q != nullptr ? a.num_seqs : 1;
+  hipLaunchKernelGGL(prefill_attention_kernel, dim3(nqb, heads8, seqs), dim3(64 * kWaves), 0, st, p, rope);
   return hipGetLastError();
 }
 

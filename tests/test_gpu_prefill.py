@@ -1,8 +1,9 @@
 """GPU parity of the prefill path: keys and values materialised per head
 from the latent cache rows by mla_linear (k^C = W^UK_i c, v = W^UV_i c),
-then mla_prefill_attention, against the float64 oracle's non-absorbed
-attention over the same rows (queries at positions 0..T-1, causal), and
-its log-sum-exp against the absorbed oracle form.
+then mla_prefill_attention (one prompt) or mla_prefill_attention_varlen
+(several sequences, each continuing after its cached context), against the
+float64 oracle's non-absorbed attention over the same rows (queries at
+their positions, causal), and the log-sum-exp against the absorbed form.
 Bar: max|err| <= 2e-2 * max|ref| for the output, |err| <= 2e-2 for lse.
 """
 
@@ -95,8 +96,110 @@ def test_prefill_full_size_sampled():
     mla.prefill_attention(dims, q_nope, q_pe, k_nope, rows[:, D_C:], v, out)
     torch.cuda.synchronize()
     got = _host_bf16(out)
-    qs = np.array([0, 1, 255, 256, 2047, 4095])
-    heads = [0, 63, 127]
+    qs = np.array([0, 1, 63, 64, 255, 256, 1000, 2047, 3333, 4095])
+    heads = [0, 17, 63, 64, 100, 127]
+    scale = 1.0 / np.sqrt(D_H + D_R)
     want = ref.attention_nonabsorbed(qn64[qs], qp64[qs], qs, rows64[:, :D_C], rows64[:, D_C:], wuk64, wuv64,
-                                     1.0 / np.sqrt(D_H + D_R), heads=heads)
+                                     scale, heads=heads)
     assert ov.rel_err(got[qs][:, heads], want) <= ov.TOL["bf16"]
+    lse = torch.empty(T, n_h, dtype=torch.float32, device="cuda")
+    mla.prefill_attention(dims, q_nope, q_pe, k_nope, rows[:, D_C:], v, out, lse)
+    torch.cuda.synchronize()
+    q_lat = ref.absorb_q(qn64[qs][:, heads], qp64[qs][:, heads], qs, wuk64[heads])
+    _, lse_ref = ref.decode_absorbed(q_lat, qs, rows64[:, :D_C], rows64[:, D_C:], scale)
+    assert np.max(np.abs(lse.cpu().numpy()[qs][:, heads] - lse_ref)) <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Chunked and multi-sequence prefill: new tokens after a cached context.
+# ---------------------------------------------------------------------------
+def _varlen_case(rng, n_h, seqs):
+    """seqs: (ctx, new) per sequence.  Latent rows of every sequence's keys
+    (context then new tokens), up-projected per head on the GPU; queries for
+    the new tokens."""
+    Tk = sum(c + n for c, n in seqs)
+    Tq = sum(n for _, n in seqs)
+    rows, rows64 = _bf16(rng, (Tk, D_C + D_R))
+    w_uk, wuk64 = _bf16(rng, (n_h, D_H, D_C), 1.0 / np.sqrt(D_C))
+    w_uv, wuv64 = _bf16(rng, (n_h, D_V, D_C), 1.0 / np.sqrt(D_C))
+    q_nope, qn64 = _bf16(rng, (Tq, n_h, D_H))
+    q_pe, qp64 = _bf16(rng, (Tq, n_h, D_R))
+    k_nope = torch.empty(Tk, n_h, D_H, dtype=torch.bfloat16, device="cuda")
+    v = torch.empty(Tk, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    mla.linear(rows[:, :D_C], w_uk.view(n_h * D_H, D_C), k_nope, ldx=D_C + D_R)
+    mla.linear(rows[:, :D_C], w_uv.view(n_h * D_V, D_C), v, ldx=D_C + D_R)
+    cu_q = np.concatenate([[0], np.cumsum([n for _, n in seqs])]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum([c + n for c, n in seqs])]).astype(np.int32)
+    return dict(rows=rows, rows64=rows64, wuk64=wuk64, wuv64=wuv64, q_nope=q_nope, qn64=qn64, q_pe=q_pe,
+                qp64=qp64, k_nope=k_nope, v=v, cu_q=cu_q, cu_k=cu_k, Tq=Tq)
+
+
+def _run_varlen(dims, c, n_h):
+    out = torch.empty(c["Tq"], n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(c["Tq"], n_h, dtype=torch.float32, device="cuda")
+    max_q = int(np.max(np.diff(c["cu_q"]))) if len(c["cu_q"]) > 1 else 0
+    mla.prefill_attention_varlen(dims, c["q_nope"], c["q_pe"], c["k_nope"], c["rows"][:, D_C:], c["v"],
+                                 torch.from_numpy(c["cu_q"]).cuda(), torch.from_numpy(c["cu_k"]).cuda(), max_q,
+                                 out, lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+VARLEN = {
+    "chunks_after_context": [(0, 300), (1000, 77), (64, 1), (257, 256), (0, 1), (100, 0), (4000, 513)],
+    "one_long_continuation": [(3000, 1100)],
+    "many_short": [(i * 37 % 300, 1 + i % 5) for i in range(40)],
+}
+
+
+@pytest.mark.parametrize("n_h", [64, 128])
+@pytest.mark.parametrize("case", sorted(VARLEN))
+def test_varlen_prefill_matches_nonabsorbed_oracle(case, n_h):
+    seqs = VARLEN[case]
+    rng = np.random.default_rng(4300 + n_h + len(seqs))
+    dims = mla.make_dims(n_h, D_C, D_H, D_R, D_V, 1024, 64, "bf16", "bf16")
+    c = _varlen_case(rng, n_h, seqs)
+    out, lse = _run_varlen(dims, c, n_h)
+    got, got_lse = _host_bf16(out), lse.cpu().numpy()
+    scale = 1.0 / np.sqrt(D_H + D_R)
+    heads = list(range(n_h)) if c["Tq"] <= 600 else [0, 5, n_h // 2, n_h - 1]
+    for s, (ctx, new) in enumerate(seqs):
+        if new == 0:
+            continue
+        q_sl = slice(c["cu_q"][s], c["cu_q"][s + 1])
+        k_sl = slice(c["cu_k"][s], c["cu_k"][s + 1])
+        rows64 = c["rows64"][k_sl]
+        pos = ctx + np.arange(new)
+        want = ref.attention_nonabsorbed(c["qn64"][q_sl], c["qp64"][q_sl], pos, rows64[:, :D_C], rows64[:, D_C:],
+                                         c["wuk64"], c["wuv64"], scale, heads=heads)
+        assert ov.rel_err(got[q_sl][:, heads], want) <= ov.TOL["bf16"], (case, s)
+        q_lat = ref.absorb_q(c["qn64"][q_sl][:, heads], c["qp64"][q_sl][:, heads], pos, c["wuk64"][heads])
+        _, lse_ref = ref.decode_absorbed(q_lat, pos, rows64[:, :D_C], rows64[:, D_C:], scale)
+        assert np.max(np.abs(got_lse[q_sl][:, heads] - lse_ref)) <= 2e-2, (case, s)
+
+
+def test_chunking_a_prompt_leaves_its_outputs_unchanged():
+    """A 900-token prompt as one sequence, and as three chunks of 300 that
+    continue after 0, 300 and 600 cached tokens: every query sees the same
+    keys in the same tile order, so the outputs are bitwise equal."""
+    rng = np.random.default_rng(4400)
+    n_h, T = 64, 900
+    dims = mla.make_dims(n_h, D_C, D_H, D_R, D_V, 1024, 64, "bf16", "bf16")
+    c = _varlen_case(rng, n_h, [(0, T)])
+    whole, whole_lse = _run_varlen(dims, c, n_h)
+    # the same queries as three sequences whose keys are the prompt's first 300, 600, 900 rows
+    parts = [(0, 300), (300, 300), (600, 300)]
+    key_rows = torch.cat([c["rows"][:ctx + new] for ctx, new in parts])
+    k_nope = torch.cat([c["k_nope"][:ctx + new] for ctx, new in parts])
+    v = torch.cat([c["v"][:ctx + new] for ctx, new in parts])
+    cu_q = torch.tensor([0, 300, 600, 900], dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0, 300, 900, 1800], dtype=torch.int32, device="cuda")
+    out = torch.empty(T, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(T, n_h, dtype=torch.float32, device="cuda")
+    mla.prefill_attention_varlen(dims, c["q_nope"], c["q_pe"], k_nope, key_rows[:, D_C:], v, cu_q, cu_k, 300,
+                                 out, lse)
+    single = torch.empty_like(out)
+    mla.prefill_attention(dims, c["q_nope"], c["q_pe"], c["k_nope"], c["rows"][:, D_C:], c["v"], single)
+    torch.cuda.synchronize()
+    assert torch.equal(out, whole) and torch.equal(lse, whole_lse)
+    assert torch.equal(single, whole)
