@@ -85,3 +85,70 @@ def test_per_row_fp8_quantisation():
     big = np.abs(x) > 2.0 ** -6 * scales[:, None] * 2
     rel = np.abs(back - x)[big] / np.abs(x)[big]
     assert rel.max() <= 2.0 ** -4 + 1e-6
+
+
+# OCP MX v1.0, FP4 E2M1 element encodings (positive half; bit 3 is the sign)
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_all_codes_matches_the_format_table():
+    ours = codecs.e2m1_decode(np.arange(16))
+    assert list(ours[:8]) == E2M1_TABLE
+    assert list(-ours[8:]) == E2M1_TABLE and np.signbit(ours[8])   # code 8 is -0
+
+
+def test_e2m1_encode_round_trips_and_rounds_to_even():
+    codes = np.arange(16)
+    assert np.array_equal(codecs.e2m1_encode(codecs.e2m1_decode(codes)), codes)
+    # midpoints between neighbours go to the code with an even mantissa bit
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for x, want in ties.items():
+        assert codecs.e2m1_round(x) == want and codecs.e2m1_round(-x) == -want
+    assert codecs.e2m1_round(0.26) == 0.5 and codecs.e2m1_round(5.01) == 6.0
+    assert codecs.e2m1_round(7.0) == 6.0 and codecs.e2m1_round(1e30) == 6.0      # saturation
+    # brute force: every value goes to a nearest representable value
+    x = np.linspace(-8, 8, 20001)
+    r = codecs.e2m1_round(x)
+    grid = np.array(sorted(set(E2M1_TABLE + [-v for v in E2M1_TABLE])))
+    best = np.min(np.abs(np.clip(x, -6, 6)[:, None] - grid[None, :]), axis=1)
+    assert np.allclose(np.abs(np.clip(x, -6, 6) - r), best, atol=1e-12)
+
+
+def test_e8m0_decode_matches_torch():
+    b = np.arange(256, dtype=np.uint8)
+    ours = codecs.e8m0_decode(b)
+    theirs = torch.from_numpy(b).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    same = (ours == theirs) | (np.isnan(ours) & np.isnan(theirs))
+    assert same.all()
+
+
+def test_mx_fp4_block_scale_rule_and_error_bound():
+    rng = np.random.default_rng(7)
+    x = rng.normal(size=(64, 576)) * rng.uniform(0.01, 100, size=(64, 1))
+    x[3] = 0.0                                                   # an all-zero row
+    x[5, :32] = 0.0                                              # an all-zero block
+    codes, sb = codecs.mx_fp4_quantize_rows(x)
+    assert codes.shape == x.shape and sb.shape == (64, 18)
+    blocks = np.abs(x).reshape(64, 18, 32)
+    amax = blocks.max(axis=-1)
+    scale = codecs.e8m0_decode(sb)
+    nz = amax > 0
+    # the largest element of a block lands in [4, 8) before saturating at 6
+    assert np.all((amax[nz] / scale[nz] >= 4) & (amax[nz] / scale[nz] < 8))
+    assert np.all(sb[~nz] == 127)
+    y = codecs.mx_fp4_dequantize_rows(codes, sb)
+    # error: half a grid step (at most 2 x 2^-2 of the block scale, i.e. 1 scale unit)
+    # below the saturation point, and at most 2 scale units above it (8 -> 6)
+    err = np.abs(y - x).reshape(64, 18, 32)
+    assert np.all(err <= 2.0 * scale[..., None] + 1e-300)
+    assert np.all(y[3] == 0) and np.all(y[5, :32] == 0)
+    # values exactly on the grid survive
+    grid_vals = codecs.mx_fp4_dequantize_rows(codes, sb)
+    c2, s2 = codecs.mx_fp4_quantize_rows(grid_vals)
+    assert np.array_equal(codecs.mx_fp4_dequantize_rows(c2, s2), grid_vals)
+
+
+def test_unpack_nibbles_order():
+    packed = np.array([[0x21, 0x43, 0xF5]], dtype=np.uint8)
+    assert codecs.unpack_nibbles(packed, 6).tolist() == [[1, 2, 3, 4, 5, 15]]
+    assert codecs.unpack_nibbles(packed, 5).tolist() == [[1, 2, 3, 4, 5]]
