@@ -87,7 +87,7 @@ def cpu_baseline(gen, min_seconds=10.0, max_units=64):
     from tests import oracle_views as ov
 
     w = gen["workload"]
-    row_bytes = w.row_dim * (1 if w.dtype == "fp8" else 2) + (4 if w.dtype == "fp8" else 0)
+    row_bytes = w.row_bytes + (4 if w.dtype in ("fp8", "fp8kr") else 0)
     T0 = int(gen["seq_lens"][0])
     whole = T0 * w.q_len * w.n_h <= 4096 * 128
     t0 = time.perf_counter()
@@ -302,11 +302,14 @@ def main():
     step = DeviceStep(gen, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    elem = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
     n_rows = int(gen["seq_lens"].sum())
-    cache_bytes = n_rows * (w.row_dim * elem + (4 if w.dtype == "fp8" else 0))   # rows (+ fp8 scales) read
+    scaled = w.dtype in ("fp8", "fp8kr")
+    cache_bytes = n_rows * (w.row_bytes + (4 if scaled else 0))               # stored rows (+ fp8 scales) read
     flops = n_rows * w.q_len * 2 * w.n_h * (w.row_dim + w.d_c)                 # scores + weighted sum
-    mfma_peak = MFMA_PEAK_TFLOPS[w.dtype]
+    # the MFMA type the decode computes in: fp8 for the fp8 cache, bf16 for the
+    # others (the FP4 and fp8-latent variants are expanded to bf16 in LDS)
+    mfma_type = {"fp8": "fp8", "f32": "f32"}.get(w.dtype, "bf16")
+    mfma_peak = MFMA_PEAK_TFLOPS[mfma_type]
     bound = "mfma" if flops / (mfma_peak * 1e12) > cache_bytes / (HBM_PEAK_GBS * 1e9) else "hbm"
 
     for _ in range(args.warmup):
@@ -382,7 +385,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": w.dtype if w.dtype in ("f32", "bf16", "fp8") else f"{w.dtype} cache, {mfma_type} MFMA",
         "data": "synthetic (seeded N(0,1) latent rows, N(0,1)/sqrt(fan_in) weights)",
         "config": {"workload": args.workload, "num_heads": w.n_h, "kv_lora_rank": w.d_c,
                    "qk_rope_head_dim": w.d_r, "qk_nope_head_dim": w.d_h, "v_head_dim": w.d_v,

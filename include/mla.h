@@ -56,6 +56,14 @@
  *                           block_size a multiple of 64 (MFMA kernels)
  *       MLA_FP8_E4M3 / MLA_BF16  same dims as bf16; the cache stores OCP
  *                           e4m3 codes with one fp32 scale per row (token)
+ *     Cache variants [MLA wiki note, open questions (FP8 / FP4 caches) and
+ *     adopting models (Kimi Linear: MLA without the RoPE part)]:
+ *       MLA_FP4_E2M1 / MLA_BF16          MX FP4 rows (see mla_dtype_t); the
+ *                           latent query is bf16 as for a bf16 cache
+ *       MLA_FP8_E4M3_KR_BF16 / MLA_BF16  e4m3 latent with a per-row scale,
+ *                           RoPE key kept in bf16; bf16 latent query
+ *       MLA_BF16 / MLA_BF16 with qk_rope_head_dim = 0 (NoPE): 512-wide rows,
+ *                           no RoPE key, latent query of d_c
  *     Anything else returns MLA_ERR_UNSUPPORTED.
  */
 #ifndef LIBMLA_MLA_H
@@ -78,7 +86,19 @@ typedef enum {
   MLA_ERR_HIP = 5
 } mla_status_t;
 
-typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype_t;
+typedef enum {
+  MLA_F32 = 0,
+  MLA_BF16 = 1,
+  MLA_FP8_E4M3 = 2,
+  /* cache only: MX FP4 rows, (d_c + d_R) E2M1 codes, two per byte
+   * (element 2i in the low nibble), then one E8M0 scale byte per 32
+   * elements (value 2^(b - 127)), then zero padding to a multiple of 16
+   * bytes (320 B for d_c + d_R = 576) */
+  MLA_FP4_E2M1 = 3,
+  /* cache only: d_c e4m3 latent codes with one fp32 scale per row in
+   * cache_scale, then the d_R RoPE-key values in bf16 (640 B for 512 + 64) */
+  MLA_FP8_E4M3_KR_BF16 = 4
+} mla_dtype_t;
 
 /* A hipStream_t (kept opaque so the header needs no HIP include). */
 typedef void* mla_stream_t;
@@ -102,14 +122,16 @@ typedef struct {
   float rms_eps;             /* <= 0 selects 1e-6 */
 } mla_dims_t;
 
-/* Bytes of one cache row: (d_c + d_R) * element size.  fp8 caches keep the
- * per-row fp32 scale in a separate [num_blocks, block_size] array.
+/* Bytes of one stored cache row: (d_c + d_R) * element size for fp32, bf16
+ * and fp8; the formats of mla_dtype_t for MLA_FP4_E2M1 and
+ * MLA_FP8_E4M3_KR_BF16.  fp8 latents keep the per-row fp32 scale in a
+ * separate [num_blocks, block_size] array.
  * Returns 0 for invalid dims.  [MLA explainer, cache comparison section;
  * variants, MLA section: per-token elements = d_c + d_R per layer.] */
 size_t mla_cache_row_bytes(const mla_dims_t* dims);
 
-/* HBM bytes one cached token occupies in one layer: the row plus, for fp8,
- * its fp32 scale ((d_c + d_R) * element size, + 4 for fp8).  Returns 0 for
+/* HBM bytes one cached token occupies in one layer: the row plus, for an fp8
+ * latent, its fp32 scale (mla_cache_row_bytes, + 4 for fp8).  Returns 0 for
  * invalid dims.  [MLA explainer, cache comparison section: per-token cache
  * of d_c + d_R elements per layer; variants, MLA section.] */
 size_t mla_cache_bytes_per_token(const mla_dims_t* dims);

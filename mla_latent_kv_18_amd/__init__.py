@@ -14,8 +14,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmla.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
-_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+F32, BF16, FP8_E4M3, FP4_E2M1, FP8_E4M3_KR_BF16 = 0, 1, 2, 3, 4
+_DTYPE_CODE = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp4": FP4_E2M1, "fp8kr": FP8_E4M3_KR_BF16}
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
           3: "MLA_ERR_WORKSPACE_TOO_SMALL", 4: "MLA_ERR_PLAN_MISMATCH", 5: "MLA_ERR_HIP"}

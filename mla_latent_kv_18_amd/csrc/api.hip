@@ -70,6 +70,29 @@ struct Resolved {
 
 int elem_size(int dt) { return dt == MLA_F32 ? 4 : (dt == MLA_BF16 ? 2 : 1); }
 
+// Stored bytes of one cache row of D = d_c + d_R elements.
+size_t row_bytes(int dt, int d_c, int d_r) {
+  const size_t D = static_cast<size_t>(d_c) + d_r;
+  switch (dt) {
+    case MLA_F32: return 4 * D;
+    case MLA_BF16: return 2 * D;
+    case MLA_FP8_E4M3: return D;
+    case MLA_FP4_E2M1: return (D / 2 + D / 32 + 15) / 16 * 16;  // codes, E8M0 scales, padding
+    case MLA_FP8_E4M3_KR_BF16: return static_cast<size_t>(d_c) + 2 * static_cast<size_t>(d_r);
+  }
+  return 0;
+}
+
+// Decode kernels for the cache format.
+hipError_t launch_decode_for(const Resolved& r, const mla::DecodeArgs& a, hipStream_t s) {
+  switch (r.cache_dtype) {
+    case MLA_FP8_E4M3: return mla::launch_decode_fp8(a, s);
+    case MLA_FP4_E2M1: return mla::launch_decode_dq(a, mla::kDqFp4Mx, s);
+    case MLA_FP8_E4M3_KR_BF16: return mla::launch_decode_dq(a, mla::kDqFp8Kr, s);
+  }
+  return r.d_r == 0 ? mla::launch_decode_dq(a, mla::kDqBf16Nope, s) : mla::launch_decode_mfma(a, s);
+}
+
 mla_status_t resolve(const mla_dims_t* d, Resolved* r) {
   if (d == nullptr) return fail(MLA_ERR_INVALID_ARGUMENT, "dims is NULL");
   r->n_h = d->num_heads;
@@ -91,9 +114,14 @@ mla_status_t resolve(const mla_dims_t* d, Resolved* r) {
     r->mfma = false;
     return MLA_OK;
   }
-  if ((r->cache_dtype == MLA_BF16 || r->cache_dtype == MLA_FP8_E4M3) && r->act_dtype == MLA_BF16) {
-    if (r->d_c != 512 || r->d_r != 64 || r->d_h != 128 || r->d_v != 128)
-      return fail(MLA_ERR_UNSUPPORTED, "bf16/fp8 kernels need d_c=512, d_R=64, d_h=d_v=128 (got %d,%d,%d,%d)",
+  const bool known = r->cache_dtype == MLA_BF16 || r->cache_dtype == MLA_FP8_E4M3 ||
+                     r->cache_dtype == MLA_FP4_E2M1 || r->cache_dtype == MLA_FP8_E4M3_KR_BF16;
+  if (known && r->act_dtype == MLA_BF16) {
+    // d_R = 0 (no decoupled RoPE part) on the bf16 cache only
+    const bool rope_ok = r->d_r == 64 || (r->d_r == 0 && r->cache_dtype == MLA_BF16);
+    if (r->d_c != 512 || !rope_ok || r->d_h != 128 || r->d_v != 128)
+      return fail(MLA_ERR_UNSUPPORTED,
+                  "MFMA kernels need d_c=512, d_h=d_v=128 and d_R=64 (or d_R=0 with a bf16 cache) (got %d,%d,%d,%d)",
                   r->d_c, r->d_r, r->d_h, r->d_v);
     if (r->n_h % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "bf16/fp8 kernels need num_heads %% 64 == 0");
     if (r->bs % 64 != 0) return fail(MLA_ERR_UNSUPPORTED, "bf16/fp8 kernels need block_size %% 64 == 0");
@@ -183,18 +211,23 @@ extern "C" {
 size_t mla_cache_row_bytes(const mla_dims_t* dims) {
   // a pure size helper: defined for any positive dims, kernel support aside
   if (dims == nullptr || dims->kv_lora_rank <= 0 || dims->qk_rope_head_dim < 0) return 0;
-  if (dims->cache_dtype < MLA_F32 || dims->cache_dtype > MLA_FP8_E4M3) return 0;
-  return static_cast<size_t>(dims->kv_lora_rank + dims->qk_rope_head_dim) * elem_size(dims->cache_dtype);
+  return row_bytes(dims->cache_dtype, dims->kv_lora_rank, dims->qk_rope_head_dim);
 }
 
 size_t mla_cache_bytes_per_token(const mla_dims_t* dims) {
   const size_t row = mla_cache_row_bytes(dims);
-  return row > 0 && dims->cache_dtype == MLA_FP8_E4M3 ? row + sizeof(float) : row;
+  const bool scaled = dims != nullptr && (dims->cache_dtype == MLA_FP8_E4M3 || dims->cache_dtype == MLA_FP8_E4M3_KR_BF16);
+  return row > 0 && scaled ? row + sizeof(float) : row;
 }
 
 size_t mla_q_lat_row_bytes(const mla_dims_t* dims) {
-  const size_t row = mla_cache_row_bytes(dims);
-  return dims != nullptr && dims->cache_dtype == MLA_FP8_E4M3 ? 2 * row : row;
+  if (mla_cache_row_bytes(dims) == 0) return 0;
+  const size_t D = static_cast<size_t>(dims->kv_lora_rank) + dims->qk_rope_head_dim;
+  switch (dims->cache_dtype) {
+    case MLA_F32: return 4 * D;
+    case MLA_FP8_E4M3: return 2 * D;  // two e4m3 planes
+    default: return 2 * D;            // bf16 (also for the FP4 and FP8-KR caches)
+  }
 }
 
 size_t mla_append_workspace_size(const mla_dims_t* dims, int32_t n_tokens) {
@@ -216,7 +249,7 @@ mla_status_t mla_append_latent(const mla_dims_t* dims, const void* hidden, const
   if (!hidden || !rms_gamma || !positions || !slot_mapping || !cache)
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if (cache_slots <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_slots must be positive");
-  if (r.cache_dtype == MLA_FP8_E4M3 && !cache_scale)
+  if ((r.cache_dtype == MLA_FP8_E4M3 || r.cache_dtype == MLA_FP8_E4M3_KR_BF16) && !cache_scale)
     return fail(MLA_ERR_INVALID_ARGUMENT, "fp8 cache needs cache_scale");
   const size_t need = mla_append_workspace_size(dims, n_tokens);
   if (r.mfma && w_dkv_kr != nullptr && (workspace == nullptr || workspace_bytes < need))
@@ -289,6 +322,8 @@ mla_status_t mla_decode_uniform(const mla_dims_t* dims, const void* q_lat, const
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if (r.cache_dtype == MLA_FP8_E4M3 && (!q_scale || !cache_scale))
     return fail(MLA_ERR_INVALID_ARGUMENT, "fp8 decode needs q_scale and cache_scale");
+  if (r.cache_dtype == MLA_FP8_E4M3_KR_BF16 && !cache_scale)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "the fp8 latent needs cache_scale");
   if (r.mfma && q_len > 2) return fail(MLA_ERR_UNSUPPORTED, "bf16/fp8 decode supports q_len <= 2");
   if (split_tokens < 0 || (r.mfma && split_tokens % 64 != 0))
     return fail(MLA_ERR_INVALID_ARGUMENT, "split_tokens must be 0 or a positive multiple of 64");
@@ -320,8 +355,7 @@ mla_status_t mla_decode_uniform(const mla_dims_t* dims, const void* q_lat, const
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu workspace bytes, got %zu", need, workspace_bytes);
   a.workspace = workspace;
-  return hip_status(r.cache_dtype == MLA_FP8_E4M3 ? mla::launch_decode_fp8(a, s) : mla::launch_decode_mfma(a, s),
-                    "mla_decode_uniform");
+  return hip_status(launch_decode_for(r, a, s), "mla_decode_uniform");
 }
 
 mla_status_t mla_decode_uniform_noalloc(const mla_dims_t* dims, const void* q_lat, const float* q_scale,
@@ -443,6 +477,8 @@ mla_status_t mla_decode(const mla_dims_t* dims, const mla_plan_t* plan, const vo
     return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
   if (r.cache_dtype == MLA_FP8_E4M3 && (!q_scale || !cache_scale))
     return fail(MLA_ERR_INVALID_ARGUMENT, "fp8 decode needs q_scale and cache_scale");
+  if (r.cache_dtype == MLA_FP8_E4M3_KR_BF16 && !cache_scale)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "the fp8 latent needs cache_scale");
   const mla::PlanLayout lay = mla::plan_layout(plan->batch, plan->num_slots,
                                                partial_bytes(r, plan->q_len, plan->num_partials));
   char* ws = static_cast<char*>(workspace);
@@ -475,8 +511,7 @@ mla_status_t mla_decode(const mla_dims_t* dims, const mla_plan_t* plan, const vo
   a.num_slots = plan->num_slots;
   a.num_partials = plan->num_partials;
   a.workspace = ws + lay.partials;
-  return hip_status(r.cache_dtype == MLA_FP8_E4M3 ? mla::launch_decode_fp8(a, s) : mla::launch_decode_mfma(a, s),
-                    "mla_decode");
+  return hip_status(launch_decode_for(r, a, s), "mla_decode");
 }
 
 mla_status_t mla_out_proj(const mla_dims_t* dims, const void* o_lat, const void* w_uv,

@@ -103,6 +103,9 @@ int decode_waves_per_group(int n_h, int q_len);
 size_t decode_mfma_workspace(int batch, int q_len, int n_h, int num_splits);
 hipError_t launch_decode_mfma(const DecodeArgs&, hipStream_t);
 hipError_t launch_decode_fp8(const DecodeArgs&, hipStream_t);
+// decode over the cache variants, rows expanded to bf16 in LDS
+enum { kDqFp4Mx = 0, kDqFp8Kr = 1, kDqBf16Nope = 2 };
+hipError_t launch_decode_dq(const DecodeArgs&, int fmt, hipStream_t);
 // causal prefill attention of one sequence with per-head keys and values
 // (q, k: [d_h content ; d_R RoPE part] = 192 wide, v: 128 wide)
 struct PrefillArgs {

@@ -41,7 +41,7 @@ __device__ __forceinline__ bf16x8_t load8(const __bf16* p) { return *reinterpret
 constexpr int kProjWaves = 4;
 constexpr int kKBatch = 8;  // k-steps per wave whose loads are in flight together
 
-template <int RT, int MT>
+template <int RT, int MT, int D>
 __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restrict__ h,
                                                           const __bf16* __restrict__ w, int n_tokens,
                                                           int d_model, int chunk_len,
@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restri
           for (int wv = 0; wv < kProjWaves; ++wv) v += red[wv][rt][mt][rl][r];
           const int n = m0 + 32 * mt + 8 * (r >> 2) + 4 * (rl >> 5) + (r & 3);
           if (n < n_tokens)
-            partial[(static_cast<int64_t>(kc) * n_tokens + n) * kD + r0 + 32 * rt + (rl & 31)] = v;
+            partial[(static_cast<int64_t>(kc) * n_tokens + n) * D + r0 + 32 * rt + (rl & 31)] = v;
         }
     __syncthreads();
   }
@@ -110,22 +110,50 @@ __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restri
 constexpr int kMaxChunks = 16;  // contraction slices of the append GEMM
 
 // One workgroup (256 threads) per token: reduce the partials, RMSNorm the
-// latent, rotate the key part, convert, write the cache row.  Thread t < 144
+// latent, rotate the key part, convert, write the cache row.  Thread t < D/4
 // owns columns 4t..4t+3; all its partial quads are requested before any is
 // summed, and the row's sum of squares and maximum go through wave
-// reductions and one LDS word per wave.
-template <bool FP8>
+// reductions and one LDS word per wave.  D = d_c + d_R (576, or 512 without
+// the RoPE part).  Stored forms (OUT):
+//   kOutBf16  the row in bf16
+//   kOutFp8   e4m3 codes of row / s, s = max|row| / 448 in cache_scale[slot]
+//   kOutFp4   MX FP4: per 32 columns one E8M0 scale 2^(floor(log2 max) - 2)
+//             and E2M1 codes of x / scale (nearest, ties to even, saturating
+//             at 6), two per byte (element 2i in the low nibble), then the
+//             D/32 scale bytes and zero padding to 16 bytes
+//   kOutFp8Kr e4m3 codes of the latent / s, s = max|latent| / 448 in
+//             cache_scale[slot], then the RoPE key in bf16
+enum { kOutBf16 = 0, kOutFp8 = 1, kOutFp4 = 2, kOutFp8Kr = 3 };
+
+template <int D, int OUT>
+constexpr int stored_row_bytes() {
+  return OUT == kOutBf16 ? 2 * D : OUT == kOutFp8 ? D : OUT == kOutFp4 ? (D / 2 + D / 32 + 15) / 16 * 16
+                                                                        : kDc + 2 * (D - kDc);
+}
+
+// E2M1 code of y (magnitude index 0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6 plus the
+// sign bit): nearest value, ties to the even index, saturating at 6.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
+  const float a = fabsf(y);
+  uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
+  return m | (__float_as_uint(y) >> 31 << 3);
+}
+
+template <int D, int OUT>
 __global__ void __launch_bounds__(256) append_finish_kernel(
     const float* __restrict__ partial, int n_chunks, int n_tokens, const float* __restrict__ gamma,
     const int32_t* __restrict__ positions, const int64_t* __restrict__ slots, int64_t cache_slots,
     float eps, RopeTable64 rope, void* __restrict__ cache, float* __restrict__ cache_scale) {
-  __shared__ __attribute__((aligned(16))) float kv[kD];
+  constexpr bool kRope = D > kDc;
+  constexpr int kRow = stored_row_bytes<D, OUT>();
+  __shared__ __attribute__((aligned(16))) float kv[D];
   __shared__ float red[2][4];
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t slot = slots[n];
   if (slot < 0 || slot >= cache_slots) return;
-  const bool own = tid < kD / 4;
-  const int q = min(tid, kD / 4 - 1);  // threads past the row repeat its last quad and store nothing
+  const bool own = tid < D / 4;
+  const int q = min(tid, D / 4 - 1);  // threads past the row repeat its last quad and store nothing
   // the rotation of this thread's four key columns (threads 128..143 own
   // them; the others compute one they do not use) only needs the position:
   // it is requested first and evaluated while the partials are in flight
@@ -139,12 +167,14 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
 #pragma unroll
   for (int kc = 0; kc < kMaxChunks; ++kc)
     v[kc] = *reinterpret_cast<const f32x4_t*>(
-        partial + (static_cast<int64_t>(min(kc, n_chunks - 1)) * n_tokens + n) * kD + 4 * q);
+        partial + (static_cast<int64_t>(min(kc, n_chunks - 1)) * n_tokens + n) * D + 4 * q);
   const f32x4_t g = *reinterpret_cast<const f32x4_t*>(gamma + 4 * min(q, kDc / 4 - 1));
   __builtin_amdgcn_sched_barrier(0);
-  float cs[4], sn[4];
+  float cs[4] = {}, sn[4] = {};
+  if constexpr (kRope) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rope_cos_sin_inv(pos, inv_freq[i], &cs[i], &sn[i]);
+    for (int i = 0; i < 4; ++i) rope_cos_sin_inv(pos, inv_freq[i], &cs[i], &sn[i]);
+  }
   f32x4_t s = f32x4_t{};
 #pragma unroll
   for (int kc = 0; kc < kMaxChunks; ++kc)
@@ -167,16 +197,37 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
       o[i] = c < 32 ? x1 * cs[i] - x2 * sn[i] : x1 * sn[i] + x2 * cs[i];
     }
   }
-  if constexpr (!FP8) {
+  uint8_t* row = static_cast<uint8_t*>(cache) + slot * kRow;
+  if constexpr (OUT == kOutBf16) {
     if (own) {
       bf16x4_t b;
 #pragma unroll
       for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16(o[i]);
-      *reinterpret_cast<bf16x4_t*>(static_cast<__bf16*>(cache) + slot * kD + 4 * q) = b;
+      *reinterpret_cast<bf16x4_t*>(row + 8 * q) = b;
+    }
+  } else if constexpr (OUT == kOutFp4) {
+    // the 8 threads of a 32-column block are 8 consecutive lanes
+    float am = fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3])));
+    am = fmaxf(am, __shfl_xor(am, 1));
+    am = fmaxf(am, __shfl_xor(am, 2));
+    am = fmaxf(am, __shfl_xor(am, 4));
+    int ex = 0;
+    frexpf(am, &ex);                                  // am = f 2^ex, f in [0.5, 1)
+    const int shared = am > 0.f ? min(max(ex - 3, -127), 127) : 0;
+    uint32_t code[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) code[i] = f32_to_e2m1(ldexpf(o[i], -shared));
+    if (own) {
+      *reinterpret_cast<uint16_t*>(row + 2 * q) =
+          static_cast<uint16_t>(code[0] | code[1] << 4 | code[2] << 8 | code[3] << 12);
+      if ((q & 7) == 0) row[D / 2 + q / 8] = static_cast<uint8_t>(shared + 127);
+      if (q == 0)
+        for (int bt = D / 2 + D / 32; bt < kRow; bt += 2) *reinterpret_cast<uint16_t*>(row + bt) = 0;
     }
   } else {
+    constexpr bool kLatentOnly = OUT == kOutFp8Kr;
     float am = 0.f;
-    if (own)
+    if (own && (!kLatentOnly || q < kDc / 4))
 #pragma unroll
       for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(o[i]));
     am = wave_max(am);
@@ -185,10 +236,17 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
     const float amax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
     if (own) {
-      uint32_t packed = 0;
+      if (!kLatentOnly || q < kDc / 4) {
+        uint32_t packed = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) packed |= f32_to_e4m3(o[i] / scale) << (8 * i);
-      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(cache) + slot * kD + 4 * q) = packed;
+        for (int i = 0; i < 4; ++i) packed |= f32_to_e4m3(o[i] / scale) << (8 * i);
+        *reinterpret_cast<uint32_t*>(row + 4 * q) = packed;
+      } else {
+        bf16x4_t b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16(o[i]);
+        *reinterpret_cast<bf16x4_t*>(row + kDc + 8 * (q - kDc / 4)) = b;
+      }
     }
     if (tid == 0) cache_scale[slot] = scale;
   }
@@ -205,7 +263,7 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
 // with the weight slice, and that item's cos/sin are evaluated while they
 // are in flight; token rows past the end are clamped to the last row and
 // never stored.
-template <bool OUT_F32, int MT>
+template <bool OUT_F32, int MT, int DR>
 __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict__ q_nope,
                                                        const __bf16* __restrict__ q_pe,
                                                        const __bf16* __restrict__ w_uk,
@@ -218,11 +276,17 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
   const __bf16* W = w_uk + static_cast<int64_t>(head) * kDh * kDc + ct * 128;
   // the first RoPE item's inputs are requested first, so that its rotation
   // only waits for them
+  constexpr int kRowD = kDc + DR;  // width of a latent-query row
   const int pair = 8 * ct + (threadIdx.x & 7);
   int item = min(static_cast<int>(threadIdx.x), 8 * n_tokens - 1);
   auto rope_in = [&](int n) { return q_pe + (static_cast<int64_t>(n) * n_h + head) * kDr + pair; };
-  const int pos = positions[item >> 3];
-  float x1 = static_cast<float>(*rope_in(item >> 3)), x2 = static_cast<float>(*(rope_in(item >> 3) + 32));
+  float x1 = 0.f, x2 = 0.f;
+  int pos = 0;
+  if constexpr (DR > 0) {
+    pos = positions[item >> 3];
+    x1 = static_cast<float>(*rope_in(item >> 3));
+    x2 = static_cast<float>(*(rope_in(item >> 3) + 32));
+  }
   const double inv_freq = rope.inv[pair];
   __builtin_amdgcn_sched_barrier(0);
   bf16x8_t v[8];
@@ -243,8 +307,8 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
     __builtin_amdgcn_sched_barrier(0);  // keep the pass's loads in flight together
   };
   load_queries(0);
-  float cs, sn;
-  rope_cos_sin_inv(pos, inv_freq, &cs, &sn);  // while the weight and query loads are in flight
+  float cs = 1.f, sn = 0.f;
+  if constexpr (DR > 0) rope_cos_sin_inv(pos, inv_freq, &cs, &sn);  // while the weight and query loads are in flight
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = threadIdx.x + 256 * j, r = i >> 4, ch = i & 15;
@@ -276,7 +340,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
       for (int r = 0; r < 16; ++r) {
         const int n = m0 + 32 * mt + 8 * (r >> 2) + 4 * hf + (r & 3);
         if (n < n_tokens) {
-          const int64_t idx = (static_cast<int64_t>(n) * n_h + head) * kD + ct * 128 + 32 * wave + l32;
+          const int64_t idx = (static_cast<int64_t>(n) * n_h + head) * kRowD + ct * 128 + 32 * wave + l32;
           if constexpr (OUT_F32) static_cast<float*>(q_out)[idx] = acc[mt][r];
           else static_cast<__bf16*>(q_out)[idx] = f32_to_bf16(acc[mt][r]);
         }
@@ -286,6 +350,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
     load_queries(m0);
   }
   // RoPE part of the latent query
+  if constexpr (DR == 0) return;
   for (int i = threadIdx.x; i < 8 * n_tokens; i += 256) {
     const int n = i >> 3;
     if (i != item) {
@@ -294,7 +359,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
       x2 = static_cast<float>(*(rope_in(n) + 32));
       rope_cos_sin_inv(positions[n], inv_freq, &cs, &sn);
     }
-    const int64_t base = (static_cast<int64_t>(n) * n_h + head) * kD + kDc + pair;
+    const int64_t base = (static_cast<int64_t>(n) * n_h + head) * kRowD + kDc + pair;
     const float y1 = x1 * cs - x2 * sn, y2 = x1 * sn + x2 * cs;
     if constexpr (OUT_F32) {
       static_cast<float*>(q_out)[base] = y1;
@@ -454,14 +519,15 @@ size_t append_mfma_workspace(int n_tokens) {
   return static_cast<size_t>(16) * n_tokens * kD * sizeof(float);
 }
 
-hipError_t launch_append_mfma(const AppendArgs& a, hipStream_t st) {
+template <int D>
+hipError_t launch_append_d(const AppendArgs& a, hipStream_t st) {
   const float* partial;
   int n_chunks;
   if (a.w != nullptr) {
     n_chunks = append_chunks(a.d_model);
     float* ws = static_cast<float*>(a.workspace);
-    auto kern = append_proj_kernel<kAppendRT, kAppendMT>;
-    hipLaunchKernelGGL(kern, dim3(kD / (32 * kAppendRT), n_chunks, token_groups(a.n_tokens, kAppendMT)), dim3(256),
+    auto kern = append_proj_kernel<kAppendRT, kAppendMT, D>;
+    hipLaunchKernelGGL(kern, dim3(D / (32 * kAppendRT), n_chunks, token_groups(a.n_tokens, kAppendMT)), dim3(256),
                        0, st,
                        static_cast<const __bf16*>(a.hidden), static_cast<const __bf16*>(a.w),
                        a.n_tokens, a.d_model, a.d_model / n_chunks, ws);
@@ -472,15 +538,21 @@ hipError_t launch_append_mfma(const AppendArgs& a, hipStream_t st) {
     n_chunks = 1;
     partial = static_cast<const float*>(a.hidden);
   }
-  if (a.cache_dtype == 2)
-    hipLaunchKernelGGL(append_finish_kernel<true>, dim3(a.n_tokens), dim3(256), 0, st, partial,
-                       n_chunks, a.n_tokens, a.gamma, a.positions, a.slots, a.cache_slots, a.eps,
-                       rope_table(a.theta), a.cache, a.cache_scale);
-  else
-    hipLaunchKernelGGL(append_finish_kernel<false>, dim3(a.n_tokens), dim3(256), 0, st, partial,
-                       n_chunks, a.n_tokens, a.gamma, a.positions, a.slots, a.cache_slots, a.eps,
-                       rope_table(a.theta), a.cache, a.cache_scale);
+  auto finish = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(a.n_tokens), dim3(256), 0, st, partial, n_chunks, a.n_tokens, a.gamma,
+                       a.positions, a.slots, a.cache_slots, a.eps, rope_table(a.theta), a.cache, a.cache_scale);
+  };
+  switch (a.cache_dtype) {
+    case 2: finish(append_finish_kernel<D, kOutFp8>); break;
+    case 3: finish(append_finish_kernel<D, kOutFp4>); break;
+    case 4: finish(append_finish_kernel<D, kOutFp8Kr>); break;
+    default: finish(append_finish_kernel<D, kOutBf16>); break;
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_append_mfma(const AppendArgs& a, hipStream_t st) {
+  return a.d_r == 0 ? launch_append_d<kDc>(a, st) : launch_append_d<kD>(a, st);
 }
 
 size_t absorb_mfma_workspace(int n_tokens, int n_h, int cache_dtype) {
@@ -493,8 +565,12 @@ hipError_t launch_absorb_q_mfma(const AbsorbArgs& a, hipStream_t st) {
   const auto q_nope = static_cast<const __bf16*>(a.q_nope);
   const auto q_pe = static_cast<const __bf16*>(a.q_pe);
   const auto w_uk = static_cast<const __bf16*>(a.w_uk);
-  if (a.cache_dtype == 2) {
-    auto kern = one ? absorb_q_kernel<true, 1> : absorb_q_kernel<true, 2>;
+  if (a.d_r == 0) {  // no RoPE part: rows of d_c, bf16
+    auto kern = one ? absorb_q_kernel<false, 1, 0> : absorb_q_kernel<false, 2, 0>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q_nope, q_pe, w_uk, a.positions, a.n_tokens, a.n_h,
+                       rope_table(a.theta), a.q_lat);
+  } else if (a.cache_dtype == 2) {
+    auto kern = one ? absorb_q_kernel<true, 1, kDr> : absorb_q_kernel<true, 2, kDr>;
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q_nope, q_pe, w_uk, a.positions, a.n_tokens, a.n_h,
                        rope_table(a.theta), a.workspace);
     hipError_t e = hipGetLastError();
@@ -503,7 +579,7 @@ hipError_t launch_absorb_q_mfma(const AbsorbArgs& a, hipStream_t st) {
                        static_cast<const float*>(a.workspace), static_cast<uint8_t*>(a.q_lat),
                        a.q_scale);
   } else {
-    auto kern = one ? absorb_q_kernel<false, 1> : absorb_q_kernel<false, 2>;
+    auto kern = one ? absorb_q_kernel<false, 1, kDr> : absorb_q_kernel<false, 2, kDr>;
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q_nope, q_pe, w_uk, a.positions, a.n_tokens, a.n_h,
                        rope_table(a.theta), a.q_lat);
   }

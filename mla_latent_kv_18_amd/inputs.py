@@ -17,6 +17,11 @@ hyper-parameters; shapes and lengths as the workload list states):
   kimi_k2_ragged_bs32   n_h=64, B=32, lengths uniform in [1024, 131072]
   v3_fp8_bs4_ctx128k_q2 fp8 e4m3 cache with one fp32 scale per token, B=4,
                     131072 tokens each, 2 causal queries per request
+  Cache variants (same V3 dims and batch as v3_bs64_ctx4k):
+  v3_fp4_bs64_ctx4k     MX FP4 rows: 576 E2M1 codes, one E8M0 scale per 32
+  v3_fp8kr_bs64_ctx4k   e4m3 latent (one fp32 scale per token) beside a
+                        bf16 RoPE key
+  nope_bs64_ctx4k       no decoupled RoPE part (d_R = 0): 512-wide bf16 rows
 
 Value recipe: weights N(0,1)/sqrt(fan_in) (fan_in = d_model for the
 down-projection, d_c for W^UK and W^UV); RMSNorm gain U[0.5, 1.5]; hidden
@@ -46,7 +51,7 @@ class Workload:
     batch: int
     seq_len: int            # tokens per request (upper bound when ragged)
     q_len: int
-    dtype: str              # "f32" | "bf16" | "fp8" (cache); activations f32 or bf16
+    dtype: str              # cache: "f32" | "bf16" | "fp8" | "fp4" | "fp8kr"; activations f32 or bf16
     block_size: int = 64
     shuffle: bool = False
     ragged_min: int = 0     # >0: lengths uniform in [ragged_min, seq_len]
@@ -61,6 +66,13 @@ class Workload:
     @property
     def row_dim(self):
         return self.d_c + self.d_r
+
+    @property
+    def row_bytes(self):
+        """Bytes of one stored cache row."""
+        D = self.row_dim
+        return {"f32": 4 * D, "bf16": 2 * D, "fp8": D, "fp4": (D // 2 + D // 32 + 15) // 16 * 16,
+                "fp8kr": self.d_c + 2 * self.d_r}[self.dtype]
 
     @property
     def softmax_scale(self):
@@ -84,6 +96,12 @@ WORKLOADS = {
     "v3_fp8_bs4_ctx128k_q2": Workload("v3_fp8_bs4_ctx128k_q2", n_h=128, d_c=512, d_h=128, d_r=64,
                                       d_v=128, d_model=7168, batch=4, seq_len=131072, q_len=2,
                                       dtype="fp8", seed=5),
+    "v3_fp4_bs64_ctx4k": Workload("v3_fp4_bs64_ctx4k", n_h=128, d_c=512, d_h=128, d_r=64, d_v=128,
+                                  d_model=7168, batch=64, seq_len=4096, q_len=1, dtype="fp4", seed=6),
+    "v3_fp8kr_bs64_ctx4k": Workload("v3_fp8kr_bs64_ctx4k", n_h=128, d_c=512, d_h=128, d_r=64, d_v=128,
+                                    d_model=7168, batch=64, seq_len=4096, q_len=1, dtype="fp8kr", seed=7),
+    "nope_bs64_ctx4k": Workload("nope_bs64_ctx4k", n_h=128, d_c=512, d_h=128, d_r=0, d_v=128,
+                                d_model=7168, batch=64, seq_len=4096, q_len=1, dtype="bf16", seed=8),
 }
 
 
@@ -102,6 +120,38 @@ def to_fp8_rows(x):
     scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
     q = torch.from_numpy(x / scale[..., None]).to(torch.float8_e4m3fn)
     return q.view(torch.uint8).numpy(), scale
+
+
+def to_fp4_rows(x):
+    """float32 rows [n, d] -> stored MX FP4 rows [n, row bytes] uint8: per
+    32-element block one E8M0 scale 2^(floor(log2 max|x|) - 2) (127 for an
+    all-zero block) and E2M1 codes of x / scale, nearest value, ties to the
+    even code, saturating at 6; two codes per byte (element 2i in the low
+    nibble); then the d/32 scale bytes; then zero padding to 16 bytes."""
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    blk = x.reshape(n, d // 32, 32)
+    amax = np.abs(blk).max(axis=-1)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    shared = np.clip(np.where(amax > 0, e - 3, 0), -127, 127)
+    y = blk / np.ldexp(1.0, shared)[..., None]
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    dist = np.abs(np.minimum(np.abs(y), 6.0)[..., None] - grid) + 1e-12 * (np.arange(8) & 1)
+    codes = (np.argmin(dist, axis=-1) | np.where(np.signbit(y), 8, 0)).astype(np.uint8).reshape(n, d)
+    row_bytes = (d // 2 + d // 32 + 15) // 16 * 16
+    out = np.zeros((n, row_bytes), dtype=np.uint8)
+    out[:, :d // 2] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    out[:, d // 2:d // 2 + d // 32] = (shared + 127).astype(np.uint8)
+    return out
+
+
+def to_fp8kr_rows(x, d_c):
+    """float32 rows [n, d_c + d_R] -> (uint8 rows [n, d_c + 2 d_R], float32
+    scale per row): the latent as e4m3 codes with one scale max|latent|/448,
+    the RoPE key as bf16 (little-endian bytes)."""
+    codes, scale = to_fp8_rows(np.asarray(x, dtype=np.float32)[:, :d_c])
+    kr = to_bf16_bits(np.asarray(x, dtype=np.float32)[:, d_c:])
+    return np.concatenate([codes, np.ascontiguousarray(kr).view(np.uint8)], axis=1), scale
 
 
 def _store(x, fmt):
@@ -156,8 +206,8 @@ def generate(w: Workload):
     elif w.dtype == "bf16":
         pool = np.zeros(pool_shape, dtype=np.uint16)
     else:
-        pool = np.zeros(pool_shape, dtype=np.uint8)
-    pool_scale = np.ones((total_blocks, bs), dtype=np.float32) if w.dtype == "fp8" else None
+        pool = np.zeros((total_blocks, bs, w.row_bytes), dtype=np.uint8)
+    pool_scale = np.ones((total_blocks, bs), dtype=np.float32) if w.dtype in ("fp8", "fp8kr") else None
 
     # pre-filled rows, request by request, written in logical order; the
     # physical placement is applied after the permutation is drawn
@@ -192,6 +242,12 @@ def generate(w: Workload):
             pool[blk, idx % bs] = rows
         elif w.dtype == "bf16":
             pool[blk, idx % bs] = to_bf16_bits(rows)
+        elif w.dtype == "fp4":
+            pool[blk, idx % bs] = to_fp4_rows(rows)
+        elif w.dtype == "fp8kr":
+            codes, scale = to_fp8kr_rows(rows, w.d_c)
+            pool[blk, idx % bs] = codes
+            pool_scale[blk, idx % bs] = scale
         else:
             codes, scale = to_fp8_rows(rows)
             pool[blk, idx % bs] = codes

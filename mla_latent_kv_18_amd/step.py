@@ -38,8 +38,8 @@ class DeviceStep:
         self.h = _dev(gen["h"], device, act)
         self.q_nope = _dev(gen["q_nope"], device, act)
         self.q_pe = _dev(gen["q_pe"], device, act)
-        self.cache = _dev(gen["pool"], device, w.dtype if w.dtype != "fp8" else "u8")
-        self.cache_scale = _dev(gen["pool_scale"], device, "f32") if w.dtype == "fp8" else None
+        self.cache = _dev(gen["pool"], device, w.dtype if w.dtype in ("f32", "bf16") else "u8")
+        self.cache_scale = _dev(gen["pool_scale"], device, "f32") if gen["pool_scale"] is not None else None
         self.block_table = _dev(gen["block_table"], device, "i32")
         self.seq_lens = _dev(gen["seq_lens"], device, "i32")
         self.max_seq_len = int(gen["seq_lens"].max())
@@ -48,7 +48,8 @@ class DeviceStep:
         self.q_pos = _dev(gen["q_positions"], device, "i32")
         N = w.batch * w.q_len
         D = w.d_c + w.d_r
-        lat_dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[w.dtype]
+        lat_dtype = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "fp4": torch.bfloat16,
+                     "fp8kr": torch.bfloat16}[w.dtype]
         out_dtype = torch.float32 if act == "f32" else torch.bfloat16
         self.q_lat = torch.empty(N, w.n_h, 2 * D if w.dtype == "fp8" else D, dtype=lat_dtype, device=device)
         self.q_scale = torch.empty(N, w.n_h, dtype=torch.float32, device=device) if w.dtype == "fp8" else None

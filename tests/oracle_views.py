@@ -16,13 +16,26 @@ def f64(a, fmt):
     raise ValueError(fmt)
 
 
-def stored_rows(pool, pool_scale, table_row, T, bs, fmt):
+def decode_rows(raw, scales, fmt, d_c=512, D=576):
+    """Stored rows [n, row bytes or elements] (+ per-row scales) -> float64
+    [n, D], exactly as a reader of the stored bits reconstructs them."""
+    if fmt == "fp8":
+        return codecs.e4m3_dequantize_rows(raw, scales)
+    if fmt == "fp4":       # [D/2 bytes of E2M1 codes | D/32 E8M0 scales | padding]
+        codes = codecs.unpack_nibbles(raw[:, :D // 2], D)
+        return codecs.mx_fp4_dequantize_rows(codes, raw[:, D // 2:D // 2 + D // 32])
+    if fmt == "fp8kr":     # [d_c e4m3 codes | d_R bf16 values]
+        lat = codecs.e4m3_dequantize_rows(raw[:, :d_c], scales)
+        kr = codecs.bf16_decode(np.ascontiguousarray(raw[:, d_c:]).view(np.uint16))
+        return np.concatenate([lat, kr], axis=1)
+    return f64(raw, fmt)
+
+
+def stored_rows(pool, pool_scale, table_row, T, bs, fmt, d_c=512, D=576):
     """Rows 0..T-1 of one request as float64, exactly as stored."""
     raw = ref.gather_rows(pool, table_row, T, bs)
-    if fmt == "fp8":
-        sc = ref.gather_rows(pool_scale[..., None], table_row, T, bs)[:, 0]
-        return codecs.e4m3_dequantize_rows(raw, sc)
-    return f64(raw, fmt)
+    sc = ref.gather_rows(pool_scale[..., None], table_row, T, bs)[:, 0] if pool_scale is not None else None
+    return decode_rows(raw, sc, fmt, d_c, D)
 
 
 def weights(gen):
@@ -55,7 +68,8 @@ def reference_cache(gen, b):
     stored, this step's rows computed in fp64 by the oracle."""
     w = gen["workload"]
     T = int(gen["seq_lens"][b])
-    rows = stored_rows(gen["pool"], gen["pool_scale"], gen["block_table"][b], T, w.block_size, w.dtype)
+    rows = stored_rows(gen["pool"], gen["pool_scale"], gen["block_table"][b], T, w.block_size, w.dtype, w.d_c,
+                       w.row_dim)
     start, c, kr = new_rows(gen, b)
     rows[start:, :w.d_c] = c
     rows[start:, w.d_c:] = kr
@@ -82,4 +96,6 @@ def rel_err(got, want):
     return float(np.max(np.abs(got - want)) / (denom if denom > 0 else 1.0))
 
 
-TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+# fp4 and fp8kr caches are read exactly as stored (the oracle uses the stored
+# values) and attended in bf16 arithmetic: the bf16 bar.
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "fp4": 2e-2, "fp8kr": 2e-2}

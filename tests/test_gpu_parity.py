@@ -37,15 +37,57 @@ def _host(t, fmt):
     return t.numpy().astype(np.float64)
 
 
-def _gpu_rows(step, b, T):
+def _gpu_raw_rows(step, b, T):
+    """Stored rows 0..T-1 of request b as the GPU holds them, and their scales."""
     w = step.w
     nb = (T + w.block_size - 1) // w.block_size
     blocks = step.block_table[b, :nb].long()
-    raw = step.cache[blocks].reshape(-1, w.row_dim)[:T]
-    if w.dtype == "fp8":
+    width = w.row_dim if w.dtype in ("f32", "bf16") else w.row_bytes
+    raw = step.cache[blocks].reshape(-1, width)[:T]
+    sc = None
+    if step.cache_scale is not None:
         sc = step.cache_scale[blocks].reshape(-1)[:T].cpu().numpy().astype(np.float64)
-        return codecs.e4m3_decode(raw.cpu().numpy()) * sc[:, None]
-    return _host(raw, w.dtype)
+    return raw, sc
+
+
+def _gpu_rows(step, b, T):
+    w = step.w
+    raw, sc = _gpu_raw_rows(step, b, T)
+    if w.dtype in ("f32", "bf16"):
+        return _host(raw, w.dtype)
+    return ov.decode_rows(raw.cpu().numpy(), sc, w.dtype, w.d_c, w.row_dim)
+
+
+def _q_fmt(w):
+    return "fp8" if w.dtype == "fp8" else ("f32" if w.dtype == "f32" else "bf16")
+
+
+E2M1_BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def check_fp4_rows(raw, exact):
+    """Stored MX FP4 rows against the oracle's quantisation of the exact rows.
+    The kernel rounds from fp32 values and the oracle from fp64 ones, so a
+    scale may differ where a block maximum sits at a power of two and a code
+    where x / scale sits at a rounding boundary; everything else is equal,
+    and the padding is zero."""
+    D = exact.shape[1]
+    codes = codecs.unpack_nibbles(raw[:, :D // 2], D).astype(np.int64)
+    sb = raw[:, D // 2:D // 2 + D // 32].astype(np.int64)
+    assert not np.any(raw[:, D // 2 + D // 32:]), "padding"
+    oc, osb = codecs.mx_fp4_quantize_rows(exact)
+    blocks = np.abs(exact).reshape(exact.shape[0], -1, 32)
+    amax = blocks.max(axis=-1)
+    with np.errstate(divide="ignore"):
+        l2 = np.log2(np.where(amax > 0, amax, 1.0))
+    near_pow2 = np.abs(l2 - np.round(l2)) < 1e-4
+    same_scale = sb == osb
+    assert np.all(same_scale | near_pow2), "block scales"
+    y = np.abs(exact) / np.repeat(codecs.e8m0_decode(osb), 32, axis=1)
+    near_tie = np.min(np.abs(y[..., None] - E2M1_BOUNDS) / E2M1_BOUNDS, axis=-1) < 1e-3
+    both_zero = ((codes & 7) == 0) & ((oc.astype(np.int64) & 7) == 0)
+    ok = (codes == oc) | near_tie | both_zero | ~np.repeat(same_scale, 32, axis=1)
+    assert ok.all(), "E2M1 codes"
 
 
 def check_request(step, gen, b, heads, tol, lse_tol):
@@ -58,8 +100,14 @@ def check_request(step, gen, b, heads, tol, lse_tol):
     start, c, kr = ov.new_rows(gen, b)
     rows = _gpu_rows(step, b, T)
     if T > start:
-        assert ov.rel_err(rows[start:, :w.d_c], c) <= tol, "append latent"
-        assert ov.rel_err(rows[start:, w.d_c:], kr) <= tol, "append rope key"
+        if w.dtype == "fp4":
+            raw, _ = _gpu_raw_rows(step, b, T)
+            check_fp4_rows(raw[start:].cpu().numpy(), np.concatenate([c, kr], axis=1))
+        else:
+            lat_tol = ov.TOL["fp8"] if w.dtype == "fp8kr" else tol   # e4m3 latent
+            assert ov.rel_err(rows[start:, :w.d_c], c) <= lat_tol, "append latent"
+            if w.d_r > 0:
+                assert ov.rel_err(rows[start:, w.d_c:], kr) <= tol, "append rope key"
     # absorb
     q_nope = ov.f64(gen["q_nope"], act)[sl]
     q_pe = ov.f64(gen["q_pe"], act)[sl]
@@ -71,7 +119,7 @@ def check_request(step, gen, b, heads, tol, lse_tol):
         q_lat = (planes[..., :D] + planes[..., D:] / 16.0) * \
             step.q_scale[sl].cpu().numpy().astype(np.float64)[..., None]
     else:
-        q_lat = _host(step.q_lat[sl], w.dtype)
+        q_lat = _host(step.q_lat[sl], _q_fmt(w))
     assert ov.rel_err(q_lat[:, heads], q_lat_ref[:, heads]) <= tol, "absorb q"
     # decode, fed the GPU's q_lat and cache rows
     o_ref, lse_ref = ref.decode_absorbed(q_lat[:, heads], q_pos, rows[:, :w.d_c], rows[:, w.d_c:],
@@ -86,8 +134,14 @@ def check_request(step, gen, b, heads, tol, lse_tol):
     # out proj, fed the GPU's o_lat
     out = _host(step.out[sl], act)
     assert ov.rel_err(out[:, heads], ref.out_proj(o_lat, wuv)[:, heads]) <= tol, "out proj"
-    # end to end against the non-absorbed oracle
-    want = ov.reference_output(gen, b, heads=heads)
+    # end to end against the non-absorbed oracle (for the FP4 and fp8-latent
+    # caches over every row as stored, this step's too: the oracle reads the
+    # cache it is given)
+    if w.dtype in ("fp4", "fp8kr"):
+        want = ref.attention_nonabsorbed(q_nope, q_pe, q_pos, rows[:, :w.d_c], rows[:, w.d_c:], wuk, wuv,
+                                         w.softmax_scale, heads=heads)
+    else:
+        want = ov.reference_output(gen, b, heads=heads)
     assert ov.rel_err(out[:, heads], want) <= tol, "end to end"
 
 
@@ -190,7 +244,35 @@ def test_small_fp8_all_heads(name, split_tokens, mode):
         check_request(step, gen, b, list(range(w.n_h)), ov.TOL["fp8"], 2e-2)
 
 
-FULL = ["v3_bs64_ctx4k", "v3_paged_bs16_ctx32k", "kimi_k2_ragged_bs32", "v3_fp8_bs4_ctx128k_q2"]
+# Cache variants: MX FP4 rows, an e4m3 latent beside a bf16 RoPE key, and
+# no RoPE part (d_R = 0), on both decode workgroup shapes (128 and 64 rows).
+SMALL_VARIANTS = {
+    "fp4_ragged": ("v3_fp4_bs64_ctx4k", dict(batch=3, lens=(1, 100, 257), shuffle=True)),
+    "fp4_heads64_q2": ("v3_fp4_bs64_ctx4k", dict(n_h=64, batch=2, lens=(2, 200), q_len=2)),
+    "fp8kr_ragged": ("v3_fp8kr_bs64_ctx4k", dict(batch=3, lens=(1, 100, 257), shuffle=True)),
+    "fp8kr_heads64": ("v3_fp8kr_bs64_ctx4k", dict(n_h=64, batch=3, lens=(33, 64, 300))),
+    "nope_ragged": ("nope_bs64_ctx4k", dict(batch=3, lens=(1, 100, 257), shuffle=True)),
+    "nope_heads64_q2": ("nope_bs64_ctx4k", dict(n_h=64, batch=2, lens=(2, 200), q_len=2)),
+    "nope_batch8": ("nope_bs64_ctx4k", dict(batch=8, lens=(0, 2, 63, 64, 65, 500, 1000, 2048))),
+}
+
+
+@pytest.mark.parametrize("mode", ["planned", "uniform"])
+@pytest.mark.parametrize("name", sorted(SMALL_VARIANTS))
+@pytest.mark.parametrize("split_tokens", [0, 64, 128])
+def test_small_cache_variants_all_heads(name, split_tokens, mode):
+    base, over = SMALL_VARIANTS[name]
+    w = WORKLOADS[base].scaled(name=name, seed=17, **over)
+    gen, step = _run(w, split_tokens, mode)
+    for b in range(w.batch):
+        if int(gen["seq_lens"][b]) == 0:
+            assert torch.all(step.o_lat[b * w.q_len:(b + 1) * w.q_len].float() == 0).item()
+            continue
+        check_request(step, gen, b, list(range(w.n_h)), ov.TOL[w.dtype], 2e-2)
+
+
+FULL = ["v3_bs64_ctx4k", "v3_paged_bs16_ctx32k", "kimi_k2_ragged_bs32", "v3_fp8_bs4_ctx128k_q2",
+        "v3_fp4_bs64_ctx4k", "v3_fp8kr_bs64_ctx4k", "nope_bs64_ctx4k"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -265,7 +347,7 @@ def plant_peaks(gen, plants, seed):
     q_nope = ov.f64(gen["q_nope"], w.act_dtype)
     q_pe = ov.f64(gen["q_pe"], w.act_dtype)
     q_lat = ref.absorb_q(q_nope, q_pe, gen["q_positions"], wuk)
-    from mla_latent_kv_18_amd.inputs import to_bf16_bits, to_fp8_rows
+    from mla_latent_kv_18_amd.inputs import to_bf16_bits, to_fp4_rows, to_fp8_rows, to_fp8kr_rows
     for b, pos, t, h, score in plants:
         assert pos < int(gen["seq_lens"][b]) - w.q_len, "plant a pre-filled row"
         q = q_lat[b * w.q_len + t, h]
@@ -273,6 +355,12 @@ def plant_peaks(gen, plants, seed):
         blk = gen["block_table"][b, pos // w.block_size]
         if w.dtype == "bf16":
             gen["pool"][blk, pos % w.block_size] = to_bf16_bits(row[None])[0]
+        elif w.dtype == "fp4":
+            gen["pool"][blk, pos % w.block_size] = to_fp4_rows(row[None].astype(np.float32))[0]
+        elif w.dtype == "fp8kr":
+            codes, sc = to_fp8kr_rows(row[None].astype(np.float32), w.d_c)
+            gen["pool"][blk, pos % w.block_size] = codes[0]
+            gen["pool_scale"][blk, pos % w.block_size] = sc[0]
         else:
             codes, sc = to_fp8_rows(row[None].astype(np.float32))
             gen["pool"][blk, pos % w.block_size] = codes[0]
@@ -291,7 +379,7 @@ def check_decode_call(step, gen, b, tol, lse_tol=2e-2):
         q_lat = (planes[..., :D] + planes[..., D:] / 16.0) * \
             step.q_scale[sl].cpu().numpy().astype(np.float64)[..., None]
     else:
-        q_lat = _host(step.q_lat[sl], w.dtype)
+        q_lat = _host(step.q_lat[sl], _q_fmt(w))
     o_ref, lse_ref = ref.decode_absorbed(q_lat, gen["q_positions"][sl], rows[:, :w.d_c], rows[:, w.d_c:],
                                          w.softmax_scale)
     o_lat = _host(step.o_lat[sl], w.act_dtype)
@@ -301,7 +389,10 @@ def check_decode_call(step, gen, b, tol, lse_tol=2e-2):
     return float(np.max(lse_ref))
 
 
-PEAK_CASES = {   # base workload, overrides: the four decode kernels
+PEAK_CASES = {   # base workload, overrides: the four decode kernels and the cache-variant kernels
+    "fp4_h128": ("v3_fp4_bs64_ctx4k", dict(batch=2, lens=(400, 700))),
+    "fp8kr_h64_q2": ("v3_fp8kr_bs64_ctx4k", dict(n_h=64, batch=2, lens=(400, 700), q_len=2)),
+    "nope_h64": ("nope_bs64_ctx4k", dict(n_h=64, batch=2, lens=(400, 700))),
     "bf16_pipelined_h128": ("v3_bs64_ctx4k", dict(batch=2, lens=(400, 700))),
     "bf16_pipelined_h128_q2": ("v3_bs64_ctx4k", dict(batch=2, lens=(400, 700), q_len=2)),
     "bf16_plain_h64": ("v3_bs64_ctx4k", dict(n_h=64, batch=2, lens=(400, 700))),
