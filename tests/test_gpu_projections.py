@@ -174,3 +174,69 @@ def test_append_from_given_projection(n, cache_dtype):
         sc = scale.cpu().numpy().astype(np.float64)[slots64[keep]]
         amax = np.max(np.abs(rows[slots64[keep]]), axis=1)
         assert np.allclose(amax, 448.0 * sc, rtol=0.07)
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8kr", "nope"])
+@pytest.mark.parametrize("n", (1, 33, 100, 300))
+def test_append_rows_cache_variants(n, fmt):
+    """mla_append_latent into the cache variants: MX FP4 rows (codes and
+    block scales against the oracle's quantisation of the exact rows), an
+    e4m3 latent beside a bf16 RoPE key, and rows without a RoPE part."""
+    from tests.test_gpu_parity import check_fp4_rows
+    from tests import oracle_views as ov
+    rng = np.random.default_rng(5000 + n)
+    d_r = 0 if fmt == "nope" else D_R
+    cache_dtype = "bf16" if fmt == "nope" else fmt
+    D = D_C + d_r
+    dims = mla.make_dims(N_H, D_C, D_H, d_r, D_V, 1024, 64, cache_dtype, "bf16")
+    h, h64 = _bf16(rng, (n, 1024))
+    w, w64 = _bf16(rng, (D, 1024), 1.0 / np.sqrt(1024))
+    gamma64 = rng.uniform(0.5, 1.5, size=D_C).astype(np.float32).astype(np.float64)
+    gamma = torch.from_numpy(gamma64.astype(np.float32)).cuda()
+    pos64 = rng.integers(0, 131072, n)
+    pos = torch.from_numpy(pos64.astype(np.int32)).cuda()
+    n_blocks = (2 * n + 63) // 64
+    slots64 = rng.permutation(n_blocks * 64)[:n]
+    if n > 1:
+        slots64[0] = -1
+    slots = torch.from_numpy(slots64.astype(np.int64)).cuda()
+    row_bytes = mla.lib().mla_cache_row_bytes(__import__("ctypes").byref(dims))
+    if fmt == "nope":
+        cache = torch.zeros(n_blocks, 64, D, dtype=torch.bfloat16, device="cuda")
+    else:
+        cache = torch.zeros(n_blocks, 64, row_bytes, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(n_blocks * 64, dtype=torch.float32, device="cuda") if fmt == "fp8kr" else None
+    mla.append_latent(dims, h, w, gamma, pos, slots, cache, scale)
+    torch.cuda.synchronize()
+    c_ref, kr_ref = ref.latent_rows(h64, w64, gamma64, pos64, D_C, 1e-6, 10000.0)
+    want = np.concatenate([c_ref, kr_ref], axis=-1)
+    keep = slots64 >= 0
+    if fmt == "nope":
+        rows = _host_bf16(cache.reshape(-1, D))
+        assert _rel_err(rows[slots64[keep]], want[keep]) <= TOL["bf16"]
+    elif fmt == "fp4":
+        raw = cache.reshape(-1, row_bytes).cpu().numpy()
+        check_fp4_rows(raw[slots64[keep]], want[keep])
+        rows = ov.decode_rows(raw, None, "fp4")
+    else:
+        raw = cache.reshape(-1, row_bytes).cpu().numpy()
+        rows = ov.decode_rows(raw, scale.cpu().numpy().astype(np.float64), "fp8kr")
+        got = rows[slots64[keep]]
+        assert _rel_err(got[:, :D_C], want[keep, :D_C]) <= TOL["fp8"], "e4m3 latent"
+        assert _rel_err(got[:, D_C:], want[keep, D_C:]) <= TOL["bf16"], "bf16 rope key"
+    untouched = np.setdiff1d(np.arange(rows.shape[0]), slots64[keep])
+    assert not np.any(rows[untouched]), "rows outside the slot mapping were written"
+
+
+@pytest.mark.parametrize("n", (1, 33, 300))
+def test_absorb_rows_without_rope_part(n):
+    rng = np.random.default_rng(6000 + n)
+    dims = mla.make_dims(N_H, D_C, D_H, 0, D_V, 1024, 64, "bf16", "bf16")
+    q_nope, qn64 = _bf16(rng, (n, N_H, D_H))
+    w_uk, wuk64 = _bf16(rng, (N_H, D_H, D_C), 1.0 / np.sqrt(D_H))
+    pos = torch.zeros(n, dtype=torch.int32, device="cuda")
+    q_lat = torch.empty(n, N_H, D_C, dtype=torch.bfloat16, device="cuda")
+    mla.absorb_q(dims, q_nope, None, w_uk, pos, q_lat)
+    torch.cuda.synchronize()
+    want = ref.absorb_q(qn64, np.zeros((n, N_H, 0)), np.zeros(n), wuk64)
+    assert _rel_err(_host_bf16(q_lat), want) <= TOL["bf16"]
