@@ -189,6 +189,26 @@ mla_status_t mla_absorb_q(const mla_dims_t* dims, const void* q_nope, const void
                           void* q_lat, float* q_scale, void* workspace, size_t workspace_bytes,
                           mla_stream_t stream);
 
+/* ------------------------------------------------------- append + absorb
+ * mla_append_latent and mla_absorb_q in one call, for a step whose new
+ * tokens are also its queries [V2 summary, "推論方法" (inference) section:
+ * both read the step's new tokens].  On the MFMA path (with w_dkv_kr) the
+ * append's down-projection and the latent query run as one launch, each
+ * workgroup streaming one of the two weights; the append's finish (and for
+ * an fp8 cache the query's quantisation) follows.  Otherwise the two calls
+ * run in order.  Arguments as for the two calls (q_positions, n_q_tokens,
+ * q_nope, q_pe, w_uk, q_lat, q_scale are mla_absorb_q's positions,
+ * n_tokens, ...); one workspace of at least
+ * mla_append_absorb_workspace_size() bytes serves both. */
+size_t mla_append_absorb_workspace_size(const mla_dims_t* dims, int32_t n_tokens, int32_t n_q_tokens);
+mla_status_t mla_append_absorb(const mla_dims_t* dims, const void* hidden, const void* w_dkv_kr,
+                               const float* rms_gamma, const int32_t* positions,
+                               const int64_t* slot_mapping, int32_t n_tokens, int64_t cache_slots,
+                               void* cache, float* cache_scale, const void* q_nope, const void* q_pe,
+                               const void* w_uk, const int32_t* q_positions, int32_t n_q_tokens,
+                               void* q_lat, float* q_scale, void* workspace, size_t workspace_bytes,
+                               mla_stream_t stream);
+
 /* --------------------------------------------------------------- decode
  * Attention over the latent cache with the absorbed query; all heads share
  * the rows (MQA with head width d_c + d_R whose value is the latent part,

@@ -23,6 +23,7 @@ STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARGUMENT", 2: "MLA_ERR_UNSUPPORTED",
 # every entry point declared in include/mla.h
 EXPORTS = ("mla_cache_row_bytes", "mla_cache_bytes_per_token", "mla_q_lat_row_bytes",
            "mla_append_workspace_size", "mla_append_latent", "mla_absorb_workspace_size", "mla_absorb_q",
+           "mla_append_absorb_workspace_size", "mla_append_absorb",
            "mla_decode_plan_workspace_size", "mla_decode_plan", "mla_decode_plan_host", "mla_decode",
            "mla_decode_uniform_workspace_size", "mla_decode_uniform", "mla_decode_uniform_noalloc",
            "mla_decode_default_split",
@@ -82,6 +83,8 @@ def lib():
         "mla_append_workspace_size": (SZ, [DP, I32]),
         "mla_append_latent": (I32, [DP, P, P, P, P, P, I32, I64, P, P, P, SZ, P]),
         "mla_absorb_workspace_size": (SZ, [DP, I32]),
+        "mla_append_absorb_workspace_size": (SZ, [DP, I32, I32]),
+        "mla_append_absorb": (I32, [DP, P, P, P, P, P, I32, I64, P, P, P, P, P, P, I32, P, P, P, SZ, P]),
         "mla_absorb_q": (I32, [DP, P, P, P, P, I32, P, P, P, SZ, P]),
         "mla_decode_plan_workspace_size": (SZ, [DP, P, I32, I32, I32]),
         "mla_decode_plan": (I32, [DP, P, I32, I32, I32, PP, P, SZ, P]),
@@ -169,6 +172,21 @@ def _host_lens(seq_lens):
     if isinstance(seq_lens, torch.Tensor):
         seq_lens = seq_lens.detach().cpu().numpy()
     return np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+
+
+def append_absorb(dims, hidden, w_dkv_kr, gamma, positions, slot_mapping, cache, cache_scale, q_nope, q_pe, w_uk,
+                  q_positions, q_lat, q_scale=None, workspace=None):
+    """mla_append_absorb: append_latent and absorb_q in one call."""
+    n, nq = positions.numel(), q_nope.shape[0]
+    need = lib().mla_append_absorb_workspace_size(ctypes.byref(dims), n, nq)
+    if workspace is None:
+        workspace, _ = _workspace(need, cache.device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    slots = cache.shape[0] * cache.shape[1]
+    _check(lib().mla_append_absorb(ctypes.byref(dims), _ptr(hidden), _ptr(w_dkv_kr), _ptr(gamma), _ptr(positions),
+                                   _ptr(slot_mapping), n, slots, _ptr(cache), _ptr(cache_scale), _ptr(q_nope),
+                                   _ptr(q_pe), _ptr(w_uk), _ptr(q_positions), nq, _ptr(q_lat), _ptr(q_scale),
+                                   _ptr(workspace), nbytes, _stream(cache.device)))
 
 
 def decode_plan_workspace_size(dims, seq_lens_host, q_len, split_tokens=0):

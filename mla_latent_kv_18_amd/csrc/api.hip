@@ -260,6 +260,49 @@ mla_status_t mla_append_latent(const mla_dims_t* dims, const void* hidden, const
   return hip_status(r.mfma ? mla::launch_append_mfma(a, s) : mla::launch_append_f32(a, s), "mla_append_latent");
 }
 
+size_t mla_append_absorb_workspace_size(const mla_dims_t* dims, int32_t n_tokens, int32_t n_q_tokens) {
+  const size_t a = (mla_append_workspace_size(dims, n_tokens) + 255) / 256 * 256;
+  return a + mla_absorb_workspace_size(dims, n_q_tokens);
+}
+
+mla_status_t mla_append_absorb(const mla_dims_t* dims, const void* hidden, const void* w_dkv_kr,
+                               const float* rms_gamma, const int32_t* positions, const int64_t* slot_mapping,
+                               int32_t n_tokens, int64_t cache_slots, void* cache, float* cache_scale,
+                               const void* q_nope, const void* q_pe, const void* w_uk,
+                               const int32_t* q_positions, int32_t n_q_tokens, void* q_lat, float* q_scale,
+                               void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+  Resolved r;
+  mla_status_t st = resolve(dims, &r);
+  if (st != MLA_OK) return st;
+  const size_t need = mla_append_absorb_workspace_size(dims, n_tokens, n_q_tokens);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "append + absorb needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  const size_t a_bytes = (mla_append_workspace_size(dims, n_tokens) + 255) / 256 * 256;
+  char* ws = static_cast<char*>(workspace);
+  void* q_ws = mla_absorb_workspace_size(dims, n_q_tokens) > 0 ? ws + a_bytes : nullptr;
+  // one fused launch on the MFMA path with both calls doing work; otherwise the two calls in order
+  if (!r.mfma || w_dkv_kr == nullptr || n_tokens <= 0 || n_q_tokens <= 0) {
+    st = mla_append_latent(dims, hidden, w_dkv_kr, rms_gamma, positions, slot_mapping, n_tokens, cache_slots, cache,
+                           cache_scale, workspace, a_bytes, stream);
+    if (st != MLA_OK) return st;
+    return mla_absorb_q(dims, q_nope, q_pe, w_uk, q_positions, n_q_tokens, q_lat, q_scale, q_ws,
+                        mla_absorb_workspace_size(dims, n_q_tokens), stream);
+  }
+  if (!hidden || !rms_gamma || !positions || !slot_mapping || !cache || !q_nope || !w_uk || !q_positions ||
+      !q_lat || (r.d_r > 0 && !q_pe))
+    return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  if (cache_slots <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "cache_slots must be positive");
+  if ((r.cache_dtype == MLA_FP8_E4M3 || r.cache_dtype == MLA_FP8_E4M3_KR_BF16) && !cache_scale)
+    return fail(MLA_ERR_INVALID_ARGUMENT, "fp8 cache needs cache_scale");
+  if (r.cache_dtype == MLA_FP8_E4M3 && !q_scale) return fail(MLA_ERR_INVALID_ARGUMENT, "fp8 needs q_scale");
+  mla::AppendArgs a{hidden, w_dkv_kr, rms_gamma, positions, slot_mapping, n_tokens, r.d_model, r.d_c,
+                    r.d_r, cache_slots, r.eps, r.theta, cache, cache_scale, workspace, r.cache_dtype};
+  mla::AbsorbArgs q{q_nope, q_pe, w_uk, q_positions, n_q_tokens, r.n_h, r.d_h, r.d_c, r.d_r, r.theta,
+                    q_lat, q_scale, q_ws, r.cache_dtype};
+  return hip_status(mla::launch_append_absorb_mfma(a, q, static_cast<hipStream_t>(stream)), "mla_append_absorb");
+}
+
 size_t mla_absorb_workspace_size(const mla_dims_t* dims, int32_t n_tokens) {
   Resolved r;
   if (resolve(dims, &r) != MLA_OK || n_tokens <= 0 || !r.mfma) return 0;

@@ -97,6 +97,8 @@ hipError_t launch_append_mfma(const AppendArgs&, hipStream_t);
 size_t absorb_mfma_workspace(int n_tokens, int n_h, int cache_dtype);
 hipError_t launch_absorb_q_mfma(const AbsorbArgs&, hipStream_t);
 hipError_t launch_out_proj_mfma(const OutProjArgs&, hipStream_t);
+// append (with its down-projection) and absorb q in one launch, then the finish
+hipError_t launch_append_absorb_mfma(const AppendArgs&, const AbsorbArgs&, hipStream_t);
 
 // latent decode, bf16 or fp8 cache (d_c = 512, d_r = 64)
 int decode_waves_per_group(int n_h, int q_len);

@@ -39,19 +39,21 @@ __device__ __forceinline__ bf16x8_t load8(const __bf16* p) { return *reinterpret
 // row groups re-read less of them.
 // partial[kc][n][r] = sum_{k in slice kc} h[n][k] * W[r][k]
 constexpr int kProjWaves = 4;
+constexpr int kAppendRTk = 1;  // 32-row tiles of W per append workgroup
+constexpr int kAppendMTk = 1;  // 32-token tiles per append pass
 constexpr int kKBatch = 8;  // k-steps per wave whose loads are in flight together
 
+// workgroup (bx, by, bz) of a (D / (32 RT), n_chunks, gz) grid
 template <int RT, int MT, int D>
-__global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restrict__ h,
-                                                          const __bf16* __restrict__ w, int n_tokens,
-                                                          int d_model, int chunk_len,
-                                                          float* __restrict__ partial) {
+__device__ __forceinline__ void append_proj_body(const __bf16* __restrict__ h, const __bf16* __restrict__ w,
+                                                 int n_tokens, int d_model, int chunk_len,
+                                                 float* __restrict__ partial, int bx, int by, int bz, int gz) {
   __shared__ f32x16_t red[kProjWaves][RT][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int r0 = blockIdx.x * 32 * RT, kc = blockIdx.y;
+  const int r0 = bx * 32 * RT, kc = by;
   const int ksteps = chunk_len / 16 / kProjWaves;  // per wave
   const int k_begin = kc * chunk_len + wave * ksteps * 16;
-  for (int m0 = blockIdx.z * 32 * MT; m0 < n_tokens; m0 += gridDim.z * 32 * MT) {
+  for (int m0 = bz * 32 * MT; m0 < n_tokens; m0 += gz * 32 * MT) {
     const int mts = min(MT, (n_tokens - m0 + 31) / 32);
     f32x16_t acc[RT][MT];
 #pragma unroll
@@ -105,6 +107,15 @@ __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restri
         }
     __syncthreads();
   }
+}
+
+template <int RT, int MT, int D>
+__global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restrict__ h,
+                                                          const __bf16* __restrict__ w, int n_tokens,
+                                                          int d_model, int chunk_len,
+                                                          float* __restrict__ partial) {
+  append_proj_body<RT, MT, D>(h, w, n_tokens, d_model, chunk_len, partial, blockIdx.x, blockIdx.y, blockIdx.z,
+                              gridDim.z);
 }
 
 constexpr int kMaxChunks = 16;  // contraction slices of the append GEMM
@@ -263,16 +274,14 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
 // with the weight slice, and that item's cos/sin are evaluated while they
 // are in flight; token rows past the end are clamped to the last row and
 // never stored.
+// workgroup (head, column tile ct) of an (n_h, d_c / 128) grid
 template <bool OUT_F32, int MT, int DR>
-__global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict__ q_nope,
-                                                       const __bf16* __restrict__ q_pe,
-                                                       const __bf16* __restrict__ w_uk,
-                                                       const int32_t* __restrict__ positions,
-                                                       int n_tokens, int n_h, RopeTable64 rope,
-                                                       void* __restrict__ q_out) {
+__device__ __forceinline__ void absorb_q_body(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_pe,
+                                              const __bf16* __restrict__ w_uk,
+                                              const int32_t* __restrict__ positions, int n_tokens, int n_h,
+                                              const RopeTable64& rope, void* __restrict__ q_out, int head, int ct) {
   __shared__ __attribute__((aligned(16))) char wl[kDh * 256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int head = blockIdx.x, ct = blockIdx.y;
   const __bf16* W = w_uk + static_cast<int64_t>(head) * kDh * kDc + ct * 128;
   // the first RoPE item's inputs are requested first, so that its rotation
   // only waits for them
@@ -368,6 +377,47 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
       static_cast<__bf16*>(q_out)[base] = f32_to_bf16(y1);
       static_cast<__bf16*>(q_out)[base + 32] = f32_to_bf16(y2);
     }
+  }
+}
+
+template <bool OUT_F32, int MT, int DR>
+__global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict__ q_nope,
+                                                       const __bf16* __restrict__ q_pe,
+                                                       const __bf16* __restrict__ w_uk,
+                                                       const int32_t* __restrict__ positions,
+                                                       int n_tokens, int n_h, RopeTable64 rope,
+                                                       void* __restrict__ q_out) {
+  absorb_q_body<OUT_F32, MT, DR>(q_nope, q_pe, w_uk, positions, n_tokens, n_h, rope, q_out, blockIdx.x, blockIdx.y);
+}
+
+// The append's down-projection and the latent query in one launch: the first
+// n_append workgroups take the append GEMM's (x, y, z) grid, the rest the
+// absorb grid (n_h, d_c / 128).  Both stream their own weights (W_dkv_kr,
+// W^UK), so together they keep more of HBM busy than either alone.
+struct AppendAbsorbArgs {
+  const __bf16* h;
+  const __bf16* w;
+  int n_tokens, d_model, chunk_len;
+  float* partial;
+  int ax, ay, az;  // append grid
+  const __bf16* q_nope;
+  const __bf16* q_pe;
+  const __bf16* w_uk;
+  const int32_t* positions;
+  int n_q, n_h;
+  void* q_out;
+};
+
+template <int D, bool OUT_F32, int MT_Q, int DR>
+__global__ void __launch_bounds__(256) append_absorb_kernel(AppendAbsorbArgs a, RopeTable64 rope) {
+  const int id = blockIdx.x, n_append = a.ax * a.ay * a.az;
+  if (id < n_append) {
+    append_proj_body<kAppendRTk, kAppendMTk, D>(a.h, a.w, a.n_tokens, a.d_model, a.chunk_len, a.partial,
+                                                 id % a.ax, (id / a.ax) % a.ay, id / (a.ax * a.ay), a.az);
+  } else {
+    const int j = id - n_append, ct_tiles = kDc / 128;
+    absorb_q_body<OUT_F32, MT_Q, DR>(a.q_nope, a.q_pe, a.w_uk, a.positions, a.n_q, a.n_h, rope, a.q_out,
+                                     j / ct_tiles, j % ct_tiles);
   }
 }
 
@@ -498,8 +548,8 @@ int append_chunks(int d_model) {
 // workgroup loops over several.  (For absorb and out proj a second token
 // workgroup would re-read the same weight slice: they keep one workgroup per
 // slice and hold up to two token tiles per pass.)
-constexpr int kAppendMT = 1;
-constexpr int kAppendRT = 1;  // 32-row tiles of W per append workgroup (a divisor of 576 / 32 = 18)
+constexpr int kAppendMT = kAppendMTk;
+constexpr int kAppendRT = kAppendRTk;  // 32-row tiles of W per append workgroup (a divisor of 576 / 32 = 18)
 constexpr int kOutVT = 1;    // 32-row tiles of W^UV_i per out-proj workgroup (a divisor of d_v / 32)
 constexpr int kMaxZ = 16;
 int token_groups(int n_tokens, int mt) {
@@ -517,6 +567,21 @@ RopeTable64 rope_table(float theta) {
 
 size_t append_mfma_workspace(int n_tokens) {
   return static_cast<size_t>(16) * n_tokens * kD * sizeof(float);
+}
+
+template <int D>
+hipError_t launch_append_finish(const AppendArgs& a, const float* partial, int n_chunks, hipStream_t st) {
+  auto finish = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(a.n_tokens), dim3(256), 0, st, partial, n_chunks, a.n_tokens, a.gamma,
+                       a.positions, a.slots, a.cache_slots, a.eps, rope_table(a.theta), a.cache, a.cache_scale);
+  };
+  switch (a.cache_dtype) {
+    case 2: finish(append_finish_kernel<D, kOutFp8>); break;
+    case 3: finish(append_finish_kernel<D, kOutFp4>); break;
+    case 4: finish(append_finish_kernel<D, kOutFp8Kr>); break;
+    default: finish(append_finish_kernel<D, kOutBf16>); break;
+  }
+  return hipGetLastError();
 }
 
 template <int D>
@@ -538,17 +603,7 @@ hipError_t launch_append_d(const AppendArgs& a, hipStream_t st) {
     n_chunks = 1;
     partial = static_cast<const float*>(a.hidden);
   }
-  auto finish = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(a.n_tokens), dim3(256), 0, st, partial, n_chunks, a.n_tokens, a.gamma,
-                       a.positions, a.slots, a.cache_slots, a.eps, rope_table(a.theta), a.cache, a.cache_scale);
-  };
-  switch (a.cache_dtype) {
-    case 2: finish(append_finish_kernel<D, kOutFp8>); break;
-    case 3: finish(append_finish_kernel<D, kOutFp4>); break;
-    case 4: finish(append_finish_kernel<D, kOutFp8Kr>); break;
-    default: finish(append_finish_kernel<D, kOutBf16>); break;
-  }
-  return hipGetLastError();
+  return launch_append_finish<D>(a, partial, n_chunks, st);
 }
 
 hipError_t launch_append_mfma(const AppendArgs& a, hipStream_t st) {
@@ -584,6 +639,52 @@ hipError_t launch_absorb_q_mfma(const AbsorbArgs& a, hipStream_t st) {
                        rope_table(a.theta), a.q_lat);
   }
   return hipGetLastError();
+}
+
+// The down-projection of the append and the latent query in one launch,
+// then the append's finish (and, for an fp8 cache, the query's quantisation).
+template <int D, int DR>
+hipError_t launch_append_absorb_d(const AppendArgs& a, const AbsorbArgs& q, hipStream_t st) {
+  const int n_chunks = append_chunks(a.d_model);
+  AppendAbsorbArgs g;
+  g.h = static_cast<const __bf16*>(a.hidden);
+  g.w = static_cast<const __bf16*>(a.w);
+  g.n_tokens = a.n_tokens;
+  g.d_model = a.d_model;
+  g.chunk_len = a.d_model / n_chunks;
+  g.partial = static_cast<float*>(a.workspace);
+  g.ax = D / (32 * kAppendRT);
+  g.ay = n_chunks;
+  g.az = token_groups(a.n_tokens, kAppendMT);
+  g.q_nope = static_cast<const __bf16*>(q.q_nope);
+  g.q_pe = static_cast<const __bf16*>(q.q_pe);
+  g.w_uk = static_cast<const __bf16*>(q.w_uk);
+  g.positions = q.positions;
+  g.n_q = q.n_tokens;
+  g.n_h = q.n_h;
+  const bool fp8 = q.cache_dtype == 2;
+  g.q_out = fp8 ? q.workspace : q.q_lat;
+  const dim3 grid(g.ax * g.ay * g.az + q.n_h * (kDc / 128));
+  const RopeTable64 rope = rope_table(q.theta);
+  const bool one = q.n_tokens <= 32;
+  if (fp8) {
+    auto kern = one ? append_absorb_kernel<D, true, 1, DR> : append_absorb_kernel<D, true, 2, DR>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, g, rope);
+  } else {
+    auto kern = one ? append_absorb_kernel<D, false, 1, DR> : append_absorb_kernel<D, false, 2, DR>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, g, rope);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_append_finish<D>(a, g.partial, n_chunks, st);
+  if (e != hipSuccess || !fp8) return e;
+  hipLaunchKernelGGL(quantize_rows_fp8_kernel, dim3(q.n_tokens * q.n_h), dim3(64), 0, st,
+                     static_cast<const float*>(q.workspace), static_cast<uint8_t*>(q.q_lat), q.q_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_absorb_mfma(const AppendArgs& a, const AbsorbArgs& q, hipStream_t st) {
+  return a.d_r == 0 ? launch_append_absorb_d<kDc, 0>(a, q, st) : launch_append_absorb_d<kD, kDr>(a, q, st);
 }
 
 hipError_t launch_out_proj_mfma(const OutProjArgs& a, hipStream_t st) {

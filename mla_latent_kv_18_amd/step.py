@@ -11,7 +11,7 @@ import ctypes
 import numpy as np
 import torch
 
-from . import (absorb_output_weights, absorb_q, absorb_query_weights, append_latent, decode, decode_plan,
+from . import (absorb_output_weights, absorb_q, absorb_query_weights, append_absorb, append_latent, decode, decode_plan,
                decode_uniform, decode_uniform_workspace_size, lib, linear, linear_workspace_size, make_dims,
                out_proj)
 
@@ -24,7 +24,10 @@ def _dev(a, device, fmt):
 
 
 class DeviceStep:
-    def __init__(self, gen, device="cuda:0", split_tokens=0, mode="planned"):
+    """fused: run() appends and absorbs with one mla_append_absorb call
+    (else mla_append_latent then mla_absorb_q)."""
+
+    def __init__(self, gen, device="cuda:0", split_tokens=0, mode="planned", fused=True):
         w = gen["workload"]
         self.w = w
         self.device = device
@@ -67,6 +70,9 @@ class DeviceStep:
                                      dtype=torch.uint8, device=device)
         self.absorb_ws = torch.empty(max(lib().mla_absorb_workspace_size(ctypes.byref(self.dims), N), 1),
                                      dtype=torch.uint8, device=device)
+        self.fused = fused
+        self.fused_ws = torch.empty(max(lib().mla_append_absorb_workspace_size(ctypes.byref(self.dims), n_new, N), 1),
+                                    dtype=torch.uint8, device=device)
 
     def append(self):
         append_latent(self.dims, self.h, self.w_dkv_kr, self.gamma, self.new_pos, self.slots,
@@ -97,9 +103,17 @@ class DeviceStep:
     def out_proj(self):
         out_proj(self.dims, self.o_lat, self.w_uv, self.out)
 
+    def append_and_absorb(self):
+        append_absorb(self.dims, self.h, self.w_dkv_kr, self.gamma, self.new_pos, self.slots, self.cache,
+                      self.cache_scale, self.q_nope, self.q_pe, self.w_uk, self.q_pos, self.q_lat, self.q_scale,
+                      workspace=self.fused_ws)
+
     def run(self):
-        self.append()
-        self.absorb()
+        if self.fused:
+            self.append_and_absorb()
+        else:
+            self.append()
+            self.absorb()
         self.decode()
         self.out_proj()
 

@@ -425,3 +425,30 @@ def test_peaked_logits_take_the_second_pass(case, score, split_tokens, mode):
     top = max(check_decode_call(step, gen, b, ov.TOL[w.dtype]) for b in range(w.batch))
     # the planted keys dominate: far above the unit-variance logits of the rest
     assert top > 0.9 * score
+
+
+@pytest.mark.parametrize("base,over", [
+    ("v3_bs64_ctx4k", dict(batch=3, lens=(1, 100, 257), shuffle=True)),
+    ("v3_fp8_bs4_ctx128k_q2", dict(batch=2, lens=(64, 130))),
+    ("v3_fp4_bs64_ctx4k", dict(n_h=64, batch=40, lens=tuple(range(10, 410, 10)))),
+    ("nope_bs64_ctx4k", dict(batch=2, lens=(70, 129), q_len=2)),
+    ("tiny_f32", dict()),
+])
+def test_fused_append_absorb_equals_the_two_calls(base, over):
+    """mla_append_absorb (one launch for the down-projection and the latent
+    query) writes the same cache rows and latent queries as the two calls."""
+    w = WORKLOADS[base].scaled(name="fused", seed=19, **over)
+    gen = generate(w)
+    a = DeviceStep(gen, fused=True)
+    b = DeviceStep(gen, fused=False)
+    a.run()
+    b.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a.cache, b.cache)
+    assert torch.equal(a.q_lat, b.q_lat)
+    if a.q_scale is not None:
+        assert torch.equal(a.q_scale, b.q_scale)
+    if a.cache_scale is not None:
+        assert torch.equal(a.cache_scale, b.cache_scale)
+    assert torch.equal(a.out, b.out)
+    check_request(a, gen, 0, list(range(w.n_h)), ov.TOL[w.dtype], 2e-2)
