@@ -16,7 +16,7 @@
 //   NoPE     d_R = 0: 512 bf16 latent values: 1024 B.
 //
 // Per 32-token tile: the stored rows arrive by direct global->LDS copies
-// into a staging buffer (three in flight), are expanded into a bf16 tile
+// into a staging buffer (three slots), are expanded into a bf16 tile
 // (the swizzled layout of decode_mfma.hip: chunk c of row t at t * D/8 +
 // (c ^ f(t))), and every wave then scores its 32 heads against the tile
 // (S^T = K Q^T, Q register resident), takes the softmax numerators with a
@@ -102,7 +102,9 @@ decode_dq_kernel(DqParams p) {
   using F = DqFmt<FMT>;
   constexpr int D = G::D, kChunks = G::kChunks, kKSteps = D / 16;
   __shared__ __attribute__((aligned(1024))) char lds_raw[G::kLds];
+  __shared__ float token_scales_raw[2 * kTileT];  // per bf16 buffer (formats with a token scale)
   __shared__ int second_pass;
+  MLA_LDS float* token_scales = (MLA_LDS float*)token_scales_raw;
   MLA_LDS char* lds = (MLA_LDS char*)lds_raw;
   const uint32_t lds_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   const int tid = threadIdx.x, lane = tid & 63;
@@ -204,6 +206,8 @@ decode_dq_kernel(DqParams p) {
   auto expand = [&](int slot, int dst) {
     MLA_LDS const char* st = lds + G::kNTile * G::kTileBytes + slot * G::kStageBytes;
     MLA_LDS char* tile = lds + dst * G::kTileBytes;
+    if (F::kScale && tid < kTileT)  // the tile's token scales move with it: the staging slot is refilled early
+      token_scales[32 * dst + tid] = *reinterpret_cast<const MLA_LDS float*>(st + G::kCopies * WAVES * 1024 + 4 * tid);
     constexpr int kPer = kTileT * kChunks / (WAVES * 64);
 #pragma unroll 3
     for (int j = 0; j < kPer; ++j) {
@@ -324,21 +328,33 @@ decode_dq_kernel(DqParams p) {
         compute(lds + (k % 3) * G::kTileBytes, nullptr, k, flagged);
       }
     } else {
+      // Software pipelined by one tile: step k expands tile k+1 (VALU and
+      // LDS work) in the same block as it scores and sums tile k (MFMA), so
+      // the two can overlap.  Stored tile j sits in staging slot j % 3, its
+      // expansion in bf16 buffer j & 1.
       if (n_tiles > 0) issue(0, 0);
       if (n_tiles > 1) issue(1, 1);
-      for (int k = 0; k < n_tiles; ++k) {
-        if (k + 1 < n_tiles) wait_vmcnt<G::kWaveCopies>();
+      if (n_tiles > 0) {
+        if (n_tiles > 1) wait_vmcnt<G::kWaveCopies>();
         else wait_vmcnt<0>();
-        // staging k visible to all; every wave is done expanding tile k-1 and
-        // computing tile k-2, whose bf16 buffer tile k reuses
-        __builtin_amdgcn_s_barrier();
-        if (k + 2 < n_tiles) issue(k + 2, (k + 2) % 3);
-        expand(k % 3, k & 1);
-        __syncthreads();  // the expanded tile is visible to all
-        compute(lds + (k & 1) * G::kTileBytes,
-                reinterpret_cast<MLA_LDS const float*>(lds + G::kNTile * G::kTileBytes + (k % 3) * G::kStageBytes +
-                                                       G::kCopies * WAVES * 1024),
-                k, flagged);
+        __builtin_amdgcn_s_barrier();  // stored tile 0 visible to all
+        if (n_tiles > 2) issue(2, 2);
+        expand(0, 0);
+        __syncthreads();  // expanded tile 0 visible to all
+      }
+      for (int k = 0; k < n_tiles; ++k) {
+        if (k + 1 < n_tiles) {
+          if (k + 2 < n_tiles) wait_vmcnt<G::kWaveCopies>();
+          else wait_vmcnt<0>();
+          // stored tile k+1 visible to all; every wave is done expanding tile
+          // k (its staging slot is free) and computing tile k-1 (its bf16
+          // buffer is free for tile k+1)
+          __builtin_amdgcn_s_barrier();
+          if (k + 3 < n_tiles) issue(k + 3, k % 3);
+          expand((k + 1) % 3, (k + 1) & 1);
+        }
+        compute(lds + (k & 1) * G::kTileBytes, token_scales + 32 * (k & 1), k, flagged);
+        __syncthreads();  // expanded tile k+1 visible to all; tile k released
       }
     }
     return flagged;
