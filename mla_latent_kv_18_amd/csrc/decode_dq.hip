@@ -80,6 +80,25 @@ __device__ __forceinline__ int swz(int t) {
   return u ^ ((u & 1) << 2);
 }
 
+// eight E2M1 codes (element 2i in the low nibble of byte i) times 2^(e - 127)
+__device__ __forceinline__ bf16x8_t fp4_word_to_bf16(uint32_t w, uint32_t e) {
+  const float sc = __uint_as_float(e << 23);
+  const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  return bf16x8_t{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+// eight e4m3 codes, unscaled (exact in bf16)
+__device__ __forceinline__ bf16x8_t fp8_pair_to_bf16(i32x2_t w) {
+  const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false);
+  const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true);
+  const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false);
+  const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true);
+  return bf16x8_t{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
 template <int FMT, int WAVES>
 struct DqGeom {
   using F = DqFmt<FMT>;
@@ -202,42 +221,54 @@ decode_dq_kernel(DqParams p) {
   };
 
   // expand staging buffer `slot` into bf16 tile `dst`: chunk (t, c) = bf16
-  // elements 8c .. 8c+7 of row t
+  // elements 8c .. 8c+7 of row t.  Wave w expands rows R w .. R w + R-1: for
+  // each of them lane l does latent chunk l (one stored word or pair, one
+  // 16-byte store), then the rows' last eight chunks (the RoPE part) go eight
+  // lanes to a row.  Row offsets are compile-time immediates; only the
+  // swizzle term changes per row, and it is wave-uniform.
+  constexpr int R = kTileT / WAVES;
+  const int wrow0 = R * wave;
+  const int xl = lane << 4;
+  int tail_src[R / 8], tail_dst[R / 8];  // per-lane offsets of the tail chunks
+#pragma unroll
+  for (int i = 0; i < R / 8; ++i) {
+    const int r = 8 * i + (lane >> 3), c = kDc / 8 + (lane & 7);
+    tail_src[i] = r * F::kRowBytes + (FMT == kDqFp4Mx ? 4 * c : kDc + 16 * (lane & 7));
+    tail_dst[i] = (r * kChunks + (c ^ swz(wrow0 + r))) * 16;
+  }
   auto expand = [&](int slot, int dst) {
     MLA_LDS const char* st = lds + G::kNTile * G::kTileBytes + slot * G::kStageBytes;
     MLA_LDS char* tile = lds + dst * G::kTileBytes;
     if (F::kScale && tid < kTileT)  // the tile's token scales move with it: the staging slot is refilled early
       token_scales[32 * dst + tid] = *reinterpret_cast<const MLA_LDS float*>(st + G::kCopies * WAVES * 1024 + 4 * tid);
-    constexpr int kPer = kTileT * kChunks / (WAVES * 64);
-#pragma unroll 3
-    for (int j = 0; j < kPer; ++j) {
-      const int id = tid + WAVES * 64 * j;
-      const int t = id / kChunks, c = id - t * kChunks;
+    MLA_LDS const char* sw = st + wrow0 * F::kRowBytes;
+    MLA_LDS char* tw = tile + wrow0 * kChunks * 16;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int f = swz(wrow0 + j) << 4;  // wave-uniform
       bf16x8_t v;
       if constexpr (FMT == kDqFp4Mx) {
-        const MLA_LDS char* row = st + t * F::kRowBytes;
-        const uint32_t w = *reinterpret_cast<const MLA_LDS uint32_t*>(row + 4 * c);
-        const uint32_t e = *reinterpret_cast<const MLA_LDS uint8_t*>(row + D / 2 + (c >> 2));
-        const float sc = __uint_as_float(e << 23);  // 2^(e - 127)
-        const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
-        const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
-        const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
-        const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
-        v = bf16x8_t{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+        const uint32_t w = *reinterpret_cast<const MLA_LDS uint32_t*>(sw + j * F::kRowBytes + 4 * lane);
+        const uint32_t e = *reinterpret_cast<const MLA_LDS uint8_t*>(sw + j * F::kRowBytes + D / 2 + (lane >> 2));
+        v = fp4_word_to_bf16(w, e);
       } else {
-        const MLA_LDS char* row = st + t * F::kRowBytes;
-        if (c < kDc / 8) {
-          const i32x2_t w = *reinterpret_cast<const MLA_LDS i32x2_t*>(row + 8 * c);
-          const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, false);
-          const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.f, true);
-          const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, false);
-          const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.f, true);
-          v = bf16x8_t{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-        } else {
-          v = *reinterpret_cast<const MLA_LDS bf16x8_t*>(row + kDc + 16 * (c - kDc / 8));
-        }
+        const i32x2_t w = *reinterpret_cast<const MLA_LDS i32x2_t*>(sw + j * F::kRowBytes + 8 * lane);
+        v = fp8_pair_to_bf16(w);
       }
-      *reinterpret_cast<MLA_LDS bf16x8_t*>(tile + (t * kChunks + (c ^ swz(t))) * 16) = v;
+      *reinterpret_cast<MLA_LDS bf16x8_t*>(tw + j * kChunks * 16 + (xl ^ f)) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < R / 8; ++i) {
+      bf16x8_t v;
+      if constexpr (FMT == kDqFp4Mx) {
+        const uint32_t w = *reinterpret_cast<const MLA_LDS uint32_t*>(sw + tail_src[i]);
+        const uint32_t e = *reinterpret_cast<const MLA_LDS uint8_t*>(
+            sw + (8 * i + (lane >> 3)) * F::kRowBytes + D / 2 + (kDc / 8 + (lane & 7)) / 4);
+        v = fp4_word_to_bf16(w, e);
+      } else {
+        v = *reinterpret_cast<const MLA_LDS bf16x8_t*>(sw + tail_src[i]);
+      }
+      *reinterpret_cast<MLA_LDS bf16x8_t*>(tw + tail_dst[i]) = v;
     }
   };
 
@@ -409,6 +440,7 @@ hipError_t launch_dq(const DqParams& p, dim3 grid, int waves, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode_dq(const DecodeArgs& a, int fmt, hipStream_t st) {
+  if (fmt != kDqFp8Kr && decode_pipe_supported(a.n_h, a.q_len)) return launch_decode_pipe(a, fmt, st);
   DqParams p;
   p.q_lat = static_cast<const __bf16*>(a.q_lat);
   p.cache = static_cast<const uint8_t*>(a.cache);

@@ -309,16 +309,43 @@ decode_bf16_kernel(DecodeParams p) {
 // and two P^T buffers.  The softmax is that of the kernel above; the scores
 // are summed in a different order (two chains), so results agree to fp32
 // rounding of the scores rather than bit for bit.
-constexpr int kPipeBufs = 4;
-constexpr int kPipeCopies = kLoadsPerTile / 4;  // 9 copies per wave per tile
-constexpr int kPBytes = kTileT * 128 * 2;        // P^T of one tile, all heads, bf16
+// The same stream serves two more row formats (PipeFmt):
+//   kPipeNope  512-wide bf16 rows (MLA without the decoupled RoPE part):
+//              32 query fragments, 32 KB tiles, eight copies per wave;
+//   kPipeFp4   576 E2M1 codes + 18 E8M0 block scales per row (320 bytes):
+//              each wave copies its eight stored rows of tile k+4 into a
+//              staging slot, and step k's stream expands its rows of tile
+//              k+2 into the bf16 tile layout between the weighted-sum MFMAs
+//              (E2M1 times a power of two is exact in bf16).  LDS: three tile
+//              buffers, two P^T buffers, three staging slots.
+enum { kPipeBf16 = 0, kPipeNope = 1, kPipeFp4 = 2 };
+constexpr int kPBytes = kTileT * 128 * 2;  // P^T of one tile, all heads, bf16
+
+template <int PF>
+struct PipeGeo {
+  static constexpr int D = PF == kPipeNope ? 512 : 576;
+  static constexpr int kNk = D / 16;                    // query fragments
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks of a tile row
+  static constexpr int kTileBytes = kTileT * D * 2;
+  static constexpr int kCopies = kTileBytes / 1024 / 4;  // direct copies per wave and tile
+  static constexpr bool kExpand = PF == kPipeFp4;
+  static constexpr int kRowBytes = kExpand ? 320 : D * 2;  // stored bytes per cache row
+  static constexpr int kBufs = kExpand ? 3 : 4;
+  static constexpr int kStageWave = 3072;               // a wave's 8 stored rows (2560 B) + pad
+  static constexpr int kStageBytes = 4 * kStageWave;
+  static constexpr int kRawCopies = 3;
+  static constexpr int kTiles = kBufs * kTileBytes;
+  static constexpr int kLds = kTiles + 2 * kPBytes + (kExpand ? 3 * kStageBytes : 0);
+  static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(4 * kTileBytes <= kLds, "query staging");
+};
 
 #define MLA_ASM_ACC                                                                          \
   [o0] "+a"(oacc[0]), [o1] "+a"(oacc[1]), [o2] "+a"(oacc[2]), [o3] "+a"(oacc[3]),            \
       [o4] "+a"(oacc[4]), [o5] "+a"(oacc[5]), [o6] "+a"(oacc[6]), [o7] "+a"(oacc[7]),        \
       [o8] "+a"(oacc[8]), [o9] "+a"(oacc[9]), [o10] "+a"(oacc[10]), [o11] "+a"(oacc[11]),    \
       [o12] "+a"(oacc[12]), [o13] "+a"(oacc[13]), [o14] "+a"(oacc[14]), [o15] "+a"(oacc[15])
-#define MLA_ASM_Q                                                                            \
+#define MLA_ASM_Q32                                                                          \
   [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),       \
       [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),   \
       [q10] "v"(qf[10]), [q11] "v"(qf[11]), [q12] "v"(qf[12]), [q13] "v"(qf[13]),            \
@@ -326,16 +353,17 @@ constexpr int kPBytes = kTileT * 128 * 2;        // P^T of one tile, all heads, 
       [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]),            \
       [q22] "v"(qf[22]), [q23] "v"(qf[23]), [q24] "v"(qf[24]), [q25] "v"(qf[25]),            \
       [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]),            \
-      [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]),            \
-      [q34] "v"(qf[34]), [q35] "v"(qf[35])
+      [q30] "v"(qf[30]), [q31] "v"(qf[31])
+#define MLA_ASM_Q MLA_ASM_Q32, [q32] "v"(qf[32]), [q33] "v"(qf[33]), [q34] "v"(qf[34]), [q35] "v"(qf[35])
 #define MLA_ASM_KEYS [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [bk] "s"(bk)
 #define MLA_ASM_VALUES \
   [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [bv] "s"(bv), [bp] "s"(bp)
 #define MLA_ASM_SOFTMAX_STATE [mref] "+v"(m_ref), [mseen] "+v"(m_seen), [lrun] "+v"(l_run), [exc] "+v"(excess)
 #define MLA_ASM_SOFTMAX_IN [scale] "s"(p.scale_log2), [bpw] "s"(bpw), [vlim] "v"(vlim), [tok] "s"(tok), [pa] "v"(pa)
 #define MLA_ASM_COPY                                                                     \
-  [cb] "s"(cb), [cd] "s"(cd), [cl] "s"(cl), [k1152] "s"(kD * 2), [c0] "v"(cpk[0]),            \
+  [cb] "s"(cb), [cd] "s"(cd), [cl] "s"(cl), [k1152] "s"(G::D * 2), [c0] "v"(cpk[0]),          \
       [c1] "v"(cpk[1]), [c2] "v"(cpk[2]), [c3] "v"(cpk[3]), [c4] "v"(cpk[4])
+#define MLA_ASM_EXPAND [xs] "s"(xs), [xt] "s"(xt), [xw] "s"(xw), [xtl0] "v"(xtl0), [xtl1] "v"(xtl1)
 #define MLA_ASM_SCRATCH MLA_BF16_ASM_SCRATCH, "memory", "m0", "scc", "vcc"
 
 #include "decode_bf16_asm.inc"
@@ -351,14 +379,27 @@ __device__ __forceinline__ void xcd_slot(int& b, int& unit) {
   unit = pos % gridDim.x;
 }
 
+// Eight E2M1 codes (element 2i in the low nibble of byte i) times 2^(e - 127).
+__device__ __forceinline__ bf16x8_t fp4_word_to_bf16(uint32_t w, uint32_t e) {
+  const float sc = __uint_as_float(e << 23);
+  const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  return bf16x8_t{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+template <int PF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-decode_bf16_pipe_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char tiles_raw[kPipeBufs * kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char pbuf_raw[2 * kPBytes];
-  MLA_LDS char* tiles = (MLA_LDS char*)tiles_raw;
-  MLA_LDS char* pbuf = (MLA_LDS char*)pbuf_raw;
+decode_pipe_kernel(DecodeParams p) {
+  using G = PipeGeo<PF>;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[G::kLds];
+  MLA_LDS char* tiles = (MLA_LDS char*)lds_raw;
+  MLA_LDS char* pbuf = tiles + G::kTiles;
   const uint32_t tiles_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles));
-  const uint32_t pbuf_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(pbuf));
+  const uint32_t pbuf_addr = tiles_addr + G::kTiles;
+  const uint32_t stage_addr = pbuf_addr + 2 * kPBytes;
+  (void)pbuf;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;
@@ -389,12 +430,12 @@ decode_bf16_pipe_kernel(DecodeParams p) {
   // per-lane LDS byte offsets of the key fragments (chunk 2s + hf of row
   // tq, four offsets cycling with s) and of the transposed value fragments
   // of column tile 4*wave ([h2][column parity]; column tile 4*wave + j adds
-  // (j >> 1) * 128 B and the second 16-token k-step 16 rows = 18432 B)
+  // (j >> 1) * 128 B and the second 16-token k-step 16 rows = 16 * D * 2 B)
   const int tq = lane & 31;
   const int fq = swz(tq);
   int ka[4], va[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ka[q] = (tq * kChunks + (((2 * q) | hf) ^ fq)) * 16;
+  for (int q = 0; q < 4; ++q) ka[q] = (tq * G::kChunks + (((2 * q) | hf) ^ fq)) * 16;
   {
     const int L = lane & 15, cg = (lane >> 4) & 1;
 #pragma unroll
@@ -404,45 +445,87 @@ decode_bf16_pipe_kernel(DecodeParams p) {
 #pragma unroll
       for (int par = 0; par < 2; ++par) {
         const int x = 4 * par + 2 * cg + ((L & 3) >> 1);
-        va[2 * h2 + par] = (row * kChunks + (x ^ f)) * 16 + 8 * (L & 1) + 256 * wave;
+        va[2 * h2 + par] = (row * G::kChunks + (x ^ f)) * 16 + 8 * (L & 1) + 256 * wave;
       }
     }
   }
 
-  // Copy ii of this wave moves wave-wide load i = wave + 4*ii of a tile:
-  // lane -> (row t, swizzled 16-byte chunk c), packed as c*16 | t << 11 in
-  // the low (even ii) or high (odd ii) half of cpk[ii / 2].
-  uint32_t cpk[(kPipeCopies + 1) / 2] = {};
+  // Copy ii of this wave moves wave-wide load i = wave + 4*ii of a bf16
+  // tile: lane -> (row t, swizzled 16-byte chunk c), packed as c*16 | t << 11
+  // in the low (even ii) or high (odd ii) half of cpk[ii / 2].  The query
+  // rows are copied this way in every format.
+  uint32_t cpk[5] = {};
 #pragma unroll
-  for (int ii = 0; ii < kPipeCopies; ++ii) {
+  for (int ii = 0; ii < G::kCopies; ++ii) {
     const int slot = 64 * (wave + 4 * ii) + lane;
-    const int t = slot / kChunks;
-    const int c = (slot - t * kChunks) ^ swz(t);
+    const int t = slot / G::kChunks;
+    const int c = (slot - t * G::kChunks) ^ swz(t);
     cpk[ii / 2] |= (static_cast<uint32_t>(c * 16) | (static_cast<uint32_t>(t) << 11)) << (16 * (ii & 1));
   }
   const int64_t bt_row = static_cast<int64_t>(b) * p.max_blocks;
-  // block-table entry of tile k, and the first cache row of tile k given it
+  // block-table entry of tile k, and the first stored cache row of tile k given it
   auto block_of = [&](int k) { return block_table[bt_row + (j0 + k * kTileT) / p.block_size]; };
   auto base_from = [&](int blk, int k) -> const char* {
     const int tok0 = j0 + k * kTileT;
     blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
-    return reinterpret_cast<const char*>(p.cache + (static_cast<int64_t>(blk) * p.block_size + tok0 % p.block_size) * kD);
+    return reinterpret_cast<const char*>(p.cache) +
+           (static_cast<int64_t>(blk) * p.block_size + tok0 % p.block_size) * G::kRowBytes;
   };
   auto tile_base = [&](int k) { return base_from(block_of(k), k); };
   auto last_row = [&](int k) { return min(kTileT, T - (j0 + k * kTileT)) - 1; };
+  auto buf_addr = [&](int k) { return tiles_addr + (static_cast<uint32_t>(k) % G::kBufs) * G::kTileBytes; };
+  auto pbuf_addr_of = [&](int k) { return pbuf_addr + (k & 1) * kPBytes; };
+  // bf16 formats: the wave's copies of tile k straight into its tile buffer
   auto issue_tile = [&](int k) {
     const char* base = tile_base(k);
     const uint32_t last = static_cast<uint32_t>(last_row(k));
-    const uint32_t dst = tiles_addr + (k & (kPipeBufs - 1)) * kTileBytes;
+    const uint32_t dst = buf_addr(k);
 #pragma unroll
-    for (int ii = 0; ii < kPipeCopies; ++ii) {
+    for (int ii = 0; ii < G::kCopies; ++ii) {
       const uint32_t pk = cpk[ii / 2] >> (16 * (ii & 1));
       const uint32_t t = min((pk >> 11) & 31u, last);  // rows past the end repeat a valid row
-      dma16_sv(base, t * (kD * 2) + (pk & 2047u), dst + (wave + 4 * ii) * 1024);
+      dma16_sv(base, t * (G::D * 2) + (pk & 2047u), dst + (wave + 4 * ii) * 1024);
     }
   };
-  auto buf_addr = [&](int k) { return tiles_addr + (k & (kPipeBufs - 1)) * kTileBytes; };
-  auto pbuf_addr_of = [&](int k) { return pbuf_addr + (k & 1) * kPBytes; };
+  // FP4: the wave's stored rows 8w..8w+7 of tile k (2560 bytes) into its
+  // part of staging slot k % 3; byte offsets past them repeat the last chunk
+  auto issue_raw_at = [&](const char* base, int k) {
+    const int last = last_row(k);
+    const uint32_t dst = stage_addr + (k % 3) * G::kStageBytes + wave * G::kStageWave;
+#pragma unroll
+    for (int i = 0; i < G::kRawCopies; ++i) {
+      const int o = min(1024 * i + 16 * lane, 8 * 320 - 16);
+      const int r = o / 320;
+      const int t = min(8 * wave + r, last);
+      dma16_sv(base, static_cast<uint32_t>(t * 320 + (o - 320 * r)), dst + 1024 * i);
+    }
+  };
+  // FP4: expand the wave's rows of staged tile k into bf16 tile k (C++ form,
+  // for the first two tiles of a pass; the step stream does the rest)
+  auto expand_cpp = [&](int k) {
+    MLA_LDS const char* sw = tiles + (stage_addr - tiles_addr) + (k % 3) * G::kStageBytes + wave * G::kStageWave;
+    MLA_LDS char* tw = tiles + (static_cast<uint32_t>(k) % G::kBufs) * G::kTileBytes + 8 * wave * G::kChunks * 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = *reinterpret_cast<const MLA_LDS uint32_t*>(sw + 320 * j + 4 * lane);
+      const uint32_t e = *reinterpret_cast<const MLA_LDS uint8_t*>(sw + 320 * j + 288 + (lane >> 2));
+      *reinterpret_cast<MLA_LDS bf16x8_t*>(tw + j * 1152 + 16 * (lane ^ swz(8 * wave + j))) =
+          fp4_word_to_bf16(w, e);
+    }
+    const int r = lane >> 3, c = 64 + (lane & 7);
+    const uint32_t w = *reinterpret_cast<const MLA_LDS uint32_t*>(sw + 320 * r + 4 * c);
+    const uint32_t e = *reinterpret_cast<const MLA_LDS uint8_t*>(sw + 320 * r + 288 + (c >> 2));
+    *reinterpret_cast<MLA_LDS bf16x8_t*>(tw + r * 1152 + 16 * (c ^ swz(8 * wave + r))) = fp4_word_to_bf16(w, e);
+  };
+  // FP4 stream inputs: the rows' last eight chunks (code word | scale byte <<
+  // 16 in the staged rows; destination in the bf16 tile) and the swizzle term
+  // 64 * (wave & 1) that the wave's rows share
+  const uint32_t xtl0 = (320 * (lane >> 3) + 4 * (lane & 7)) | ((320 * (lane >> 3) + ((lane & 7) >> 2)) << 16);
+  const uint32_t xtl1 = 1152 * (lane >> 3) + 16 * ((64 + (lane & 7)) ^ swz(8 * wave + (lane >> 3)));
+  const uint32_t xw = 64 * (wave & 1);
+  (void)xtl0;
+  (void)xtl1;
+  (void)xw;
   const uint32_t pa = 16 * lane;
 
   constexpr float kSlack = 64.f;
@@ -453,36 +536,47 @@ decode_bf16_pipe_kernel(DecodeParams p) {
   const int vlim = vis_end - j0 - 4 * hf;
 
   // Latent queries.  The workgroup's 128 rows are contiguous in q_lat; they
-  // are copied with whole-kilobyte loads into the four tile buffers (32 rows
-  // each, in the tile layout) and each wave then reads its 36 fragments with
-  // the key-fragment addressing.  Loading them straight into registers would
-  // take one 32-byte piece from each of 32 rows per load instruction.
-  bf16x8_t qf[36];
+  // are copied with whole-kilobyte loads into the first four tile-sized
+  // areas of LDS (32 rows each, in the tile layout) and each wave then reads
+  // its fragments with the key-fragment addressing.  Loading them straight
+  // into registers would take one 32-byte piece from each of 32 rows per
+  // load instruction.
+  bf16x8_t qf[G::kNk];
   {
-    const char* qblk = reinterpret_cast<const char*>(p.q_lat + (static_cast<int64_t>(b) * rows_per_req + rg * 128) * kD);
+    const char* qblk =
+        reinterpret_cast<const char*>(p.q_lat + (static_cast<int64_t>(b) * rows_per_req + rg * 128) * G::D);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const char* base = qblk + w * kTileBytes;
-      const uint32_t dst = tiles_addr + w * kTileBytes;
+      const char* base = qblk + w * G::kTileBytes;
+      const uint32_t dst = tiles_addr + w * G::kTileBytes;
 #pragma unroll
-      for (int ii = 0; ii < kPipeCopies; ++ii) {
+      for (int ii = 0; ii < G::kCopies; ++ii) {
         const uint32_t pk = cpk[ii / 2] >> (16 * (ii & 1));
-        dma16_sv(base, ((pk >> 11) & 31u) * (kD * 2) + (pk & 2047u), dst + (wave + 4 * ii) * 1024);
+        dma16_sv(base, ((pk >> 11) & 31u) * (G::D * 2) + (pk & 2047u), dst + (wave + 4 * ii) * 1024);
       }
     }
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    MLA_LDS const char* qb = tiles + wave * kTileBytes;
+    MLA_LDS const char* qb = tiles + wave * G::kTileBytes;
 #pragma unroll
-    for (int s = 0; s < 36; ++s)
+    for (int s = 0; s < G::kNk; ++s)
       qf[s] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(qb + ka[s & 3] + 128 * (s >> 2));
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
     __builtin_amdgcn_s_barrier();        // every wave done with the buffers
   }
-  if (n_tiles > 0) issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
-  wait_vmcnt<0>();
+  auto issue_first = [&]() {  // the first tiles of a pass
+    if constexpr (G::kExpand) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if (k < n_tiles) issue_raw_at(tile_base(k), k);
+    } else {
+      if (n_tiles > 0) issue_tile(0);
+      if (n_tiles > 1) issue_tile(1);
+      wait_vmcnt<0>();
+    }
+  };
+  issue_first();
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -492,66 +586,129 @@ decode_bf16_pipe_kernel(DecodeParams p) {
     l_run = 0.f;
     excess = -INFINITY;
     if (n_tiles == 0) return false;
-    if (n_tiles > 2) issue_tile(2);
+    if constexpr (G::kExpand) {
+      // staged tiles 0..2 are in flight; tiles 0 and 1 into bf16 buffers 0, 1
+      if (n_tiles >= 3) wait_vmcnt<2 * G::kRawCopies>();
+      else if (n_tiles == 2) wait_vmcnt<G::kRawCopies>();
+      else wait_vmcnt<0>();
+      expand_cpp(0);
+      if (n_tiles > 1) {
+        if (n_tiles >= 3) wait_vmcnt<G::kRawCopies>();
+        else wait_vmcnt<0>();
+        expand_cpp(1);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging slot 0 read
+      if (n_tiles > 3) issue_raw_at(tile_base(3), 3);
+    } else {
+      if (n_tiles > 2) issue_tile(2);
+    }
     __builtin_amdgcn_s_barrier();  // tiles 0 and 1 visible to all waves
     {  // scores and numerators of tile 0
       const uint32_t bk = buf_addr(0);
       const uint32_t bpw = pbuf_addr_of(0) + wave * 2048;
       const int tok = 0;
-      asm volatile(MLA_BF16_FIRST
-                   : MLA_ASM_SOFTMAX_STATE
-                   : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_SOFTMAX_IN
-                   : MLA_ASM_SCRATCH);
+      if constexpr (PF == kPipeNope)
+        asm volatile(MLA_NOPE_FIRST
+                     : MLA_ASM_SOFTMAX_STATE
+                     : MLA_ASM_Q32, MLA_ASM_KEYS, MLA_ASM_SOFTMAX_IN
+                     : MLA_ASM_SCRATCH);
+      else
+        asm volatile(MLA_BF16_FIRST
+                     : MLA_ASM_SOFTMAX_STATE
+                     : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_SOFTMAX_IN
+                     : MLA_ASM_SCRATCH);
     }
     int k = 0;
-    // Steps that also copy tile k+3.  Their scored tile k+1 ends at least 32
-    // tokens before the sequence end, so with q_len <= 32 all of it is
-    // visible and the stream skips the mask.
-    // Copy sources are looked up ahead: the block-table entry of tile k+5 is
-    // read in step k and turned into an address in step k+1, so no step
-    // waits for a table read.
-    const char* cb_next = n_tiles > 3 ? tile_base(3) : nullptr;
-    int blk_next = n_tiles > 4 ? block_of(4) : 0;
-    for (; k + 3 < n_tiles; ++k) {
-      const char* cb = cb_next;
-      wait_vmcnt<kPipeCopies>();
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's P^T of tile k written
-      __builtin_amdgcn_s_barrier();  // tile k+1 and P^T of tile k visible; tile k-1 released
-      const int cl = last_row(k + 3);
-      const uint32_t cd = buf_addr(k + 3) + wave * 1024;
-      const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k), bp = pbuf_addr_of(k);
-      const uint32_t bpw = pbuf_addr_of(k + 1) + wave * 2048;
-      const int tok = 32 * (k + 1);
-      asm volatile(MLA_BF16_STEP_COPY
-                   : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
-                   : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN, MLA_ASM_COPY
-                   : MLA_ASM_SCRATCH);
-      if (k + 4 < n_tiles) cb_next = base_from(blk_next, k + 4);
-      if (k + 5 < n_tiles) blk_next = block_of(k + 5);
+    if constexpr (G::kExpand) {
+      // Step k expands tile k+2 and copies the stored rows of tile k+4 (into
+      // the staging slot that tile k+1 left in step k-1).  Its scored tile
+      // k+1 is not the chunk's last, so with q_len <= 32 all of it is
+      // visible and the stream skips the mask.  Copy sources are looked up
+      // a step ahead.
+      const char* cb_next = n_tiles > 4 ? tile_base(4) : nullptr;
+      int blk_next = n_tiles > 5 ? block_of(5) : 0;
+      for (; k + 2 < n_tiles; ++k) {
+        if (k + 3 < n_tiles) wait_vmcnt<G::kRawCopies>();  // this wave's stored rows of tile k+2
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's tile k+1 rows and P^T of tile k written
+        __builtin_amdgcn_s_barrier();  // tile k+1 and P^T of tile k visible; tile k-1 released
+        if (k + 4 < n_tiles) issue_raw_at(cb_next, k + 4);
+        const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k), bp = pbuf_addr_of(k);
+        const uint32_t bpw = pbuf_addr_of(k + 1) + wave * 2048;
+        const uint32_t xs = stage_addr + ((k + 2) % 3) * G::kStageBytes + wave * G::kStageWave;
+        const uint32_t xt = buf_addr(k + 2) + 8 * wave * G::kChunks * 16;
+        const int tok = 32 * (k + 1);
+        asm volatile(MLA_FP4_STEP_EXPAND
+                     : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                     : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN, MLA_ASM_EXPAND
+                     : MLA_ASM_SCRATCH);
+        if (k + 5 < n_tiles) cb_next = base_from(blk_next, k + 5);
+        if (k + 6 < n_tiles) blk_next = block_of(k + 6);
+      }
+    } else {
+      // Steps that also copy tile k+3.  Their scored tile k+1 ends at least 32
+      // tokens before the sequence end, so with q_len <= 32 all of it is
+      // visible and the stream skips the mask.
+      // Copy sources are looked up ahead: the block-table entry of tile k+5 is
+      // read in step k and turned into an address in step k+1, so no step
+      // waits for a table read.
+      const char* cb_next = n_tiles > 3 ? tile_base(3) : nullptr;
+      int blk_next = n_tiles > 4 ? block_of(4) : 0;
+      for (; k + 3 < n_tiles; ++k) {
+        const char* cb = cb_next;
+        wait_vmcnt<G::kCopies>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's P^T of tile k written
+        __builtin_amdgcn_s_barrier();  // tile k+1 and P^T of tile k visible; tile k-1 released
+        const int cl = last_row(k + 3);
+        const uint32_t cd = buf_addr(k + 3) + wave * 1024;
+        const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k), bp = pbuf_addr_of(k);
+        const uint32_t bpw = pbuf_addr_of(k + 1) + wave * 2048;
+        const int tok = 32 * (k + 1);
+        if constexpr (PF == kPipeNope)
+          asm volatile(MLA_NOPE_STEP_COPY
+                       : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                       : MLA_ASM_Q32, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN, MLA_ASM_COPY
+                       : MLA_ASM_SCRATCH);
+        else
+          asm volatile(MLA_BF16_STEP_COPY
+                       : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                       : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN, MLA_ASM_COPY
+                       : MLA_ASM_SCRATCH);
+        if (k + 4 < n_tiles) cb_next = base_from(blk_next, k + 4);
+        if (k + 5 < n_tiles) blk_next = block_of(k + 5);
+      }
     }
     for (; k + 1 < n_tiles; ++k) {
-      if (k + 2 < n_tiles) wait_vmcnt<kPipeCopies>();
+      if (!G::kExpand && k + 2 < n_tiles) wait_vmcnt<G::kCopies>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_s_barrier();
       const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k), bp = pbuf_addr_of(k);
       const uint32_t bpw = pbuf_addr_of(k + 1) + wave * 2048;
       const int tok = 32 * (k + 1);
-      asm volatile(MLA_BF16_STEP_MASKED
-                   : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
-                   : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN
-                   : MLA_ASM_SCRATCH);
+      if constexpr (PF == kPipeNope)
+        asm volatile(MLA_NOPE_STEP_MASKED
+                     : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                     : MLA_ASM_Q32, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN
+                     : MLA_ASM_SCRATCH);
+      else
+        asm volatile(MLA_BF16_STEP_MASKED
+                     : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                     : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN
+                     : MLA_ASM_SCRATCH);
     }
     {  // weighted sum of the last tile (its keys were scored in the last step)
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_s_barrier();  // P^T of the last tile visible
       const uint32_t bv = buf_addr(k), bp = pbuf_addr_of(k);
-      asm volatile(MLA_BF16_PV_ONLY : MLA_ASM_ACC : MLA_ASM_VALUES, [pa] "v"(pa) : MLA_ASM_SCRATCH);
+      if constexpr (PF == kPipeNope)
+        asm volatile(MLA_NOPE_PV_ONLY : MLA_ASM_ACC : MLA_ASM_VALUES, [pa] "v"(pa) : MLA_ASM_SCRATCH);
+      else
+        asm volatile(MLA_BF16_PV_ONLY : MLA_ASM_ACC : MLA_ASM_VALUES, [pa] "v"(pa) : MLA_ASM_SCRATCH);
     }
     return excess > kSlack;
   };
 #pragma clang diagnostic pop
-
   // Cross-wave words (second-pass flag, per-head 1/l) live in tile buffer 0,
   // which no wave reads once every wave has passed the barrier below.
   MLA_LDS int* xflag = reinterpret_cast<MLA_LDS int*>(tiles);
@@ -570,9 +727,7 @@ decode_bf16_pipe_kernel(DecodeParams p) {
   if (second_pass) {
     __builtin_amdgcn_s_barrier();  // every wave has read the flags
     m_ref = m_seen;
-    if (n_tiles > 0) issue_tile(0);
-    if (n_tiles > 1) issue_tile(1);
-    wait_vmcnt<0>();
+    issue_first();
     run_pass();
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -750,7 +905,9 @@ int64_t partial_units(const DecodeArgs& a) {
   return a.num_splits > 1 ? static_cast<int64_t>(a.batch) * a.num_splits : 0;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+namespace {
+
+DecodeParams decode_params(const DecodeArgs& a) {
   DecodeParams p;
   p.q_lat = static_cast<const __bf16*>(a.q_lat);
   p.cache = static_cast<const __bf16*>(a.cache);
@@ -773,18 +930,44 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
   p.items = a.items;
   const int waves = decode_waves_per_group(a.n_h, a.q_len);
   p.row_groups = a.q_len * a.n_h / (32 * waves);
-  const bool pipe = waves == 4 && a.q_len <= 32;
+  p.xcd_group = 0;
+  return p;
+}
+
+}  // namespace
+
+bool decode_pipe_supported(int n_h, int q_len) { return decode_waves_per_group(n_h, q_len) == 4 && q_len <= 32; }
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+  DecodeParams p = decode_params(a);
+  const int waves = decode_waves_per_group(a.n_h, a.q_len);
+  const bool pipe = decode_pipe_supported(a.n_h, a.q_len);
   p.xcd_group = a.items == nullptr && pipe && a.batch % 8 == 0;
   const dim3 grid = a.items != nullptr ? dim3(a.num_slots) : dim3(a.num_splits * p.row_groups, a.batch);
   if (a.items != nullptr && a.num_slots == 0) return hipSuccess;
   if (pipe)
-    hipLaunchKernelGGL(decode_bf16_pipe_kernel, grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL(decode_pipe_kernel<kPipeBf16>, grid, dim3(256), 0, st, p);
   else if (waves == 4)
     hipLaunchKernelGGL((decode_bf16_kernel<4, 3>), grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((decode_bf16_kernel<2, 2>), grid, dim3(128), 0, st, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || rows == 0) return e;
+  if (e != hipSuccess || partial_units(a) == 0) return e;
+  return launch_combine(a, st, p.xcd_group != 0);
+}
+
+// The pipelined stream over the NoPE (512-wide bf16) and FP4 cache rows.
+hipError_t launch_decode_pipe(const DecodeArgs& a, int fmt, hipStream_t st) {
+  DecodeParams p = decode_params(a);
+  p.xcd_group = a.items == nullptr && a.batch % 8 == 0;
+  const dim3 grid = a.items != nullptr ? dim3(a.num_slots) : dim3(a.num_splits * p.row_groups, a.batch);
+  if (a.items != nullptr && a.num_slots == 0) return hipSuccess;
+  if (fmt == kDqFp4Mx)
+    hipLaunchKernelGGL(decode_pipe_kernel<kPipeFp4>, grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(decode_pipe_kernel<kPipeNope>, grid, dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || partial_units(a) == 0) return e;
   return launch_combine(a, st, p.xcd_group != 0);
 }
 

@@ -41,6 +41,22 @@ Operands (named in the kernel):
                   visible iff t < vlim - tok
   %[cb], %[cd], %[cl], %[k1152], %[c0..4]   the tile copy (see copy())
 The streams use v177-v255, vcc, m0 and scc as scratch.
+
+The same streams serve two more row formats of the latent cache:
+  NoPE  rows of 512 bf16 values (no RoPE part): 32 query fragments in two
+        chains of 16, eight copies per wave, 64 chunks per tile row
+  FP4   rows of 576 E2M1 codes with an E8M0 scale per 32 values (320 bytes):
+        the stored rows are staged in LDS by copies the kernel issues, and
+        the step stream expands tile k+2 into the bf16 tile layout between
+        the weighted-sum MFMAs of its second part (each wave its own eight
+        rows: one 4-byte code word and one scale byte per lane and row, four
+        conversions, one 16-byte store), with the inputs
+  %[xs]           LDS byte address of this wave's staged rows of tile k+2
+  %[xt]           LDS byte address of this wave's rows of bf16 tile k+2
+  %[xw]           64 * (wave & 1): the swizzle term the wave's rows share
+  %[xtl0], %[xtl1]  per-lane offsets of the rows' last eight chunks (the
+                  RoPE part): code word | scale byte << 16 in the staged
+                  rows, and the destination in the bf16 tile
 """
 import sys
 
@@ -56,6 +72,23 @@ SA = 224                              # score chain A, then scores / numerators
 SB = 240                              # score chain B, then bf16 numerators + temps
 PW = KADDR[0]                         # P^T write address (keys are done by then)
 NEG_INF = "0xff800000"
+WRITE_TAGS = ("pw", "xw")                     # LDS ops that write no register
+
+
+class Geo:
+    """Tile geometry of a row width D (bf16 elements per cache row)."""
+
+    def __init__(self, d):
+        self.d = d
+        self.nk = d // 16                 # 16-wide query fragments
+        self.half = self.nk // 2          # fragments per score chain
+        self.chunks = d // 8              # 16-byte chunks per tile row
+        self.copies = d * 2 * 32 // 1024 // 4   # 1 KB copies per wave and tile
+        self.kseq = [f for i in range(self.half) for f in (i, self.half + i)]
+
+
+G576 = Geo(576)
+G512 = Geo(512)
 
 
 def vr(base, n=4):
@@ -63,7 +96,8 @@ def vr(base, n=4):
 
 
 class Stream:
-    def __init__(self):
+    def __init__(self, geo=G576):
+        self.geo = geo
         self.lines = []
         self.issued = []      # LDS op tags in issue order
         self.done = 0         # ops known complete (prefix of issued)
@@ -84,9 +118,15 @@ class Stream:
         self.done = len(self.issued) - n
 
     def wait_all(self):
-        if self.done < len(self.issued):
-            self.emit("s_waitcnt lgkmcnt(0)")
-            self.done = len(self.issued)
+        # every LDS read has landed (the scratch registers are free after the
+        # stream); LDS writes issued after the last read may stay in flight
+        # (the kernel waits for them before its next barrier)
+        reads = [i for i, t in enumerate(self.issued) if t[0] not in WRITE_TAGS]
+        if not reads or reads[-1] < self.done:
+            return
+        n = min(len(self.issued) - (reads[-1] + 1), 15)
+        self.emit(f"s_waitcnt lgkmcnt({n})")
+        self.done = len(self.issued) - n
 
     # ---- LDS reads
     def kread(self, s, slot):
@@ -96,7 +136,7 @@ class Stream:
         # value fragment vi = (k-step ks, column tile j of this wave's four)
         ks, j = vi >> 2, vi & 3
         slot = VF[vi % len(VF)]
-        off = ks * 16 * 72 * 16 + (j >> 1) * 128
+        off = ks * 16 * self.geo.chunks * 16 + (j >> 1) * 128
         self.lds(("v", vi), f"ds_read_b64_tr_b16 {vr(slot, 2)}, v{VADDR[j & 1]} offset:{off}")
         self.lds(("v", vi), f"ds_read_b64_tr_b16 {vr(slot + 2, 2)}, v{VADDR[2 + (j & 1)]} offset:{off}")
 
@@ -129,6 +169,17 @@ class Stream:
         self.emit(f"v_mad_u32_u24 v{CO}, v{CT}, %[k1152], v{CO}")
         self.emit(f"s_add_u32 m0, %[cd], {4096 * ii}")
         self.emit(f"global_load_lds_dwordx4 v{CO}, %[cb]")
+
+    def op(self, items):
+        """Emit one op group: plain lines, ("lds", tag, text) for LDS
+        instructions (counted for the waits) and ("wait", tag)."""
+        for it in items:
+            if isinstance(it, str):
+                self.emit(it)
+            elif it[0] == "lds":
+                self.lds(it[1], it[2])
+            else:
+                self.wait_for(it[1])
 
     def text(self):
         return "\n".join(self.lines)
@@ -179,8 +230,8 @@ def softmax_ops(masked):
     for i in range(8):
         ops.append([f"v_cvt_pk_bf16_f32 v{b[i]}, v{a[2 * i]}, v{a[2 * i + 1]}"])
     ops.append([f"v_add_u32 v{PW}, %[bpw], %[pa]",
-                f"ds_write_b128 v{PW}, {vr(b[0])}",
-                f"ds_write_b128 v{PW}, {vr(b[4])} offset:1024"])
+                ("lds", ("pw",), f"ds_write_b128 v{PW}, {vr(b[0])}"),
+                ("lds", ("pw",), f"ds_write_b128 v{PW}, {vr(b[4])} offset:1024")])
     return ops
 
 
@@ -203,72 +254,144 @@ def mfma_results_ready(st):
 
 def scores(st, kseq, p):
     """Score MFMA at position p of kseq (chain A takes fragment i, chain B
-    fragment 18 + i), with the key read KF slots ahead."""
+    fragment half + i), with the key read KF slots ahead."""
     f = kseq[p]
+    h = st.geo.half
     st.wait_for(("k", f))
-    chain = SA if f < 18 else SB
-    acc = "0" if f in (0, 18) else vr(chain, 16)
+    chain = SA if f < h else SB
+    acc = "0" if f in (0, h) else vr(chain, 16)
     st.emit(f"v_mfma_f32_32x32x16_bf16 {vr(chain, 16)}, {vr(KF[p % len(KF)])}, %[q{f}], {acc}")
     if p + len(KF) < len(kseq):
         st.kread(kseq[p + len(KF)], p % len(KF))
 
 
-KSEQ = [f for i in range(18) for f in (i, 18 + i)]
-
-
-def first():
+def first(geo=G576):
     """Scores and softmax numerators of the first tile of a pass."""
-    st = Stream()
+    st = Stream(geo)
     st.emit("s_nop 4")
     addresses(st, True, False)
     for p in range(len(KF)):
-        st.kread(KSEQ[p], p)
-    for p in range(len(KSEQ)):
-        scores(st, KSEQ, p)
+        st.kread(geo.kseq[p], p)
+    for p in range(len(geo.kseq)):
+        scores(st, geo.kseq, p)
     mfma_results_ready(st)
     for op in softmax_ops(True):
-        for line in op:
-            st.emit(line)
+        st.op(op)
     return st.text()
 
 
-def step(copies, masked):
-    st = Stream()
+# FP4 expansion registers (free in the step's second part: the key address
+# and key fragment registers, after the last score MFMA)
+XS, XSS, XW = KADDR[1], KADDR[2], KADDR[3]    # code, scale and store bases
+XSLOT = [(188, 192), (194, 198)]              # (4 output VGPRs, scale/address)
+XTAIL = 193                                   # second address of the tail chunk
+FP4_ROW = 320                                 # bytes per stored row
+FP4_CODES = 288                               # code bytes per stored row
+
+
+def swz_even(j):
+    # the tile layout's chunk swizzle of row j for a wave with even index
+    u = j >> 1
+    return u ^ ((u & 1) << 2)
+
+
+def fp4_cvt(o, e):
+    # four conversions of the code word in o+3 (read last), scale in e
+    sels = ["", " op_sel:[1,0,0]", " op_sel:[0,1,0]", " op_sel:[1,1,0]"]
+    return [f"v_cvt_scalef32_pk_bf16_fp4 v{o + i}, v{o + 3}, v{e}{sels[i]}" for i in range(4)]
+
+
+def fp4_expand_ops():
+    """Op groups expanding this wave's eight rows of one staged FP4 tile into
+    the bf16 tile (chunk c of row t at t*72 + (c ^ swz(t))): a setup, then per
+    row j reads (slot j%2), conversion, store; reads run one row ahead."""
+    rows = 8
+    ops = [[f"v_lshrrev_b32 v{XS}, 2, %[pa]", f"v_add_u32 v{XS}, %[xs], v{XS}",
+            f"v_lshrrev_b32 v{XSS}, 6, %[pa]", f"v_add_u32 v{XSS}, %[xs], v{XSS}",
+            f"v_xor_b32 v{XW}, %[xw], %[pa]", f"v_add_u32 v{XW}, %[xt], v{XW}"]]
+
+    def reads(j):
+        o, e = XSLOT[j % 2]
+        if j < rows:
+            return [("lds", ("xr", j), f"ds_read_b32 v{o + 3}, v{XS} offset:{FP4_ROW * j}"),
+                    ("lds", ("xr", j), f"ds_read_u8 v{e}, v{XSS} offset:{FP4_ROW * j + FP4_CODES}")]
+        return [f"v_and_b32 v{e}, 0xffff, %[xtl0]", f"v_add_u32 v{e}, %[xs], v{e}",
+                f"v_lshrrev_b32 v{XTAIL}, 16, %[xtl0]", f"v_add_u32 v{XTAIL}, %[xs], v{XTAIL}",
+                ("lds", ("xr", j), f"ds_read_b32 v{o + 3}, v{e} offset:256"),
+                ("lds", ("xr", j), f"ds_read_u8 v{XTAIL}, v{XTAIL} offset:{FP4_CODES + 16}")]
+
+    def convert(j):
+        o, e = XSLOT[j % 2]
+        sc = e if j < rows else XTAIL
+        return [("wait", ("xr", j)), f"v_lshlrev_b32 v{sc}, 23, v{sc}"] + fp4_cvt(o, sc)
+
+    def store(j):
+        o, e = XSLOT[j % 2]
+        if j < rows:
+            return [f"v_xor_b32 v{e}, {16 * swz_even(j)}, v{XW}",
+                    ("lds", ("xw", j), f"ds_write_b128 v{e}, {vr(o)} offset:{1152 * j}")]
+        return [f"v_add_u32 v{e}, %[xt], %[xtl1]", ("lds", ("xw", j), f"ds_write_b128 v{e}, {vr(o)}")]
+
+    ops.append(reads(0))
+    for j in range(rows + 1):
+        if j + 1 <= rows:
+            ops.append(reads(j + 1))
+        ops.append(convert(j))
+        ops.append(store(j))
+    return ops
+
+
+def merge(a, b):
+    """Alternate two op lists, spreading the shorter one evenly."""
+    if len(a) < len(b):
+        a, b = b, a
+    out, bi = [], 0
+    for n, op in enumerate(a):
+        out.append(op)
+        while bi < len(b) and (bi + 1) * len(a) <= (n + 1) * len(b):
+            out.append(b[bi])
+            bi += 1
+    out.extend(b[bi:])
+    return out
+
+
+def step(copies, masked, geo=G576, expand=False):
+    st = Stream(geo)
     st.emit("s_nop 4")
     addresses(st, True, True)
     for p in range(len(KF)):
-        st.kread(KSEQ[p], p)
+        st.kread(geo.kseq[p], p)
     for g in range(4):
         st.pread(0, g)
     for vi in range(len(VF) - 1):
         st.vread(vi)
-    for p in range(len(KSEQ)):
-        scores(st, KSEQ, p)
+    for p in range(len(geo.kseq)):
+        scores(st, geo.kseq, p)
         if p & 1:
             i = p >> 1
             st.pv(i)
-            if copies and i % 2 == 0 and i // 2 < 9:
+            if copies and i % 2 == 0 and i // 2 < geo.copies:
                 st.copy(i // 2)
     mfma_results_ready(st)
     ops = softmax_ops(masked)
-    rest = list(range(18, 32))
+    if expand:
+        ops = merge(ops, fp4_expand_ops())
+    rest = list(range(geo.half, 32))
     per = -(-len(ops) // (len(rest) + 1))
     for n, i in enumerate(rest):
         for op in ops[n * per:(n + 1) * per]:
-            for line in op:
-                st.emit(line)
+            st.op(op)
         st.pv(i)
     for op in ops[len(rest) * per:]:
-        for line in op:
-            st.emit(line)
+        st.op(op)
     st.wait_all()
     mfma_results_ready(st)
     return st.text()
 
 
-def pv_only():
+def pv_only(geo=G576):
     """Weighted sum of the last tile of a pass."""
-    st = Stream()
+    st = Stream(geo)
     st.emit("s_nop 4")
     addresses(st, False, True)
     for g in range(4):
@@ -294,6 +417,11 @@ def main():
     out.append(as_c_string("MLA_BF16_STEP_MASKED", step(False, True)))
     out.append(as_c_string("MLA_BF16_FIRST", first()))
     out.append(as_c_string("MLA_BF16_PV_ONLY", pv_only()))
+    out.append(as_c_string("MLA_NOPE_STEP_COPY", step(True, False, G512)))
+    out.append(as_c_string("MLA_NOPE_STEP_MASKED", step(False, True, G512)))
+    out.append(as_c_string("MLA_NOPE_FIRST", first(G512)))
+    out.append(as_c_string("MLA_NOPE_PV_ONLY", pv_only(G512)))
+    out.append(as_c_string("MLA_FP4_STEP_EXPAND", step(False, False, G576, expand=True)))
     sys.stdout.write("\n".join(out))
 
 

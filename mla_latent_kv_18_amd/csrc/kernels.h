@@ -108,6 +108,10 @@ hipError_t launch_decode_fp8(const DecodeArgs&, hipStream_t);
 // decode over the cache variants, rows expanded to bf16 in LDS
 enum { kDqFp4Mx = 0, kDqFp8Kr = 1, kDqBf16Nope = 2 };
 hipError_t launch_decode_dq(const DecodeArgs&, int fmt, hipStream_t);
+// the pipelined decode stream (workgroups of 128 rows, q_len <= 32) over
+// bf16 576-wide rows (launch_decode_mfma), NoPE rows and FP4 rows
+bool decode_pipe_supported(int n_h, int q_len);
+hipError_t launch_decode_pipe(const DecodeArgs&, int fmt, hipStream_t);
 // causal prefill attention of one sequence with per-head keys and values
 // (q, k: [d_h content ; d_R RoPE part] = 192 wide, v: 128 wide)
 struct PrefillArgs {

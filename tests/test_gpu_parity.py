@@ -254,6 +254,9 @@ SMALL_VARIANTS = {
     "nope_ragged": ("nope_bs64_ctx4k", dict(batch=3, lens=(1, 100, 257), shuffle=True)),
     "nope_heads64_q2": ("nope_bs64_ctx4k", dict(n_h=64, batch=2, lens=(2, 200), q_len=2)),
     "nope_batch8": ("nope_bs64_ctx4k", dict(batch=8, lens=(0, 2, 63, 64, 65, 500, 1000, 2048))),
+    "nope_q2": ("nope_bs64_ctx4k", dict(batch=2, lens=(3, 300), q_len=2)),
+    "fp4_batch8": ("v3_fp4_bs64_ctx4k", dict(batch=8, lens=(0, 2, 63, 64, 65, 97, 161, 2048))),
+    "fp4_q2": ("v3_fp4_bs64_ctx4k", dict(batch=2, lens=(3, 300), q_len=2)),
 }
 
 
