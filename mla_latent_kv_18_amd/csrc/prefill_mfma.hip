@@ -53,7 +53,7 @@ constexpr int kTK = 64;                 // keys per staged tile (two 32-key MFMA
 constexpr int kKTile = kTK * kKC * 16;  // 24,576 B
 constexpr int kVTile = kTK * kVS * 16;  // 16,384 B
 constexpr int kBuf = kKTile + kVTile;   // one tile: 40 wave-wide 1 KB copies
-constexpr int kNBuf = 4;                // tiles in LDS (160 KB): the one computed and three landing
+constexpr int kNBuf = 4;                // tiles in LDS (160 KB): keys and values of one tile each
 constexpr int kCopies = kBuf / 1024 / kWaves;  // copies per wave per tile
 
 struct PrefillParams {
@@ -79,7 +79,7 @@ __device__ __forceinline__ bf16x8_t ld8(const __bf16* p) { return *reinterpret_c
 // r * 16 + (c ^ 2(r & 3)), so the four rows of a transposed read hit four
 // different 32-byte spans.  Tiles arrive by direct global->LDS copies (lane l of copy i fills
 // slot 64i + l, so the layout is chosen by which chunk each lane fetches),
-// up to three tiles ahead of the one being computed.
+// two tiles ahead of the one being computed (four tile buffers).
 __device__ __forceinline__ int k_slot(int r, int c) { return r * kKC + (c ^ ((r >> 1) & 7)); }
 
 __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillParams p, RopeTable64 rope) {
@@ -141,27 +141,29 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
     wait_vmcnt<0>();  // complete before the tile copies start counting
   }
 
-  // per-lane LDS offsets
-  int kq_off[kPD / 16];
+  // per-lane LDS offsets.  Key fragment s of lane (row l32, chunk 2s + hf) is
+  // at kq_off[s & 3] + 128 (s >> 2): the row's XOR swizzle touches only the
+  // low three chunk bits.  Value fragment (k-step ks, half h2, column tile
+  // ct) is at pv_off[h2][ct & 1] + 4096 ks + 128 (ct >> 1), for the same
+  // reason (16 rows further keep the row's swizzle).
+  int kq_off[4];
 #pragma unroll
-  for (int s = 0; s < kPD / 16; ++s) kq_off[s] = k_slot(l32, 2 * s + hf) * 16;
+  for (int s = 0; s < 4; ++s) kq_off[s] = k_slot(l32, 2 * s + hf) * 16;
   const int L = lane & 15, cg = (lane >> 4) & 1;
-  int pv_off[2][2][4];  // [k-step][h2][value column tile]
+  int pv_off[2][2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int row = 8 * h2 + 4 * hf + (L >> 2);
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int row = 16 * ks + 8 * h2 + 4 * hf + (L >> 2);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int chunk = 8 * (ct >> 1) + 4 * (ct & 1) + 2 * cg + ((L & 3) >> 1);
-        pv_off[ks][h2][ct] = (row * kVS + (chunk ^ (2 * (row & 3)))) * 16 + 8 * (L & 1);
-      }
+    for (int par = 0; par < 2; ++par) {
+      const int chunk = 4 * par + 2 * cg + ((L & 3) >> 1);
+      pv_off[h2][par] = (row * kVS + (chunk ^ (2 * (row & 3)))) * 16 + 8 * (L & 1);
     }
+  }
 
   // copies of tile k into buffer bi: copy i = wave + 8j; the first 24 fill the
   // key rows, the last 16 the value rows
-  auto issue = [&](int k, int bi) {
+  auto issue = [&](int k) {
 #pragma unroll
     for (int j = 0; j < kCopies; ++j) {
       const int i = wave + kWaves * j, slot = 64 * i + lane;
@@ -176,7 +178,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
         const int64_t key = k_row0 + min(kTK * k + r, Tk - 1);
         g = p.v + (key * p.n_h + head) * kPV + 8 * c;
       }
-      dma16(g, tiles_addr + bi * kBuf + i * 1024);
+      dma16(g, tiles_addr + (k % kNBuf) * kBuf + i * 1024);
     }
   };
 
@@ -186,77 +188,130 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
   float m_run = -INFINITY, l_run = 0.f;
   const int last_key = min(ctx + qb * kQB + kQB - 1, Tk - 1);
   const int n_tiles = last_key / kTK + 1;
+  // the wave's queries see keys up to ctx + q0 + 31 (its last query), and
+  // every key of a tile up to min(ctx + q0, Tk - 1) (its first query's last)
+  const int wave_last = ctx + q0 + 31;
+  const int wave_full = min(ctx + q0, Tk - 1);
+  auto visible = [&](int k) { return kTK * k <= wave_last; };
+
+  f32x16_t sc[2];
+  bf16x8_t pf[4];
+  // scores of tile k: S^T for the two 32-key sub-tiles, two independent
+  // chains; key fragments are read two k-steps ahead
+  auto scores = [&](int k) {
+    MLA_LDS const char* ktile = tiles + (k % kNBuf) * kBuf;
+    auto kread = [&](int s, int sub) {
+      return *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + sub * (32 * kKC * 16) + kq_off[s & 3] + 128 * (s >> 2));
+    };
+    constexpr int kAhead = 2;
+    bf16x8_t kf[kAhead][2];
 #pragma unroll
-  for (int k = 0; k < kNBuf - 1; ++k)
-    if (k < n_tiles) issue(k, k);
-  for (int k = 0; k < n_tiles; ++k) {
-    // copies still allowed in flight: those of the tiles issued after tile k
-    switch (min(n_tiles - 1 - k, kNBuf - 2)) {  // copies of the tiles issued after tile k may be in flight
-      case 2: wait_vmcnt<2 * kCopies>(); break;
-      case 1: wait_vmcnt<kCopies>(); break;
-      default: wait_vmcnt<0>(); break;
+    for (int s = 0; s < kAhead; ++s)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) kf[s][sub] = kread(s, sub);
+    sc[0] = f32x16_t{};
+    sc[1] = f32x16_t{};
+#pragma unroll
+    for (int s = 0; s < kPD / 16; ++s)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const bf16x8_t cur = kf[s % kAhead][sub];
+        if (s + kAhead < kPD / 16) kf[s % kAhead][sub] = kread(s + kAhead, sub);
+        sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sc[sub], 0, 0, 0);
+      }
+  };
+  // O^T += V^T P^T for tile k (k-steps 0, 1 sum the first sub-tile's
+  // values, 2, 3 the second's); value fragments are read one MFMA ahead
+  auto weighted_sum = [&](int k) {
+    MLA_LDS char* vtile = tiles + (k % kNBuf) * kBuf + kKTile;
+    auto vread = [&](int i) {
+      const int ks = i >> 2, ct = i & 3;
+      MLA_LDS char* vb = vtile + (ks >> 1) * (32 * kVS * 16) + (ks & 1) * 4096 + 128 * (ct >> 1);
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[0][ct & 1]));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[1][ct & 1]));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t vf[2];
+    vf[0] = vread(0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 1 < 16) vf[(i + 1) & 1] = vread(i + 1);
+      oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 1], pf[i >> 2], oacc[i & 3], 0, 0, 0);
     }
-    __builtin_amdgcn_s_barrier();  // tile k visible to all; tile k-1 released by all
-    if (k + kNBuf - 1 < n_tiles) issue(k + kNBuf - 1, (k + kNBuf - 1) % kNBuf);
-    MLA_LDS char* ktile = tiles + (k % kNBuf) * kBuf;
-    MLA_LDS char* vtile = ktile + kKTile;
+  };
+  // online softmax of tile k's scores: numerators P (bf16) for the next
+  // weighted sum, running maximum and sum, O rescaled where a maximum grew.
+  // The scale goes into the exponent's fma (the maximum is taken on the raw
+  // scores; the scale is positive); keys are masked only in tiles that reach
+  // past some query's last visible key.
+  auto softmax = [&](int k) {
     const int key0 = kTK * k;
-    if (key0 <= ctx + q0 + 31) {  // some key of the tile is visible to this wave
-      // scores of the two 32-key sub-tiles: two independent MFMA chains
-      f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-      for (int s = 0; s < kPD / 16; ++s)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          const bf16x8_t kf = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + sub * (32 * kKC * 16) + kq_off[s]);
-          sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[sub], 0, 0, 0);
-        }
+    if (key0 + kTK - 1 > wave_full) {
       // register r of sub-tile u holds key key0 + 32u + 8(r/4) + 4hf + r%4
-      float mx = -INFINITY;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * sub + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sc[sub][r] = key <= vis ? sc[sub][r] * p.scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sc[sub][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      // key 0 is visible to every query, so m_new is finite from the first tile on
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      bf16x8_t pf[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(sc[sub][r] - m_new);
-          psum += pr;
-          pf[2 * sub + (r >> 3)][r & 7] = f32_to_bf16(pr);
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // the accumulators are rescaled only when some query's maximum grew
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-        for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] *= alpha;
-      }
-      // k-steps 0, 1 sum the first sub-tile's values, 2, 3 the second's
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int ct = 0; ct < kPV / 32; ++ct) {
-          MLA_LDS char* vb = vtile + (ks >> 1) * (32 * kVS * 16);
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[ks & 1][0][ct]));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[ks & 1][1][ct]));
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], oacc[ct], 0, 0, 0);
+          sc[sub][r] = key <= vis ? sc[sub][r] : -INFINITY;
         }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sub][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // key 0 is visible to every query, so m_new is finite from the first tile on
+    const float m_new = fmaxf(m_run, mx * p.scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(fmaf(sc[sub][r], p.scale_log2, -m_new));
+        psum += pr;
+        pf[2 * sub + (r >> 3)][r & 7] = f32_to_bf16(pr);
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // the accumulators are rescaled only when some query's maximum grew
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] *= alpha;
+    }
+  };
+
+  // Two groups of four waves (waves w and w + 4 share a SIMD) run the same
+  // phase sequence -- matrix phase k (scores of tile k, weighted sum of tile
+  // k-1, copies of tile k+2), softmax phase k -- with the second group one
+  // phase behind, so that on every SIMD one wave's softmax runs beside the
+  // other wave's MFMAs.  Barriers separate the phases.  Tile k+2 goes into
+  // the buffer of tile k-2, whose values both groups summed in their matrix
+  // phase k-1; each wave's copies of tile k+1 have landed by the end of its
+  // matrix phase k.
+  if (n_tiles > 0) issue(0);
+  if (n_tiles > 1) issue(1);
+  if (n_tiles > 1) wait_vmcnt<kCopies>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();  // tile 0 visible to all
+  const bool late = wave >= kWaves / 2;
+  if (late) __builtin_amdgcn_s_barrier();
+  for (int k = 0;; ++k) {
+    __builtin_amdgcn_s_setprio(1);
+    if (k + 2 < n_tiles) issue(k + 2);
+    if (k < n_tiles && visible(k)) scores(k);
+    if (k >= 1 && visible(k - 1)) weighted_sum(k - 1);
+    if (k + 2 < n_tiles) wait_vmcnt<kCopies>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_barrier();
+    if (k == n_tiles) break;
+    if (visible(k)) softmax(k);
+    __builtin_amdgcn_s_barrier();
   }
+  if (!late) __builtin_amdgcn_s_barrier();
 
   // epilogue: normalise and store the rows of this wave's queries
   const float l_tot = l_run + __shfl_xor(l_run, 32);
