@@ -47,8 +47,8 @@ constexpr int kKBatch = 8;  // k-steps per wave whose loads are in flight togeth
 template <int RT, int MT, int D>
 __device__ __forceinline__ void append_proj_body(const __bf16* __restrict__ h, const __bf16* __restrict__ w,
                                                  int n_tokens, int d_model, int chunk_len,
-                                                 float* __restrict__ partial, int bx, int by, int bz, int gz) {
-  __shared__ f32x16_t red[kProjWaves][RT][MT][64];
+                                                 float* __restrict__ partial, int bx, int by, int bz, int gz,
+                                                 MLA_LDS f32x4_t (*red)[RT][MT][4][64]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int r0 = bx * 32 * RT, kc = by;
   const int ksteps = chunk_len / 16 / kProjWaves;  // per wave
@@ -85,26 +85,33 @@ __device__ __forceinline__ void append_proj_body(const __bf16* __restrict__ h, c
             for (int mt = 0; mt < MT; ++mt)
               acc[rt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[mt][j], bw[rt][j], acc[rt][mt], 0, 0, 0);
     }
+    // registers 4q..4q+3 of each lane go to LDS as one 16-byte quad, quads
+    // of one q contiguous over the lanes (conflict-free stores and loads)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) red[wave][rt][mt][lane] = acc[rt][mt];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          red[wave][rt][mt][q][lane] = f32x4_t{acc[rt][mt][4 * q], acc[rt][mt][4 * q + 1], acc[rt][mt][4 * q + 2],
+                                               acc[rt][mt][4 * q + 3]};
     __syncthreads();
     // thread t sums registers 4*(t/64) .. +3 of lane t%64 over the 4 waves
     const int rl = threadIdx.x & 63, rq = threadIdx.x >> 6;
     for (int mt = 0; mt < mts; ++mt)
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4_t v = red[0][rt][mt][rq][rl];
+#pragma unroll
+        for (int wv = 1; wv < kProjWaves; ++wv) v += red[wv][rt][mt][rq][rl];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * rq + i;
-          float v = 0.f;
-#pragma unroll
-          for (int wv = 0; wv < kProjWaves; ++wv) v += red[wv][rt][mt][rl][r];
           const int n = m0 + 32 * mt + 8 * (r >> 2) + 4 * (rl >> 5) + (r & 3);
           if (n < n_tokens)
-            partial[(static_cast<int64_t>(kc) * n_tokens + n) * D + r0 + 32 * rt + (rl & 31)] = v;
+            partial[(static_cast<int64_t>(kc) * n_tokens + n) * D + r0 + 32 * rt + (rl & 31)] = v[i];
         }
+      }
     __syncthreads();
   }
 }
@@ -114,8 +121,9 @@ __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restri
                                                           const __bf16* __restrict__ w, int n_tokens,
                                                           int d_model, int chunk_len,
                                                           float* __restrict__ partial) {
+  __shared__ f32x4_t red[kProjWaves][RT][MT][4][64];
   append_proj_body<RT, MT, D>(h, w, n_tokens, d_model, chunk_len, partial, blockIdx.x, blockIdx.y, blockIdx.z,
-                              gridDim.z);
+                              gridDim.z, (MLA_LDS f32x4_t(*)[RT][MT][4][64])red);
 }
 
 constexpr int kMaxChunks = 16;  // contraction slices of the append GEMM
@@ -279,8 +287,8 @@ template <bool OUT_F32, int MT, int DR>
 __device__ __forceinline__ void absorb_q_body(const __bf16* __restrict__ q_nope, const __bf16* __restrict__ q_pe,
                                               const __bf16* __restrict__ w_uk,
                                               const int32_t* __restrict__ positions, int n_tokens, int n_h,
-                                              const RopeTable64& rope, void* __restrict__ q_out, int head, int ct) {
-  __shared__ __attribute__((aligned(16))) char wl[kDh * 256];
+                                              const RopeTable64& rope, void* __restrict__ q_out, int head, int ct,
+                                              MLA_LDS char* wl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const __bf16* W = w_uk + static_cast<int64_t>(head) * kDh * kDc + ct * 128;
   // the first RoPE item's inputs are requested first, so that its rotation
@@ -387,7 +395,9 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
                                                        const int32_t* __restrict__ positions,
                                                        int n_tokens, int n_h, RopeTable64 rope,
                                                        void* __restrict__ q_out) {
-  absorb_q_body<OUT_F32, MT, DR>(q_nope, q_pe, w_uk, positions, n_tokens, n_h, rope, q_out, blockIdx.x, blockIdx.y);
+  __shared__ __attribute__((aligned(16))) char wl[kDh * 256];
+  absorb_q_body<OUT_F32, MT, DR>(q_nope, q_pe, w_uk, positions, n_tokens, n_h, rope, q_out, blockIdx.x, blockIdx.y,
+                                 (MLA_LDS char*)wl);
 }
 
 // The append's down-projection and the latent query in one launch: the first
@@ -408,16 +418,31 @@ struct AppendAbsorbArgs {
   void* q_out;
 };
 
+// The two grids are interleaved (workgroup 2i appends, 2i+1 absorbs, while
+// both have workgroups left), so that the dispatcher starts both weight
+// streams at once; the two bodies share one LDS area.
 template <int D, bool OUT_F32, int MT_Q, int DR>
 __global__ void __launch_bounds__(256) append_absorb_kernel(AppendAbsorbArgs a, RopeTable64 rope) {
-  const int id = blockIdx.x, n_append = a.ax * a.ay * a.az;
-  if (id < n_append) {
-    append_proj_body<kAppendRTk, kAppendMTk, D>(a.h, a.w, a.n_tokens, a.d_model, a.chunk_len, a.partial,
-                                                 id % a.ax, (id / a.ax) % a.ay, id / (a.ax * a.ay), a.az);
+  constexpr int kRedBytes = kProjWaves * kAppendRTk * kAppendMTk * 4 * 64 * sizeof(f32x4_t);
+  constexpr int kWlBytes = kDh * 256;
+  __shared__ __attribute__((aligned(16))) char lds[kRedBytes > kWlBytes ? kRedBytes : kWlBytes];
+  const int id = blockIdx.x, n_append = a.ax * a.ay * a.az, ct_tiles = kDc / 128;
+  const int n_absorb = a.n_h * ct_tiles, both = min(n_append, n_absorb);
+  int ja = -1, jq = -1;
+  if (id < 2 * both) {
+    (id & 1 ? jq : ja) = id >> 1;
+  } else if (n_append > both) {
+    ja = id - both;
   } else {
-    const int j = id - n_append, ct_tiles = kDc / 128;
+    jq = id - both;
+  }
+  if (ja >= 0) {
+    append_proj_body<kAppendRTk, kAppendMTk, D>(
+        a.h, a.w, a.n_tokens, a.d_model, a.chunk_len, a.partial, ja % a.ax, (ja / a.ax) % a.ay,
+        ja / (a.ax * a.ay), a.az, (MLA_LDS f32x4_t(*)[kAppendRTk][kAppendMTk][4][64])(MLA_LDS char*)lds);
+  } else {
     absorb_q_body<OUT_F32, MT_Q, DR>(a.q_nope, a.q_pe, a.w_uk, a.positions, a.n_q, a.n_h, rope, a.q_out,
-                                     j / ct_tiles, j % ct_tiles);
+                                     jq / ct_tiles, jq % ct_tiles, (MLA_LDS char*)lds);
   }
 }
 
@@ -464,7 +489,7 @@ template <int VT, int MT>
 __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict__ o_lat,
                                                        const __bf16* __restrict__ w_uv, int n_tokens,
                                                        int n_h, int d_v, __bf16* __restrict__ out) {
-  __shared__ f32x16_t red[kProjWaves][VT][MT][64];
+  __shared__ f32x4_t red[kProjWaves][VT][MT][4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int head = blockIdx.x, v0 = 32 * VT * blockIdx.y;
   const int c_begin = wave * (kDc / kProjWaves);
@@ -502,26 +527,33 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[vt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[mt][j], bw[vt][j], acc[vt][mt], 0, 0, 0);
+    // registers 4q..4q+3 of each lane as one 16-byte quad, quads of one q
+    // contiguous over the lanes (conflict-free stores and loads)
 #pragma unroll
     for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) red[wave][vt][mt][lane] = acc[vt][mt];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          red[wave][vt][mt][q][lane] = f32x4_t{acc[vt][mt][4 * q], acc[vt][mt][4 * q + 1], acc[vt][mt][4 * q + 2],
+                                               acc[vt][mt][4 * q + 3]};
     __syncthreads();
     // thread t sums registers 4*(t/64) .. +3 of lane t%64 over the 4 waves
     const int rl = threadIdx.x & 63, rq = threadIdx.x >> 6;
     for (int mt = 0; mt < mts; ++mt)
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt)
+      for (int vt = 0; vt < VT; ++vt) {
+        f32x4_t v = red[0][vt][mt][rq][rl];
+#pragma unroll
+        for (int wv = 1; wv < kProjWaves; ++wv) v += red[wv][vt][mt][rq][rl];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * rq + i;
-          float v = 0.f;
-#pragma unroll
-          for (int wv = 0; wv < kProjWaves; ++wv) v += red[wv][vt][mt][rl][r];
           const int n = m0 + 32 * mt + 8 * (r >> 2) + 4 * (rl >> 5) + (r & 3);
           if (n < n_tokens)
-            out[(static_cast<int64_t>(n) * n_h + head) * d_v + v0 + 32 * vt + (rl & 31)] = f32_to_bf16(v);
+            out[(static_cast<int64_t>(n) * n_h + head) * d_v + v0 + 32 * vt + (rl & 31)] = f32_to_bf16(v[i]);
         }
+      }
     m0 += 32 * MT;
     if (m0 >= n_tokens) break;
     __syncthreads();
@@ -666,14 +698,13 @@ hipError_t launch_append_absorb_d(const AppendArgs& a, const AbsorbArgs& q, hipS
   g.q_out = fp8 ? q.workspace : q.q_lat;
   const dim3 grid(g.ax * g.ay * g.az + q.n_h * (kDc / 128));
   const RopeTable64 rope = rope_table(q.theta);
-  const bool one = q.n_tokens <= 32;
-  if (fp8) {
-    auto kern = one ? append_absorb_kernel<D, true, 1, DR> : append_absorb_kernel<D, true, 2, DR>;
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, g, rope);
-  } else {
-    auto kern = one ? append_absorb_kernel<D, false, 1, DR> : append_absorb_kernel<D, false, 2, DR>;
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, g, rope);
-  }
+  // one token tile per absorb pass: the fused kernel then needs 136 rather
+  // than 232 registers per lane, and three workgroups fit a CU instead of two
+  // (measured 2-3 us less per V3 bs64 step than two tiles per pass)
+  if (fp8)
+    hipLaunchKernelGGL((append_absorb_kernel<D, true, 1, DR>), grid, dim3(256), 0, st, g, rope);
+  else
+    hipLaunchKernelGGL((append_absorb_kernel<D, false, 1, DR>), grid, dim3(256), 0, st, g, rope);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_append_finish<D>(a, g.partial, n_chunks, st);
