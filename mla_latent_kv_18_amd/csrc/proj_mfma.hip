@@ -420,9 +420,12 @@ struct AppendAbsorbArgs {
 
 // The two grids are interleaved (workgroup 2i appends, 2i+1 absorbs, while
 // both have workgroups left), so that the dispatcher starts both weight
-// streams at once; the two bodies share one LDS area.
+// streams at once; the two bodies share one LDS area.  Four waves per SIMD
+// (at most 128 registers, 102 used): four workgroups fit a CU, so the 1088
+// workgroups of the V3 shape at 64 tokens run in about one round.
 template <int D, bool OUT_F32, int MT_Q, int DR>
-__global__ void __launch_bounds__(256) append_absorb_kernel(AppendAbsorbArgs a, RopeTable64 rope) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
+append_absorb_kernel(AppendAbsorbArgs a, RopeTable64 rope) {
   constexpr int kRedBytes = kProjWaves * kAppendRTk * kAppendMTk * 4 * 64 * sizeof(f32x4_t);
   constexpr int kWlBytes = kDh * 256;
   __shared__ __attribute__((aligned(16))) char lds[kRedBytes > kWlBytes ? kRedBytes : kWlBytes];
