@@ -18,6 +18,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace mla {
 namespace {
@@ -484,15 +485,25 @@ __global__ void __launch_bounds__(64) quantize_rows_fp8_kernel(const float* __re
 // W^UV_i, and wave w takes c in [128w, 128w+128) (8 k-steps) of each; the
 // wave partials are summed through LDS:
 // out[n][i][v] = sum_c o[n][i][c] W[i][v][c]
-// A pass covers MT 32-token tiles whose o_lat loads are issued together (the
-// first pass's with the weight loads); token rows past the end are clamped
-// to the last row and never stored.  Every workgroup of a head reads that
-// head's o_lat rows, so fewer, wider workgroups re-read less of them.
+// A pass covers MT 32-token tiles.  Their o_lat rows (the head's 512 latent
+// values, 1 KB each) are copied whole into LDS, one row per direct 1 KB copy
+// (token row r at r * 1024, its 16-byte chunk c at c ^ (r & 15), so that the
+// fragment reads of 32 rows at one column hit 16 distinct bank groups), and
+// every wave reads its A fragments from there; the first pass's copies are
+// issued with the weight loads.  Fragment loads straight from global memory
+// touched 32 rows per instruction.  Token rows past the end are clamped to
+// the last row and never stored.  The cross-wave reduction reuses the LDS
+// area.
 template <int VT, int MT>
 __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict__ o_lat,
                                                        const __bf16* __restrict__ w_uv, int n_tokens,
                                                        int n_h, int d_v, __bf16* __restrict__ out) {
-  __shared__ f32x4_t red[kProjWaves][VT][MT][4][64];
+  constexpr int kRowsBytes = 32 * MT * 1024;
+  constexpr int kRedBytes = kProjWaves * VT * MT * 4 * 64 * 16;
+  __shared__ __attribute__((aligned(1024))) char lds[kRowsBytes > kRedBytes ? kRowsBytes : kRedBytes];
+  MLA_LDS char* ol = (MLA_LDS char*)lds;
+  auto red = (MLA_LDS f32x4_t(*)[VT][MT][4][64])(MLA_LDS char*)lds;
+  const uint32_t ol_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ol));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int head = blockIdx.x, v0 = 32 * VT * blockIdx.y;
   const int c_begin = wave * (kDc / kProjWaves);
@@ -505,17 +516,28 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
     for (int j = 0; j < 8; ++j) bw[vt][j] = load8(wrow + 16 * j);
   }
   bf16x8_t oa[MT][8];
-  auto load_rows = [&](int m0) {
+  // copies of the pass's token rows: wave w moves rows w, w + 4, ...
+  auto copy_rows = [&](int m0) {
+#pragma unroll
+    for (int i = 0; i < 8 * MT; ++i) {
+      const int r = wave + kProjWaves * i;
+      const int n = min(m0 + r, n_tokens - 1);
+      dma16(o_lat + (static_cast<int64_t>(n) * n_h + head) * kDc + 8 * (lane ^ (r & 15)), ol_addr + r * 1024);
+    }
+  };
+  auto read_rows = [&]() {
+    wait_vmcnt<0>();
+    __syncthreads();  // every wave's rows (and weight loads) have landed
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int n = min(m0 + 32 * mt + l32, n_tokens - 1);
-      const __bf16* orow = o_lat + (static_cast<int64_t>(n) * n_h + head) * kDc + c_begin + 8 * hf;
+      const int r = 32 * mt + l32;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) oa[mt][j] = load8(orow + 16 * j);
+      for (int j = 0; j < 8; ++j)
+        oa[mt][j] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ol + r * 1024 + 16 * ((16 * wave + 2 * j + hf) ^ (r & 15)));
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the pass's loads in flight together
   };
-  load_rows(0);
+  copy_rows(0);
+  read_rows();
   for (int m0 = 0;;) {
     const int mts = min(MT, (n_tokens - m0 + 31) / 32);
     f32x16_t acc[VT][MT];
@@ -530,6 +552,7 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[vt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa[mt][j], bw[vt][j], acc[vt][mt], 0, 0, 0);
+    __syncthreads();  // every wave has read its rows: the area takes the reduction
     // registers 4q..4q+3 of each lane as one 16-byte quad, quads of one q
     // contiguous over the lanes (conflict-free stores and loads)
 #pragma unroll
@@ -559,8 +582,9 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
       }
     m0 += 32 * MT;
     if (m0 >= n_tokens) break;
-    __syncthreads();
-    load_rows(m0);
+    __syncthreads();  // the reduction is read: the area takes the next rows
+    copy_rows(m0);
+    read_rows();
   }
 }
 
