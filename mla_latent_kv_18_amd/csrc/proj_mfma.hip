@@ -500,21 +500,24 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
                                                        int n_h, int d_v, __bf16* __restrict__ out) {
   constexpr int kRowsBytes = 32 * MT * 1024;
   constexpr int kRedBytes = kProjWaves * VT * MT * 4 * 64 * 16;
-  __shared__ __attribute__((aligned(1024))) char lds[kRowsBytes > kRedBytes ? kRowsBytes : kRedBytes];
+  static_assert(kRedBytes <= kRowsBytes, "the reduction reuses the token rows' area");
+  __shared__ __attribute__((aligned(1024))) char lds[kRowsBytes + 32 * VT * 1024];
   MLA_LDS char* ol = (MLA_LDS char*)lds;
   auto red = (MLA_LDS f32x4_t(*)[VT][MT][4][64])(MLA_LDS char*)lds;
   const uint32_t ol_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ol));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int head = blockIdx.x, v0 = 32 * VT * blockIdx.y;
   const int c_begin = wave * (kDc / kProjWaves);
-  bf16x8_t bw[VT][8];
+  // the workgroup's W^UV_i rows (1 KB each) go to LDS the same way, after
+  // the token rows
+  MLA_LDS char* wl = ol + kRowsBytes;
+  const uint32_t wl_addr = ol_addr + kRowsBytes;
 #pragma unroll
-  for (int vt = 0; vt < VT; ++vt) {
-    const __bf16* wrow =
-        w_uv + (static_cast<int64_t>(head) * d_v + v0 + 32 * vt + l32) * kDc + c_begin + 8 * hf;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) bw[vt][j] = load8(wrow + 16 * j);
+  for (int i = 0; i < 8 * VT; ++i) {
+    const int r = wave + kProjWaves * i;
+    dma16(w_uv + (static_cast<int64_t>(head) * d_v + v0 + r) * kDc + 8 * (lane ^ (r & 15)), wl_addr + r * 1024);
   }
+  bf16x8_t bw[VT][8];
   bf16x8_t oa[MT][8];
   // copies of the pass's token rows: wave w moves rows w, w + 4, ...
   auto copy_rows = [&](int m0) {
@@ -536,8 +539,18 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const __bf16* __restrict_
         oa[mt][j] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ol + r * 1024 + 16 * ((16 * wave + 2 * j + hf) ^ (r & 15)));
     }
   };
+  auto read_weights = [&]() {
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      const int r = 32 * vt + l32;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        bw[vt][j] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(wl + r * 1024 + 16 * ((16 * wave + 2 * j + hf) ^ (r & 15)));
+    }
+  };
   copy_rows(0);
   read_rows();
+  read_weights();
   for (int m0 = 0;;) {
     const int mts = min(MT, (n_tokens - m0 + 31) / 32);
     f32x16_t acc[VT][MT];
@@ -747,7 +760,7 @@ hipError_t launch_append_absorb_mfma(const AppendArgs& a, const AbsorbArgs& q, h
 
 hipError_t launch_out_proj_mfma(const OutProjArgs& a, hipStream_t st) {
   constexpr int VT = kOutVT;
-  auto kern = a.n_tokens <= 32 ? out_proj_kernel<VT, 1> : out_proj_kernel<VT, 2>;
+  auto kern = out_proj_kernel<VT, 1>;  // 32 KB of token rows + 32 KB of weights: two workgroups per CU
   hipLaunchKernelGGL(kern, dim3(a.n_h, a.d_v / (32 * VT)), dim3(256), 0, st,
                      static_cast<const __bf16*>(a.o_lat), static_cast<const __bf16*>(a.w_uv),
                      a.n_tokens, a.n_h, a.d_v, static_cast<__bf16*>(a.out));
