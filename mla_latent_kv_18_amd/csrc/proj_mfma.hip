@@ -45,15 +45,29 @@ constexpr int kAppendMTk = 1;  // 32-token tiles per append pass
 constexpr int kKBatch = 8;  // k-steps per wave whose loads are in flight together
 
 // workgroup (bx, by, bz) of a (D / (32 RT), n_chunks, gz) grid
+// Hidden-state rows of one 32-token pass staged in LDS for the append GEMM
+// (chunk_len <= kStageMaxLen): row r's 16-byte chunk c at r * (C + 1) + c
+// with C = chunk_len / 8 chunks per row; the odd row stride puts the
+// fragment reads of 32 rows at one column on 16 distinct bank groups.  The
+// copies move whole 1 KB runs of that layout (the pad chunk repeats a valid
+// one).  Fragment loads straight from global memory touched 32 rows per
+// instruction.
+constexpr int kStageMaxLen = 512;
+constexpr int kStageBytes = (32 * (kStageMaxLen / 8 + 1) * 16 + 1023) / 1024 * 1024;  // 33 KB
+
 template <int RT, int MT, int D>
 __device__ __forceinline__ void append_proj_body(const __bf16* __restrict__ h, const __bf16* __restrict__ w,
                                                  int n_tokens, int d_model, int chunk_len,
                                                  float* __restrict__ partial, int bx, int by, int bz, int gz,
-                                                 MLA_LDS f32x4_t (*red)[RT][MT][4][64]) {
+                                                 MLA_LDS f32x4_t (*red)[RT][MT][4][64], MLA_LDS char* hs) {
+  static_assert(MT == 1, "the staged hidden rows hold one 32-token tile");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int r0 = bx * 32 * RT, kc = by;
   const int ksteps = chunk_len / 16 / kProjWaves;  // per wave
   const int k_begin = kc * chunk_len + wave * ksteps * 16;
+  const bool staged = chunk_len <= kStageMaxLen;
+  const int row_chunks = chunk_len / 8, stride = row_chunks + 1;
+  const uint32_t hs_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(hs));
   for (int m0 = bz * 32 * MT; m0 < n_tokens; m0 += gz * 32 * MT) {
     const int mts = min(MT, (n_tokens - m0 + 31) / 32);
     f32x16_t acc[RT][MT];
@@ -61,6 +75,15 @@ __device__ __forceinline__ void append_proj_body(const __bf16* __restrict__ h, c
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[rt][mt] = f32x16_t{};
+    if (staged) {
+      const int copies = (32 * stride + 63) / 64;
+      for (int i = wave; i < copies; i += kProjWaves) {
+        const int pidx = 64 * i + lane;
+        const int r = min(pidx / stride, 31), c = min(pidx - (pidx / stride) * stride, row_chunks - 1);
+        const int n = min(m0 + r, n_tokens - 1);
+        dma16(h + static_cast<int64_t>(n) * d_model + kc * chunk_len + 8 * c, hs_addr + i * 1024);
+      }
+    }
     for (int kb = 0; kb < ksteps; kb += kKBatch) {
       bf16x8_t bw[RT][kKBatch], ha[MT][kKBatch];
 #pragma unroll
@@ -69,12 +92,22 @@ __device__ __forceinline__ void append_proj_body(const __bf16* __restrict__ h, c
 #pragma unroll
         for (int j = 0; j < kKBatch; ++j) bw[rt][j] = load8(wrow + 16 * min(kb + j, ksteps - 1));
       }
+      if (staged) {
+        wait_vmcnt<0>();
+        __syncthreads();  // every wave's copies (and this batch's weight loads) have landed
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int n = min(m0 + 32 * mt + l32, n_tokens - 1);
-        const __bf16* hrow = h + static_cast<int64_t>(n) * d_model + k_begin + 8 * hf;
+        for (int j = 0; j < kKBatch; ++j) {
+          const int c = 2 * (wave * ksteps + min(kb + j, ksteps - 1)) + hf;
+          ha[0][j] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(hs + (l32 * stride + c) * 16);
+        }
+      } else {
 #pragma unroll
-        for (int j = 0; j < kKBatch; ++j) ha[mt][j] = load8(hrow + 16 * min(kb + j, ksteps - 1));
+        for (int mt = 0; mt < MT; ++mt) {
+          const int n = min(m0 + 32 * mt + l32, n_tokens - 1);
+          const __bf16* hrow = h + static_cast<int64_t>(n) * d_model + k_begin + 8 * hf;
+#pragma unroll
+          for (int j = 0; j < kKBatch; ++j) ha[mt][j] = load8(hrow + 16 * min(kb + j, ksteps - 1));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads in flight together
 #pragma unroll
@@ -86,6 +119,7 @@ __device__ __forceinline__ void append_proj_body(const __bf16* __restrict__ h, c
             for (int mt = 0; mt < MT; ++mt)
               acc[rt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[mt][j], bw[rt][j], acc[rt][mt], 0, 0, 0);
     }
+    if (staged) __syncthreads();  // every wave has read the staged rows (the reduction may share the area)
     // registers 4q..4q+3 of each lane go to LDS as one 16-byte quad, quads
     // of one q contiguous over the lanes (conflict-free stores and loads)
 #pragma unroll
@@ -122,9 +156,10 @@ __global__ void __launch_bounds__(256) append_proj_kernel(const __bf16* __restri
                                                           const __bf16* __restrict__ w, int n_tokens,
                                                           int d_model, int chunk_len,
                                                           float* __restrict__ partial) {
-  __shared__ f32x4_t red[kProjWaves][RT][MT][4][64];
+  __shared__ __attribute__((aligned(1024))) char lds[kStageBytes];
+  static_assert(kProjWaves * RT * MT * 4 * 64 * 16 <= kStageBytes, "the reduction shares the staging area");
   append_proj_body<RT, MT, D>(h, w, n_tokens, d_model, chunk_len, partial, blockIdx.x, blockIdx.y, blockIdx.z,
-                              gridDim.z, (MLA_LDS f32x4_t(*)[RT][MT][4][64])red);
+                              gridDim.z, (MLA_LDS f32x4_t(*)[RT][MT][4][64])(MLA_LDS char*)lds, (MLA_LDS char*)lds);
 }
 
 constexpr int kMaxChunks = 16;  // contraction slices of the append GEMM
@@ -289,7 +324,7 @@ __device__ __forceinline__ void absorb_q_body(const __bf16* __restrict__ q_nope,
                                               const __bf16* __restrict__ w_uk,
                                               const int32_t* __restrict__ positions, int n_tokens, int n_h,
                                               const RopeTable64& rope, void* __restrict__ q_out, int head, int ct,
-                                              MLA_LDS char* wl) {
+                                              MLA_LDS char* wl, MLA_LDS char* ql) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const __bf16* W = w_uk + static_cast<int64_t>(head) * kDh * kDc + ct * 128;
   // the first RoPE item's inputs are requested first, so that its rotation
@@ -313,18 +348,30 @@ __device__ __forceinline__ void absorb_q_body(const __bf16* __restrict__ q_nope,
     const int i = threadIdx.x + 256 * j;
     v[j] = load8(W + static_cast<int64_t>(i >> 4) * kDc + (i & 15) * 8);
   }
+  // The pass's query rows (the head's 128 content values, 256 B per token)
+  // are copied into LDS four rows per 1 KB copy, chunk c of row r at
+  // c ^ (r & 15), and every wave reads its A fragments from there (fragment
+  // loads straight from global memory touched 32 rows per instruction).
   bf16x8_t a[MT][kDh / 16];
-  auto load_queries = [&](int m0) {
+  const uint32_t ql_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ql));
+  auto copy_queries = [&](int m0) {
+#pragma unroll
+    for (int i = wave; i < 8 * MT; i += kProjWaves) {
+      const int r = 4 * i + (lane >> 4);
+      const int n = min(m0 + r, n_tokens - 1);
+      dma16(q_nope + (static_cast<int64_t>(n) * n_h + head) * kDh + 8 * ((lane & 15) ^ (r & 15)), ql_addr + i * 1024);
+    }
+  };
+  auto read_queries = [&]() {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int n = min(m0 + 32 * mt + l32, n_tokens - 1);
-      const __bf16* qr = q_nope + (static_cast<int64_t>(n) * n_h + head) * kDh + 8 * hf;
+      const int r = 32 * mt + l32;
 #pragma unroll
-      for (int ks = 0; ks < kDh / 16; ++ks) a[mt][ks] = load8(qr + 16 * ks);
+      for (int ks = 0; ks < kDh / 16; ++ks)
+        a[mt][ks] = *reinterpret_cast<MLA_LDS const bf16x8_t*>(ql + (r * 16 + ((2 * ks + hf) ^ (r & 15))) * 16);
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the pass's loads in flight together
   };
-  load_queries(0);
+  copy_queries(0);
   float cs = 1.f, sn = 0.f;
   if constexpr (DR > 0) rope_cos_sin_inv(pos, inv_freq, &cs, &sn);  // while the weight and query loads are in flight
 #pragma unroll
@@ -332,7 +379,9 @@ __device__ __forceinline__ void absorb_q_body(const __bf16* __restrict__ q_nope,
     const int i = threadIdx.x + 256 * j, r = i >> 4, ch = i & 15;
     *reinterpret_cast<MLA_LDS bf16x8_t*>((MLA_LDS char*)wl + (r * 16 + (ch ^ (4 * (r & 3)))) * 16) = v[j];
   }
-  __syncthreads();
+  wait_vmcnt<0>();
+  __syncthreads();  // the weight slice and every wave's query rows are in LDS
+  read_queries();
   const int L = lane & 15, cg = (lane >> 4) & 1;
   for (int m0 = 0;;) {
     f32x16_t acc[MT];
@@ -365,7 +414,11 @@ __device__ __forceinline__ void absorb_q_body(const __bf16* __restrict__ q_nope,
       }
     m0 += 32 * MT;
     if (m0 >= n_tokens) break;
-    load_queries(m0);
+    __syncthreads();  // every wave has read this pass's query rows
+    copy_queries(m0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    read_queries();
   }
   // RoPE part of the latent query
   if constexpr (DR == 0) return;
@@ -396,9 +449,9 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(const __bf16* __restrict_
                                                        const int32_t* __restrict__ positions,
                                                        int n_tokens, int n_h, RopeTable64 rope,
                                                        void* __restrict__ q_out) {
-  __shared__ __attribute__((aligned(16))) char wl[kDh * 256];
+  __shared__ __attribute__((aligned(1024))) char wl[kDh * 256 + 32 * MT * kDh * 2];
   absorb_q_body<OUT_F32, MT, DR>(q_nope, q_pe, w_uk, positions, n_tokens, n_h, rope, q_out, blockIdx.x, blockIdx.y,
-                                 (MLA_LDS char*)wl);
+                                 (MLA_LDS char*)wl, (MLA_LDS char*)wl + kDh * 256);
 }
 
 // The append's down-projection and the latent query in one launch: the first
@@ -427,9 +480,8 @@ struct AppendAbsorbArgs {
 template <int D, bool OUT_F32, int MT_Q, int DR>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4)))
 append_absorb_kernel(AppendAbsorbArgs a, RopeTable64 rope) {
-  constexpr int kRedBytes = kProjWaves * kAppendRTk * kAppendMTk * 4 * 64 * sizeof(f32x4_t);
-  constexpr int kWlBytes = kDh * 256;
-  __shared__ __attribute__((aligned(16))) char lds[kRedBytes > kWlBytes ? kRedBytes : kWlBytes];
+  constexpr int kAbsorbBytes = kDh * 256 + 32 * MT_Q * kDh * 2;  // weight slice + one pass's query rows
+  __shared__ __attribute__((aligned(1024))) char lds[kStageBytes > kAbsorbBytes ? kStageBytes : kAbsorbBytes];
   const int id = blockIdx.x, n_append = a.ax * a.ay * a.az, ct_tiles = kDc / 128;
   const int n_absorb = a.n_h * ct_tiles, both = min(n_append, n_absorb);
   int ja = -1, jq = -1;
@@ -443,10 +495,11 @@ append_absorb_kernel(AppendAbsorbArgs a, RopeTable64 rope) {
   if (ja >= 0) {
     append_proj_body<kAppendRTk, kAppendMTk, D>(
         a.h, a.w, a.n_tokens, a.d_model, a.chunk_len, a.partial, ja % a.ax, (ja / a.ax) % a.ay,
-        ja / (a.ax * a.ay), a.az, (MLA_LDS f32x4_t(*)[kAppendRTk][kAppendMTk][4][64])(MLA_LDS char*)lds);
+        ja / (a.ax * a.ay), a.az, (MLA_LDS f32x4_t(*)[kAppendRTk][kAppendMTk][4][64])(MLA_LDS char*)lds,
+        (MLA_LDS char*)lds);
   } else {
     absorb_q_body<OUT_F32, MT_Q, DR>(a.q_nope, a.q_pe, a.w_uk, a.positions, a.n_q, a.n_h, rope, a.q_out,
-                                     jq / ct_tiles, jq % ct_tiles, (MLA_LDS char*)lds);
+                                     jq / ct_tiles, jq % ct_tiles, (MLA_LDS char*)lds, (MLA_LDS char*)lds + kDh * 256);
   }
 }
 
