@@ -31,6 +31,7 @@
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "merge_row.h"
 
 namespace mla {
 namespace {
@@ -783,15 +784,14 @@ decode_pipe_kernel(DecodeParams p) {
   }
 }
 
-// Merge the chunk partials of one row: L = log sum_s exp(lse_s),
-// o = sum_s exp(lse_s - L) o_s.  One wave per (row, request).  The lse of the
-// first 64 splits (one per lane) and the partial rows of the first 8 splits
-// are requested together, before the request's length is known: slots of
-// splits past that length hold stale workspace contents and are masked out
-// after loading rather than skipped, so the common case costs one memory
-// round trip.  Further splits follow in batches of 8.  With xcd_group the
-// rows of request b run on XCD b % 8, where the pipelined kernel wrote the
-// request's partials, so that their reads can hit that XCD's L2.
+// Merge the chunk partials of one row (merge_row): one wave per (row,
+// request).  The lse of the first 64 splits (one per lane) and the partial
+// rows of the first 8 splits are requested together, before the request's
+// length is known: slots of splits past that length hold stale workspace
+// contents and are never used, so the common case costs one memory round
+// trip.  With xcd_group the rows of request b run on XCD b % 8, where the
+// pipelined kernel wrote the request's partials, so that their reads can hit
+// that XCD's L2.
 template <typename OutT>
 __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ o_part,
                                                      const float* __restrict__ lse_part,
@@ -817,58 +817,20 @@ __global__ void __launch_bounds__(64) combine_kernel(const __bf16* __restrict__ 
     last = ns_planned - 1;
   }
   const int64_t base = first * rows + row;
-  auto lse_of = [&](int s) { return lse_part[base + static_cast<int64_t>(s) * rows]; };
   auto part_of = [&](int s) {
     return *reinterpret_cast<const bf16x8_t*>(o_part + (base + static_cast<int64_t>(s) * rows) * kDc + lane * 8);
   };
   // Indices are clamped rather than branched on, so that every load issues
   // before the first wait.
   int T = seq_lens[b];
-  const float lse_lane = lse_of(min(lane, last));
+  const float lv = lse_part[base + static_cast<int64_t>(min(lane, last)) * rows];
   bf16x8_t x0[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) x0[j] = part_of(min(j, last));
   T = T < 0 ? 0 : (T > max_seq_len ? max_seq_len : T);
   const int ns = part_ptr != nullptr ? ns_planned : (T + split_tokens - 1) / split_tokens;
-  const float v0 = lane < ns ? lse_lane : -INFINITY;  // splits 0..63
-  float mx = v0;
-  for (int s = 64 + lane; s < ns; s += 64) mx = fmaxf(mx, lse_of(s));
-  mx = wave_max(mx);
   float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  float L = -INFINITY;
-  if (mx != -INFINITY) {
-    float sum = v0 == -INFINITY ? 0.f : __expf(v0 - mx);
-    for (int s = 64 + lane; s < ns; s += 64) {
-      const float v = lse_of(s);
-      sum += v == -INFINITY ? 0.f : __expf(v - mx);
-    }
-    L = mx + __logf(wave_sum(sum));
-    const float w_lane = v0 == -INFINITY ? 0.f : __expf(v0 - L);  // weight of split `lane`
-    auto weight = [&](int s) {  // s is uniform across the wave
-      return s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), s))
-                    : __expf(lse_of(s) - L);
-    };
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < ns) {
-        const float w = weight(j);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, static_cast<float>(x0[j][i]), acc[i]);
-      }
-    for (int s0 = 8; s0 < ns; s0 += 8) {
-      bf16x8_t x[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = s0 + j < ns ? part_of(s0 + j) : bf16x8_t{};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float w = s0 + j < ns ? weight(s0 + j) : 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, static_cast<float>(x[j][i]), acc[i]);
-      }
-    }
-  }
+  const float L = merge_row<8>(ns, lv, lse_part + base, rows, x0, part_of, acc);
   const int n = b * q_len + row / n_h, h = row % n_h;
   OutT* dst = o_lat + (static_cast<int64_t>(n) * n_h + h) * kDc + lane * 8;
   if constexpr (sizeof(OutT) == 2) {
