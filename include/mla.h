@@ -434,6 +434,17 @@ size_t mla_linear_workspace_size(int32_t m, int32_t n, int32_t k);
 mla_status_t mla_linear(const void* x, int32_t ldx, const void* w, int32_t m, int32_t n, int32_t k,
                         void* y, void* workspace, size_t workspace_bytes, mla_stream_t stream);
 
+/* Two projections of the same activations in one launch: y1 [m, n1] =
+ * x w1^T and y2 [m, n2] = x w2^T, e.g. the query path's q^C = W^UQ c^Q and
+ * the RoPE query input W^QR c^Q [MLA explainer, query-compression eq.(17);
+ * decoupled RoPE eq.(15)], which share c^Q.  The same as two mla_linear
+ * calls (up to the order of the fp32 partial sums); n1 and n2 multiples of
+ * 128; workspace: at least mla_linear_workspace_size(m, n1 + n2, k) bytes.
+ * Arguments and errors otherwise as for mla_linear. */
+mla_status_t mla_linear_pair(const void* x, int32_t ldx, int32_t m, int32_t k, const void* w1, int32_t n1,
+                             void* y1, const void* w2, int32_t n2, void* y2, void* workspace,
+                             size_t workspace_bytes, mla_stream_t stream);
+
 /* ------------------------------------------------------- absorbed weights
  * Formed once when a model is loaded, not per step.  act_dtype buffers
  * (bf16 or fp32), caller-owned device memory; fp32 accumulation.

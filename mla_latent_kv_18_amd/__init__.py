@@ -27,7 +27,7 @@ EXPORTS = ("mla_cache_row_bytes", "mla_cache_bytes_per_token", "mla_q_lat_row_by
            "mla_decode_plan_workspace_size", "mla_decode_plan", "mla_decode_plan_host", "mla_decode",
            "mla_decode_uniform_workspace_size", "mla_decode_uniform", "mla_decode_uniform_noalloc",
            "mla_decode_default_split",
-           "mla_out_proj", "mla_linear_workspace_size", "mla_linear", "mla_prefill_attention", "mla_prefill_attention_varlen",
+           "mla_out_proj", "mla_linear_workspace_size", "mla_linear", "mla_linear_pair", "mla_prefill_attention", "mla_prefill_attention_varlen",
            "mla_absorb_output_weights", "mla_absorb_query_weights",
            "mla_status_string", "mla_last_error_message", "mla_version")
 
@@ -98,6 +98,7 @@ def lib():
         "mla_decode_default_split": (I32, [DP, I32, I32, I32]),
         "mla_out_proj": (I32, [DP, P, P, I32, P, P]),
         "mla_linear_workspace_size": (SZ, [I32, I32, I32]),
+        "mla_linear_pair": (I32, [P, I32, I32, I32, P, I32, P, P, I32, P, P, SZ, P]),
         "mla_prefill_attention": (I32, [DP, P, P, P, P, I32, P, I32, P, P, P]),
         "mla_prefill_attention_varlen": (I32, [DP, P, P, P, P, I32, P, P, P, I32, I32, I32, P, P, P]),
         "mla_linear": (I32, [P, I32, P, I32, I32, I32, P, P, SZ, P]),
@@ -280,6 +281,25 @@ def linear(x, w, y, workspace=None, ldx=None):
         workspace, _ = _workspace(need, y.device)
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().mla_linear(xp, ldx, _ptr(w), m, n, k, _ptr(y), _ptr(workspace), nbytes, _stream(y.device)))
+
+
+def linear_pair(x, w1, y1, w2, y2, workspace=None):
+    """mla_linear_pair: y1 [m, n1] = x w1^T and y2 [m, n2] = x w2^T in one
+    launch (x contiguous [m, k]; y1, y2 any contiguous tensors with m rows)."""
+    m, k = x.shape[0], x.numel() // x.shape[0]
+    n1, n2 = w1.shape[0], w2.shape[0]
+    if not x.is_contiguous() or w1.numel() != n1 * k or w2.numel() != n2 * k:
+        raise ValueError(f"linear_pair: x {tuple(x.shape)} does not match w1 {tuple(w1.shape)}, w2 {tuple(w2.shape)}")
+    if y1.numel() != m * n1 or y2.numel() != m * n2:
+        raise ValueError("linear_pair: outputs do not match [m, n1] and [m, n2]")
+    if not all(t.dtype == torch.bfloat16 for t in (x, w1, y1, w2, y2)):
+        raise ValueError("linear_pair: all tensors must be bfloat16")
+    need = linear_workspace_size(m, n1 + n2, k)
+    if workspace is None:
+        workspace, _ = _workspace(need, y1.device)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().mla_linear_pair(_ptr(x), k, m, k, _ptr(w1), n1, _ptr(y1), _ptr(w2), n2, _ptr(y2), _ptr(workspace),
+                                 nbytes, _stream(y1.device)))
 
 
 def prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out, lse=None):

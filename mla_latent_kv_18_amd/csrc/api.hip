@@ -633,6 +633,22 @@ mla_status_t mla_linear(const void* x, int32_t ldx, const void* w, int32_t m, in
   return hip_status(mla::launch_linear(a, static_cast<hipStream_t>(stream)), "mla_linear");
 }
 
+mla_status_t mla_linear_pair(const void* x, int32_t ldx, int32_t m, int32_t k, const void* w1, int32_t n1, void* y1,
+                             const void* w2, int32_t n2, void* y2, void* workspace, size_t workspace_bytes,
+                             mla_stream_t stream) {
+  if (m < 0 || n1 <= 0 || n2 <= 0 || k <= 0) return fail(MLA_ERR_INVALID_ARGUMENT, "m < 0 or n1, n2, k <= 0");
+  if (ldx < k || ldx % 8 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "ldx must be >= k and a multiple of 8 (got %d)", ldx);
+  if (n1 % 128 != 0 || n2 % 128 != 0 || k % 16 != 0)
+    return fail(MLA_ERR_UNSUPPORTED, "linear pair needs n1, n2 %% 128 == 0 and k %% 16 == 0 (got %d, %d, %d)", n1, n2, k);
+  if (m == 0) return hip_status(hipSuccess, "");
+  if (!x || !w1 || !y1 || !w2 || !y2) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+  const size_t need = mla_linear_workspace_size(m, n1 + n2, k);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE_TOO_SMALL, "linear pair needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  mla::LinearArgs a{x, w1, m, n1, k, ldx, y1, workspace};
+  return hip_status(mla::launch_linear_pair(a, w2, n2, y2, static_cast<hipStream_t>(stream)), "mla_linear_pair");
+}
+
 mla_status_t mla_absorb_output_weights(const mla_dims_t* dims, const void* w_o, const void* w_uv, void* b,
                                        mla_stream_t stream) {
   Resolved r;

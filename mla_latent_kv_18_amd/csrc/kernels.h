@@ -136,6 +136,9 @@ hipError_t launch_prefill_attention(const PrefillArgs&, hipStream_t);
 int linear_chunks(int m, int n, int k);
 size_t linear_workspace(int m, int n, int k);
 hipError_t launch_linear(const LinearArgs&, hipStream_t);
+// y [m, n] = x w^T and y2 [m, n2] = x w2^T in one launch (n2 % 128 == 0;
+// workspace sized by linear_workspace(m, n + n2, k))
+hipError_t launch_linear_pair(const LinearArgs&, const void* w2, int n2, void* y2, hipStream_t);
 
 // merge of the chunk partials that a split decode left in the workspace
 // (xcd_group: the partials of request b were written on XCD b % 8, batch % 8 == 0)

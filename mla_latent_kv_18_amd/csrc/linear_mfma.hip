@@ -41,18 +41,25 @@ constexpr int kLinMaxZ = 16;
 
 __device__ __forceinline__ bf16x8_t load8(const __bf16* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
+// Two weight matrices over the same activations run as one problem of
+// N = n1 + n2 rows: row groups below n1 read w and store into y (rows n1
+// apart), the others read w2 and store into y2 (rows N - n1 apart); fp32
+// partials use the combined N.  A single matrix has n1 = N.
 template <int MT>
 __global__ void __launch_bounds__(256) linear_kernel(const __bf16* __restrict__ x, const __bf16* __restrict__ w,
                                                      int ldx, int M, int N, int K, int chunk_len,
-                                                     float* __restrict__ partial, __bf16* __restrict__ y) {
+                                                     float* __restrict__ partial, __bf16* __restrict__ y,
+                                                     const __bf16* __restrict__ w2, int n1, __bf16* __restrict__ y2) {
   constexpr int kTile = 32 * MT * 256;  // bytes of one batch's activation tile
   constexpr int kPer = 2 * MT;          // 16-byte tile chunks copied per thread
   __shared__ __attribute__((aligned(16))) char xs[2][kTile];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hf = lane >> 5, l32 = lane & 31;
   const int n0 = blockIdx.x * kLinRows + 32 * wave, kc = blockIdx.y;
+  const bool second = static_cast<int>(blockIdx.x) * kLinRows >= n1;
   const int ksteps = chunk_len / 16, nb = (ksteps + kLinBatch - 1) / kLinBatch;
   const int64_t k_begin = static_cast<int64_t>(kc) * chunk_len;
-  const __bf16* wrow = w + static_cast<int64_t>(n0 + l32) * K + k_begin + 8 * hf;
+  const __bf16* wrow = (second ? w2 + static_cast<int64_t>(n0 - n1 + l32) * K : w + static_cast<int64_t>(n0 + l32) * K) +
+                       k_begin + 8 * hf;
   for (int m0 = blockIdx.z * 32 * MT; m0 < M; m0 += gridDim.z * 32 * MT) {
     // chunk i = tid + 256 s of the tile: row r = i / 16, 16-byte chunk c = i % 16
     // (k-step c / 2 of the batch, half c % 2), stored at chunk c ^ (r % 16) of row r
@@ -115,8 +122,10 @@ __global__ void __launch_bounds__(256) linear_kernel(const __bf16* __restrict__ 
         if (m < M) {
           if (partial != nullptr)
             partial[(static_cast<int64_t>(kc) * M + m) * N + n0 + l32] = acc[mt][r];
+          else if (second)
+            y2[static_cast<int64_t>(m) * (N - n1) + n0 - n1 + l32] = f32_to_bf16(acc[mt][r]);
           else
-            y[static_cast<int64_t>(m) * N + n0 + l32] = f32_to_bf16(acc[mt][r]);
+            y[static_cast<int64_t>(m) * n1 + n0 + l32] = f32_to_bf16(acc[mt][r]);
         }
       }
     __syncthreads();  // the next pass rewrites the tiles
@@ -200,7 +209,8 @@ __global__ void __launch_bounds__(64 * kWsWaves) linear_ws_kernel(const __bf16* 
 // (MAXC >= n_chunks loads; the ones past n_chunks repeat the last slice).
 template <int MAXC>
 __global__ void __launch_bounds__(256) linear_reduce_kernel(const float* __restrict__ partial, int n_chunks, int M,
-                                                            int N, __bf16* __restrict__ y) {
+                                                            int N, __bf16* __restrict__ y, int n1,
+                                                            __bf16* __restrict__ y2) {
   const int m = blockIdx.y, q = blockIdx.x * 256 + threadIdx.x;
   if (4 * q >= N) return;
   f32x4_t v[MAXC];
@@ -214,7 +224,8 @@ __global__ void __launch_bounds__(256) linear_reduce_kernel(const float* __restr
   bf16x4_t b;
 #pragma unroll
   for (int i = 0; i < 4; ++i) b[i] = f32_to_bf16(s[i]);
-  *reinterpret_cast<bf16x4_t*>(y + static_cast<int64_t>(m) * N + 4 * q) = b;
+  __bf16* dst = 4 * q < n1 ? y + static_cast<int64_t>(m) * n1 + 4 * q : y2 + static_cast<int64_t>(m) * (N - n1) + 4 * q - n1;
+  *reinterpret_cast<bf16x4_t*>(dst) = b;
 }
 
 }  // namespace
@@ -257,22 +268,28 @@ hipError_t launch_linear(const LinearArgs& a, hipStream_t st) {
                        static_cast<__bf16*>(a.y));
     return hipGetLastError();
   }
-  const int chunks = linear_chunks(a.m, a.n, a.k);
+  return launch_linear_pair(a, nullptr, 0, nullptr, st);
+}
+
+hipError_t launch_linear_pair(const LinearArgs& a, const void* w2, int n2, void* y2, hipStream_t st) {
+  const int n = a.n + n2;
+  const int chunks = linear_chunks(a.m, n, a.k);
   const int mt = a.m <= 32 ? 1 : 2;
   int groups = (a.m + 32 * mt - 1) / (32 * mt);
   groups = groups > kLinMaxZ ? kLinMaxZ : groups;
   float* partial = chunks > 1 ? static_cast<float*>(a.workspace) : nullptr;
-  const dim3 grid(a.n / kLinRows, chunks, groups);
+  const dim3 grid(n / kLinRows, chunks, groups);
   auto kern = mt == 1 ? linear_kernel<1> : linear_kernel<2>;
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const __bf16*>(a.x), static_cast<const __bf16*>(a.w),
-                     a.ldx, a.m, a.n, a.k, a.k / chunks, partial, static_cast<__bf16*>(a.y));
+                     a.ldx, a.m, n, a.k, a.k / chunks, partial, static_cast<__bf16*>(a.y),
+                     static_cast<const __bf16*>(w2), a.n, static_cast<__bf16*>(y2));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || chunks == 1) return e;
   auto red = chunks <= 4 ? linear_reduce_kernel<4>
              : chunks <= 8 ? linear_reduce_kernel<8>
              : chunks <= 16 ? linear_reduce_kernel<16> : linear_reduce_kernel<kLinMaxChunks>;
-  hipLaunchKernelGGL(red, dim3((a.n / 4 + 255) / 256, a.m), dim3(256), 0, st, partial, chunks, a.m, a.n,
-                     static_cast<__bf16*>(a.y));
+  hipLaunchKernelGGL(red, dim3((n / 4 + 255) / 256, a.m), dim3(256), 0, st, partial, chunks, a.m, n,
+                     static_cast<__bf16*>(a.y), a.n, static_cast<__bf16*>(y2));
   return hipGetLastError();
 }
 

@@ -12,8 +12,8 @@ import numpy as np
 import torch
 
 from . import (absorb_output_weights, absorb_q, absorb_query_weights, append_absorb, append_latent, decode, decode_plan,
-               decode_uniform, decode_uniform_workspace_size, lib, linear, linear_workspace_size, make_dims,
-               out_proj)
+               decode_uniform, decode_uniform_workspace_size, lib, linear, linear_pair, linear_workspace_size,
+               make_dims, out_proj)
 
 
 def _dev(a, device, fmt):
@@ -152,16 +152,20 @@ class BlockStep(DeviceStep):
         self.w_o = _dev(block["w_o"], device, act)
         self.c_q = torch.empty(N, self.d_cq, dtype=torch.bfloat16, device=device)
         self.u = torch.empty(N, w.d_model, dtype=torch.bfloat16, device=device)
-        shapes = [(self.d_cq, w.d_model), (w.n_h * w.d_h, self.d_cq), (w.n_h * w.d_r, self.d_cq),
+        shapes = [(self.d_cq, w.d_model), (w.n_h * w.d_h, self.d_cq), (w.n_h * (w.d_h + w.d_r), self.d_cq),
                   (w.d_model, w.n_h * w.d_v), (w.d_model, w.n_h * w.d_c)]
         nws = max(linear_workspace_size(N, n, k) for n, k in shapes)
         self.linear_ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=device)
         self.b = None
 
     def query(self):
+        """c^Q = W^DQ h, then W^UQ c^Q and W^QR c^Q in one mla_linear_pair call
+        (a model without the RoPE part runs W^UQ alone)."""
         linear(self.h, self.w_dq, self.c_q, workspace=self.linear_ws)
-        linear(self.c_q, self.w_uq, self.q_nope, workspace=self.linear_ws)
-        linear(self.c_q, self.w_qr, self.q_pe, workspace=self.linear_ws)
+        if self.w.d_r > 0:
+            linear_pair(self.c_q, self.w_uq, self.q_nope, self.w_qr, self.q_pe, workspace=self.linear_ws)
+        else:
+            linear(self.c_q, self.w_uq, self.q_nope, workspace=self.linear_ws)
 
     def o_proj(self):
         linear(self.out, self.w_o, self.u, workspace=self.linear_ws)

@@ -52,6 +52,25 @@ def test_linear_matches_definition(m, n, k):
     assert ov.rel_err(_host_bf16(y), x64 @ w64.T) <= ov.TOL["bf16"]
 
 
+# (m, n1, n2, k): one token, a ragged token tail, one and several k slices,
+# and the V3 query path's W^UQ and W^QR at 64 tokens
+PAIR_SHAPES = [(1, 128, 256, 48), (33, 256, 128, 4096), (100, 384, 128, 1024), (64, 16384, 8192, 1536)]
+
+
+@pytest.mark.parametrize("m,n1,n2,k", PAIR_SHAPES)
+def test_linear_pair_matches_definition(m, n1, n2, k):
+    rng = np.random.default_rng(m * 131 + n1 + 7 * n2 + k)
+    x, x64 = _bf16(rng, (m, k))
+    w1, w164 = _bf16(rng, (n1, k), 1.0 / np.sqrt(k))
+    w2, w264 = _bf16(rng, (n2, k), 1.0 / np.sqrt(k))
+    y1 = torch.empty(m, n1, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty(m, n2, dtype=torch.bfloat16, device="cuda")
+    mla.linear_pair(x, w1, y1, w2, y2)
+    torch.cuda.synchronize()
+    assert ov.rel_err(_host_bf16(y1), x64 @ w164.T) <= ov.TOL["bf16"]
+    assert ov.rel_err(_host_bf16(y2), x64 @ w264.T) <= ov.TOL["bf16"]
+
+
 def test_linear_strided_rows():
     """x read from rows ldx elements apart (the latent part of cache rows)."""
     rng = np.random.default_rng(6)
