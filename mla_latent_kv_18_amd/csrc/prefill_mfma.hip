@@ -17,26 +17,35 @@
 // w owns queries 32w..32w+31 of the block.  The keys and values of each
 // 64-token tile are staged once in LDS and shared by the eight waves (a
 // workgroup of 128 queries fetched twice the bytes per flop and was bound by
-// them).  Per 64-key tile, per wave (bf16 MFMA 32x32x16, fp32 accumulate), as
-// two 32-key sub-tiles whose score chains run side by side:
+// them), three tiles ahead of the one computed.  One step of a wave is one
+// hand-ordered instruction stream over one tile (prefill_asm.inc, written by
+// gen_prefill_asm.py; bf16 MFMA 32x32x16, fp32 accumulate), the tile split
+// into 32-key halves A and B:
 //   S^T[key, q] = sum_d K[key, d] Q[q, d]     A = K tile (ds_read_b128),
 //                                             B = Q^T, register resident
-//   (two chains over the even and odd k-steps), online softmax over the keys
-//   (per lane: one query, 16 keys; the other 16 keys of that query sit in
-//   lane ^ 32), rescaling O only in the tiles where some query's maximum grows
+//   softmax numerators p = 2^(s * scale - m_ref) (per lane: one query, 16
+//   keys of a half; the other 16 keys of that query sit in lane ^ 32)
 //   O^T[v, q] += sum_key V^T[v, key] P^T[key, q]   A = V^T read with
 //                                             ds_read_b64_tr_b16, B = P^T
 //                                             straight from the S^T registers
-// The token order inside each 16-key MFMA k-step is the same permutation on
-// both operands (register r of the scores holds key 8(r/4) + 4hf + r%4), so
-// P never leaves registers.  The query's RoPE part is rotated as it is
-// loaded (pair k of the 64-wide part: dims k and k + 32, angle
-// pos / theta^(2k/64)).  Query blocks run longest first.
+// in the order scores A, scores B with the softmax of A between them, sum A
+// with the softmax of B between them, sum B.  The token order inside each
+// 16-key MFMA k-step is the same permutation on both operands (register r of
+// the scores holds key 8(r/4) + 4hf + r%4), so P never leaves registers.
+// The reference m_ref is fixed per query at its first tile (key 0 is
+// visible to every query), so the accumulators are never rescaled; if a
+// later score exceeds it by more than 64 (log2 units), past which the
+// numerators could overflow, the workgroup redoes its pass with the largest
+// score as reference.  The query's RoPE part is rotated as it is loaded
+// (pair k of the 64-wide part: dims k and k + 32, angle pos / theta^(2k/64))
+// and rounded to bf16 like the rest of the query.  Query blocks run longest
+// first.
 #include <cmath>
 
 #include "device_common.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "prefill_asm.inc"
 
 namespace mla {
 namespace {
@@ -79,7 +88,7 @@ __device__ __forceinline__ bf16x8_t ld8(const __bf16* p) { return *reinterpret_c
 // r * 16 + (c ^ 2(r & 3)), so the four rows of a transposed read hit four
 // different 32-byte spans.  Tiles arrive by direct global->LDS copies (lane l of copy i fills
 // slot 64i + l, so the layout is chosen by which chunk each lane fetches),
-// two tiles ahead of the one being computed (four tile buffers).
+// three tiles ahead of the one being computed (four tile buffers).
 __device__ __forceinline__ int k_slot(int r, int c) { return r * kKC + (c ^ ((r >> 1) & 7)); }
 
 __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillParams p, RopeTable64 rope) {
@@ -161,157 +170,128 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
     }
   }
 
-  // copies of tile k into buffer bi: copy i = wave + 8j; the first 24 fill the
-  // key rows, the last 16 the value rows
-  auto issue = [&](int k) {
+  // Copies of tile k into buffer k % kNBuf: copy i = wave + 8j of the
+  // tile's 40 lands at buffer offset 1024 i; lane l fills slot 64 i + l.
+  // Copies 0-2 of a wave fill key rows, copies 3, 4 value rows.  A key lane's
+  // source is its chunk of key row 0 of the sequence (cp) plus the row times
+  // the stride of the array the chunk comes from (cs); a value lane's is the
+  // tile's first value row (a uniform base) plus row * n_h * 256 B plus its
+  // column.  The rows (0..63) and value columns are packed into d0, d1.
+  const char* cp[3];
+  uint32_t cs[3];
+  uint32_t d0 = 0, d1 = 0;
 #pragma unroll
-    for (int j = 0; j < kCopies; ++j) {
-      const int i = wave + kWaves * j, slot = 64 * i + lane;
-      const __bf16* g;
-      if (i < kKTile / 1024) {
-        const int r = slot / kKC, c = (slot - r * kKC) ^ ((r >> 1) & 7);
-        const int64_t key = k_row0 + min(kTK * k + r, Tk - 1);
-        g = c < 16 ? p.k_nope + (key * p.n_h + head) * kPH + 8 * c
-                   : p.k_rope + key * p.k_rope_stride + 8 * (c - 16);
+  for (int j = 0; j < kCopies; ++j) {
+    const int i = wave + kWaves * j, slot = 64 * i + lane;
+    if (j < 3) {
+      const int r = slot / kKC, c = (slot - r * kKC) ^ ((r >> 1) & 7);
+      d0 |= static_cast<uint32_t>(r) << (8 * j);
+      if (c < 16) {
+        cp[j] = reinterpret_cast<const char*>(p.k_nope + (static_cast<int64_t>(k_row0) * p.n_h + head) * kPH + 8 * c);
+        cs[j] = p.n_h * kPH * 2;
       } else {
-        const int s2 = slot - kKTile / 16, r = s2 / kVS, c = (s2 - r * kVS) ^ (2 * (r & 3));
-        const int64_t key = k_row0 + min(kTK * k + r, Tk - 1);
-        g = p.v + (key * p.n_h + head) * kPV + 8 * c;
+        cp[j] = reinterpret_cast<const char*>(p.k_rope + static_cast<int64_t>(k_row0) * p.k_rope_stride + 8 * (c - 16));
+        cs[j] = p.k_rope_stride * 2;
       }
-      dma16(g, tiles_addr + (k % kNBuf) * kBuf + i * 1024);
+    } else {
+      const int s2 = slot - kKTile / 16, r = s2 / kVS, c = (s2 - r * kVS) ^ (2 * (r & 3));
+      if (j == 3) d0 |= static_cast<uint32_t>(r) << 24, d1 |= static_cast<uint32_t>(16 * c) << 8;
+      else d1 |= static_cast<uint32_t>(r) | static_cast<uint32_t>(16 * c) << 16;
     }
+  }
+  const uint32_t vs = p.n_h * kPV * 2;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  auto issue = [&](int k) {
+    const int row0 = kTK * k;
+    const int rlast = min(kTK - 1, Tk - 1 - row0);
+    const char* vbase = reinterpret_cast<const char*>(p.v + ((static_cast<int64_t>(k_row0) + row0) * p.n_h + head) * kPV);
+    const uint32_t cd = __builtin_amdgcn_readfirstlane(tiles_addr + (k % kNBuf) * kBuf + wave * 1024);
+    asm volatile(MLA_PF_COPY
+                 :
+                 : [d0] "v"(d0), [d1] "v"(d1), [cp0] "v"(cp[0]), [cp1] "v"(cp[1]), [cp2] "v"(cp[2]),
+                   [cs0] "v"(cs[0]), [cs1] "v"(cs[1]), [cs2] "v"(cs[2]), [rlast] "s"(rlast), [row0] "s"(row0),
+                   [vbase] "s"(vbase), [vs] "s"(vs), [cd] "s"(cd)
+                 : MLA_PF_ASM_SCRATCH, "vcc", "m0", "memory");
   };
+#pragma clang diagnostic pop
 
   f32x16_t oacc[kPV / 32];
-#pragma unroll
-  for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
   const int last_key = min(ctx + qb * kQB + kQB - 1, Tk - 1);
   const int n_tiles = last_key / kTK + 1;
   // the wave's queries see keys up to ctx + q0 + 31 (its last query), and
   // every key of a tile up to min(ctx + q0, Tk - 1) (its first query's last)
   const int wave_last = ctx + q0 + 31;
   const int wave_full = min(ctx + q0, Tk - 1);
-  auto visible = [&](int k) { return kTK * k <= wave_last; };
+  const int vis_lim = vis - 4 * hf;
+  const float scale = p.scale_log2;
 
-  f32x16_t sc[2];
-  bf16x8_t pf[4];
-  // scores of tile k: S^T for the two 32-key sub-tiles, two independent
-  // chains; key fragments are read two k-steps ahead
-  auto scores = [&](int k) {
-    MLA_LDS const char* ktile = tiles + (k % kNBuf) * kBuf;
-    auto kread = [&](int s, int sub) {
-      return *reinterpret_cast<MLA_LDS const bf16x8_t*>(ktile + sub * (32 * kKC * 16) + kq_off[s & 3] + 128 * (s >> 2));
-    };
-    constexpr int kAhead = 2;
-    bf16x8_t kf[kAhead][2];
-#pragma unroll
-    for (int s = 0; s < kAhead; ++s)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) kf[s][sub] = kread(s, sub);
-    sc[0] = f32x16_t{};
-    sc[1] = f32x16_t{};
-#pragma unroll
-    for (int s = 0; s < kPD / 16; ++s)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const bf16x8_t cur = kf[s % kAhead][sub];
-        if (s + kAhead < kPD / 16) kf[s % kAhead][sub] = kread(s + kAhead, sub);
-        sc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[s], sc[sub], 0, 0, 0);
-      }
-  };
-  // O^T += V^T P^T for tile k (k-steps 0, 1 sum the first sub-tile's
-  // values, 2, 3 the second's); value fragments are read one MFMA ahead
-  auto weighted_sum = [&](int k) {
-    MLA_LDS char* vtile = tiles + (k % kNBuf) * kBuf + kKTile;
-    auto vread = [&](int i) {
-      const int ks = i >> 2, ct = i & 3;
-      MLA_LDS char* vb = vtile + (ks >> 1) * (32 * kVS * 16) + (ks & 1) * 4096 + 128 * (ct >> 1);
-      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[0][ct & 1]));
-      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<MLA_LDS i16x4_t*>(vb + pv_off[1][ct & 1]));
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8_t vf[2];
-    vf[0] = vread(0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + 1 < 16) vf[(i + 1) & 1] = vread(i + 1);
-      oacc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i & 1], pf[i >> 2], oacc[i & 3], 0, 0, 0);
-    }
-  };
-  // online softmax of tile k's scores: numerators P (bf16) for the next
-  // weighted sum, running maximum and sum, O rescaled where a maximum grew.
-  // The scale goes into the exponent's fma (the maximum is taken on the raw
-  // scores; the scale is positive); keys are masked only in tiles that reach
-  // past some query's last visible key.
-  auto softmax = [&](int k) {
-    const int key0 = kTK * k;
-    if (key0 + kTK - 1 > wave_full) {
-      // register r of sub-tile u holds key key0 + 32u + 8(r/4) + 4hf + r%4
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * sub + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sc[sub][r] = key <= vis ? sc[sub][r] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[sub][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // key 0 is visible to every query, so m_new is finite from the first tile on
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(sc[sub][r], p.scale_log2, -m_new));
-        psum += pr;
-        pf[2 * sub + (r >> 3)][r & 7] = f32_to_bf16(pr);
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // the accumulators are rescaled only when some query's maximum grew
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-      for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] *= alpha;
-    }
-  };
+#define MLA_PF_OUT                                                                             \
+  [o0] "+v"(oacc[0]), [o1] "+v"(oacc[1]), [o2] "+v"(oacc[2]), [o3] "+v"(oacc[3]),             \
+      [mref] "+v"(m_ref), [mseen] "+v"(m_seen), [lrun] "+v"(l_run)
+#define MLA_PF_IN                                                                              \
+  [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]),         \
+      [q5] "v"(qf[5]), [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]),     \
+      [q10] "v"(qf[10]), [q11] "v"(qf[11]), [kq0] "v"(kq_off[0]), [kq1] "v"(kq_off[1]),        \
+      [kq2] "v"(kq_off[2]), [kq3] "v"(kq_off[3]), [va0] "v"(pv_off[0][0]),                     \
+      [va1] "v"(pv_off[0][1]), [va2] "v"(pv_off[1][0]), [va3] "v"(pv_off[1][1]), [kb] "s"(kb),  \
+      [vb] "s"(vb), [scale] "s"(scale), [lim] "v"(lim), [msk] "s"(msk)
+#define MLA_PF_CLOBBER MLA_PF_ASM_SCRATCH, "vcc", "scc", "memory"
 
-  // Two groups of four waves (waves w and w + 4 share a SIMD) run the same
-  // phase sequence -- matrix phase k (scores of tile k, weighted sum of tile
-  // k-1, copies of tile k+2), softmax phase k -- with the second group one
-  // phase behind, so that on every SIMD one wave's softmax runs beside the
-  // other wave's MFMAs.  Barriers separate the phases.  Tile k+2 goes into
-  // the buffer of tile k-2, whose values both groups summed in their matrix
-  // phase k-1; each wave's copies of tile k+1 have landed by the end of its
-  // matrix phase k.
-  if (n_tiles > 0) issue(0);
-  if (n_tiles > 1) issue(1);
-  if (n_tiles > 1) wait_vmcnt<kCopies>();
-  else wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();  // tile 0 visible to all
-  const bool late = wave >= kWaves / 2;
-  if (late) __builtin_amdgcn_s_barrier();
-  for (int k = 0;; ++k) {
-    __builtin_amdgcn_s_setprio(1);
-    if (k + 2 < n_tiles) issue(k + 2);
-    if (k < n_tiles && visible(k)) scores(k);
-    if (k >= 1 && visible(k - 1)) weighted_sum(k - 1);
-    if (k + 2 < n_tiles) wait_vmcnt<kCopies>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_barrier();
-    if (k == n_tiles) break;
-    if (visible(k)) softmax(k);
-    __builtin_amdgcn_s_barrier();
+  // One pass over the wave's tiles.  Step k waits for tile k (each wave its
+  // own copies, then a barrier), issues the copies of tile k+3 into the
+  // buffer of tile k-1 (which every wave finished in step k-1), and runs one
+  // stream over tile k.  The numerators are taken against a reference fixed
+  // at the first tile (key 0 is visible to every query); the pass reports
+  // whether a later tile's largest score exceeded it by more than kSlack
+  // (log2 units), past which the numerators could overflow.
+  constexpr float kSlack = 64.f;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  auto run_pass = [&](bool set_ref) -> bool {
+#pragma unroll
+    for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] = f32x16_t{};
+    l_run = 0.f;
+    for (int k = 0; k < 3 && k < n_tiles; ++k) issue(k);
+    for (int k = 0; k < n_tiles; ++k) {
+      const int ahead = min(n_tiles - 1 - k, 2);  // tiles issued after tile k
+      if (ahead == 2) wait_vmcnt<2 * kCopies>();
+      else if (ahead == 1) wait_vmcnt<kCopies>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (k + 3 < n_tiles) issue(k + 3);
+      if (kTK * k > wave_last) continue;
+      const uint32_t kb = __builtin_amdgcn_readfirstlane(tiles_addr + (k % kNBuf) * kBuf);
+      const uint32_t vb = kb + kKTile;
+      const int lim = vis_lim - kTK * k;
+      const int msk = __builtin_amdgcn_readfirstlane(kTK * k + kTK - 1 > wave_full);
+      if (k == 0 && set_ref)
+        asm volatile(MLA_PF_FIRST : MLA_PF_OUT : MLA_PF_IN : MLA_PF_CLOBBER);
+      else
+        asm volatile(MLA_PF_STEP : MLA_PF_OUT : MLA_PF_IN : MLA_PF_CLOBBER);
+    }
+    return m_seen * scale > m_ref + kSlack;
+  };
+#pragma clang diagnostic pop
+  const bool flagged = run_pass(true);
+  // workgroup-wide decision on a second pass, through words in tile buffer 0
+  // (no wave reads the tiles once every wave has passed this barrier)
+  MLA_LDS int* xflag = reinterpret_cast<MLA_LDS int*>(tiles);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  if (lane == 0) xflag[wave] = __builtin_amdgcn_ballot_w64(flagged) != 0;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  int any = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) any |= xflag[w];
+  if (any) {
+    __builtin_amdgcn_s_barrier();  // every wave has read the flags
+    // the reference becomes the largest scaled score of the query (both lanes)
+    m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32)) * scale;
+    run_pass(false);
   }
-  if (!late) __builtin_amdgcn_s_barrier();
 
   // epilogue: normalise and store the rows of this wave's queries
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -330,7 +310,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
       }
     if (p.lse != nullptr && hf == 0)
       p.lse[out_row * p.n_h + head] =
-          (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+          (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
 

@@ -60,6 +60,80 @@ def test_prefill_matches_nonabsorbed_oracle(T, n_h):
     assert np.max(np.abs(lse.cpu().numpy() - lse_ref)) <= 2e-2
 
 
+def _per_head_oracle(qn64, qp64, kn64, kr64, v64, scale):
+    """Causal attention of each head over explicit keys and values, through
+    the oracle's non-absorbed and absorbed forms: the head's latent rows are
+    [k_nope | v | 0] and its up-projections select the two blocks."""
+    T, n_h, _ = qn64.shape
+    pos = np.arange(T)
+    w_uk = np.zeros((1, D_H, D_C))
+    w_uk[0, :, :D_H] = np.eye(D_H)
+    w_uv = np.zeros((1, D_V, D_C))
+    w_uv[0, :, D_H:D_H + D_V] = np.eye(D_V)
+    out = np.empty((T, n_h, D_V))
+    lse = np.empty((T, n_h))
+    for h in range(n_h):
+        C = np.zeros((T, D_C))
+        C[:, :D_H] = kn64[:, h]
+        C[:, D_H:D_H + D_V] = v64[:, h]
+        qn, qp = qn64[:, h:h + 1], qp64[:, h:h + 1]
+        out[:, h] = ref.attention_nonabsorbed(qn, qp, pos, C, kr64, w_uk, w_uv, scale)[:, 0]
+        _, l = ref.decode_absorbed(ref.absorb_q(qn, qp, pos, w_uk), pos, C, kr64, scale)
+        lse[:, h] = l[:, 0]
+    return out, lse
+
+
+@pytest.mark.parametrize("n_h", [64, 128])
+def test_prefill_peaked_scores(n_h):
+    """One key row scaled up (x20, content and RoPE parts, every head) gives
+    some queries a score more than 64 log2 units above every score of their
+    first 64-key tile: the case in which a softmax that fixes its reference
+    at the first tile has to redo the pass with the true maximum.  Keys and
+    values are given directly (bf16), so both sides score the same inputs.
+    The gain stays moderate and no second large key competes with it: the
+    kernel rounds the rotated query to bf16 (up to 2^-8 of each value, as in the
+    unscaled cases), an error on each score proportional to the key's norm,
+    and two large keys near a tie would turn it into a weight error above
+    the bar.  Same bar as the unscaled cases for the output; for lse the
+    bar adds the largest score shift that rounding can cause."""
+    rng = np.random.default_rng(4200 + n_h)
+    T = 300
+    dims = mla.make_dims(n_h, D_C, D_H, D_R, D_V, 1024, 64, "bf16", "bf16")
+    gain = np.ones((T, 1, 1), dtype=np.float32)
+    gain[100] = 20.0
+    q_nope, qn64 = _bf16(rng, (T, n_h, D_H))
+    q_pe, qp64 = _bf16(rng, (T, n_h, D_R))
+    k_nope = torch.from_numpy(rng.standard_normal((T, n_h, D_H), dtype=np.float32) * gain).bfloat16().cuda()
+    k_rope = torch.from_numpy(rng.standard_normal((T, D_R), dtype=np.float32) * gain[:, 0]).bfloat16().cuda()
+    v, v64 = _bf16(rng, (T, n_h, D_V))
+    kn64, kr64 = _host_bf16(k_nope), _host_bf16(k_rope)
+    out = torch.empty(T, n_h, D_V, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(T, n_h, dtype=torch.float32, device="cuda")
+    mla.prefill_attention(dims, q_nope, q_pe, k_nope, k_rope, v, out, lse)
+    torch.cuda.synchronize()
+
+    scale = 1.0 / np.sqrt(D_H + D_R)
+    want, lse_ref = _per_head_oracle(qn64, qp64, kn64, kr64, v64, scale)
+    # the case is there: for some (query, head) the largest visible score is
+    # far above the largest score of the first tile
+    w_uk = np.zeros((1, D_H, D_C))
+    w_uk[0, :, :D_H] = np.eye(D_H)
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    gap, slack = [], []
+    for h in range(n_h):
+        C = np.zeros((T, D_C))
+        C[:, :D_H] = kn64[:, h]
+        q_lat = ref.absorb_q(qn64[:, h:h + 1], qp64[:, h:h + 1], np.arange(T), w_uk)[:, 0]
+        s = np.where(causal, (q_lat[:, :D_C] @ C.T + q_lat[:, D_C:] @ kr64.T) * scale, -np.inf)
+        gap.append(np.max(s, axis=1) - np.max(s[:, :64], axis=1))
+        # the kernel rounds the rotated query to bf16 (at most 2^-8 of each
+        # element): every score moves by at most this much, and so does lse
+        slack.append(2.0 ** -8 * scale * np.max(np.where(causal, np.abs(q_lat[:, D_C:]) @ np.abs(kr64).T, 0), axis=1))
+    assert np.max(gap) * np.log2(np.e) > 64
+    assert ov.rel_err(_host_bf16(out), want) <= ov.TOL["bf16"]
+    assert np.all(np.abs(lse.cpu().numpy() - lse_ref) <= 2e-2 + np.stack(slack, axis=1))
+
+
 def test_prefill_first_token_is_its_own_value():
     """Query 0 sees only key 0: its output is v_0 exactly up to bf16 rounding
     (softmax over one key), whatever the scores."""
