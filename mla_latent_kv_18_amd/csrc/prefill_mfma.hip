@@ -123,9 +123,19 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
   const int my_q = q0 + l32;
   const int qc = min(my_q, Tq - 1);
   const int vis = min(ctx + my_q, Tk - 1);               // last key this query sees
+  const int last_key = min(ctx + qb * kQB + kQB - 1, Tk - 1);
+  const int n_tiles = last_key / kTK + 1;              // tiles the workgroup reads
 
-  // Q^T fragments: qf[s] = Q[q][16s + 8hf .. +7]; s < 8 content, s >= 8 RoPE part
+  // Q^T fragments: qf[s] = Q[q][16s + 8hf .. +7]; s < 8 content, s >= 8 RoPE
+  // part.  The RoPE part is rotated once the loads have landed and the
+  // first tile copies are on their way (further down); its angles are taken
+  // here, while the loads are in flight: the angle is reduced to a fraction
+  // of a turn in double precision and its sine and cosine taken by the
+  // hardware's turn-based v_sin / v_cos (about 1e-6 absolute, far below the
+  // bf16 rounding of the rotated values).
   bf16x8_t qf[kPD / 16];
+  bf16x8_t x[4];
+  float rc[16], rs[16];
   {
     const int64_t qrow = q_row0 + qc;
     const int qpos = ctx + qc;
@@ -133,23 +143,18 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
 #pragma unroll
     for (int s = 0; s < kPH / 16; ++s) qf[s] = ld8(qn + 16 * s);
     const __bf16* qr = p.q_pe + (qrow * p.n_h + head) * kPR + 8 * hf;
-    bf16x8_t x[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) x[s] = ld8(qr + 16 * s);
     // dims d = 16s + 8hf + e; s = 0, 1 hold pair members k = d, s = 2, 3 their partners k + 32
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float cs, sn;
-        rope_cos_sin_inv(qpos, rope.inv[16 * s + 8 * hf + e], &cs, &sn);
-        const float a = static_cast<float>(x[s][e]), b = static_cast<float>(x[s + 2][e]);
-        qf[8 + s][e] = f32_to_bf16(a * cs - b * sn);
-        qf[10 + s][e] = f32_to_bf16(a * sn + b * cs);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const double turns = static_cast<double>(qpos) * rope.inv[16 * (i >> 3) + 8 * hf + (i & 7)] * 0.15915494309189533577;
+      const float f = static_cast<float>(turns - rint(turns));
+      rc[i] = __builtin_amdgcn_cosf(f);
+      rs[i] = __builtin_amdgcn_sinf(f);
+    }
     wait_vmcnt<0>();  // complete before the tile copies start counting
   }
-
   // per-lane LDS offsets.  Key fragment s of lane (row l32, chunk 2s + hf) is
   // at kq_off[s & 3] + 128 (s >> 2): the row's XOR swizzle touches only the
   // low three chunk bits.  Value fragment (k-step ks, half h2, column tile
@@ -216,10 +221,20 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
   };
 #pragma clang diagnostic pop
 
+  // the first tiles' copies go out before the query's RoPE part is rotated
+  for (int k = 0; k < 3 && k < n_tiles; ++k) issue(k);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float cs = rc[8 * s + e], sn = rs[8 * s + e];
+      const float a = static_cast<float>(x[s][e]), b = static_cast<float>(x[s + 2][e]);
+      qf[8 + s][e] = f32_to_bf16(a * cs - b * sn);
+      qf[10 + s][e] = f32_to_bf16(a * sn + b * cs);
+    }
+
   f32x16_t oacc[kPV / 32];
   float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
-  const int last_key = min(ctx + qb * kQB + kQB - 1, Tk - 1);
-  const int n_tiles = last_key / kTK + 1;
   // the wave's queries see keys up to ctx + q0 + 31 (its last query), and
   // every key of a tile up to min(ctx + q0, Tk - 1) (its first query's last)
   const int wave_last = ctx + q0 + 31;
@@ -253,7 +268,8 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_attention_kernel(PrefillP
 #pragma unroll
     for (int ct = 0; ct < kPV / 32; ++ct) oacc[ct] = f32x16_t{};
     l_run = 0.f;
-    for (int k = 0; k < 3 && k < n_tiles; ++k) issue(k);
+    if (!set_ref)  // the first pass finds its first tiles issued
+      for (int k = 0; k < 3 && k < n_tiles; ++k) issue(k);
     for (int k = 0; k < n_tiles; ++k) {
       const int ahead = min(n_tiles - 1 - k, 2);  // tiles issued after tile k
       if (ahead == 2) wait_vmcnt<2 * kCopies>();
