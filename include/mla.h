@@ -95,8 +95,12 @@ typedef enum {
    * elements (value 2^(b - 127)), then zero padding to a multiple of 16
    * bytes (320 B for d_c + d_R = 576) */
   MLA_FP4_E2M1 = 3,
-  /* cache only: d_c e4m3 latent codes with one fp32 scale per row in
-   * cache_scale, then the d_R RoPE-key values in bf16 (640 B for 512 + 64) */
+  /* cache only: d_c e4m3 latent codes with one scale per row in
+   * cache_scale, then the d_R RoPE-key values in bf16 (640 B for 512 + 64).
+   * The scale is a power of two, stored as fp32: the smallest s with
+   * max|latent| / s <= 448 (mla_append_latent writes it so; the 128-row
+   * decode applies it inside its e4m3 -> bf16 conversion, which is exact
+   * only for powers of two) */
   MLA_FP8_E4M3_KR_BF16 = 4
 } mla_dtype_t;
 

@@ -440,7 +440,7 @@ hipError_t launch_dq(const DqParams& p, dim3 grid, int waves, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode_dq(const DecodeArgs& a, int fmt, hipStream_t st) {
-  if (fmt != kDqFp8Kr && decode_pipe_supported(a.n_h, a.q_len)) return launch_decode_pipe(a, fmt, st);
+  if (decode_pipe_supported(a.n_h, a.q_len)) return launch_decode_pipe(a, fmt, st);
   DqParams p;
   p.q_lat = static_cast<const __bf16*>(a.q_lat);
   p.cache = static_cast<const uint8_t*>(a.cache);

@@ -57,6 +57,7 @@ struct DecodeParams {
   int xcd_group;  // 1: the workgroups of one request share an XCD (see xcd_slot)
   float scale_log2;
   const int32_t* items;  // planned launch list, or null for the uniform split
+  const float* cache_scale;  // e4m3 latent rows: one fp32 scale per cache slot
 };
 
 __device__ __forceinline__ int swz(int t) {
@@ -319,7 +320,17 @@ decode_bf16_kernel(DecodeParams p) {
 //              k+2 into the bf16 tile layout between the weighted-sum MFMAs
 //              (E2M1 times a power of two is exact in bf16).  LDS: three tile
 //              buffers, two P^T buffers, three staging slots.
-enum { kPipeBf16 = 0, kPipeNope = 1, kPipeFp4 = 2 };
+//   kPipeFp8Kr 512 e4m3 latent codes with one power-of-two scale per row
+//              (fp32, beside the pool) and a 64-wide bf16 RoPE key (640 bytes): each wave
+//              copies the codes and scales of its eight rows of tile k+3 into
+//              a staging slot, and its rows' RoPE keys straight into their
+//              place in bf16 tile k+3 (that buffer still holds tile k, whose
+//              keys were scored a step earlier; the weighted sum reads only
+//              the latent columns).  Step k's stream expands its rows of tile
+//              k+2 between the weighted-sum MFMAs (the row scale is a power
+//              of two, so code * scale is exact in bf16).  LDS: three tile
+//              buffers, two P^T buffers, two staging slots.
+enum { kPipeBf16 = 0, kPipeNope = 1, kPipeFp4 = 2, kPipeFp8Kr = 3 };
 constexpr int kPBytes = kTileT * 128 * 2;  // P^T of one tile, all heads, bf16
 
 template <int PF>
@@ -330,13 +341,19 @@ struct PipeGeo {
   static constexpr int kTileBytes = kTileT * D * 2;
   static constexpr int kCopies = kTileBytes / 1024 / 4;  // direct copies per wave and tile
   static constexpr bool kExpand = PF == kPipeFp4;
-  static constexpr int kRowBytes = kExpand ? 320 : D * 2;  // stored bytes per cache row
-  static constexpr int kBufs = kExpand ? 3 : 4;
-  static constexpr int kStageWave = 3072;               // a wave's 8 stored rows (2560 B) + pad
+  static constexpr bool kFp8 = PF == kPipeFp8Kr;
+  static constexpr bool kStaged = kExpand || kFp8;
+  // stored bytes per cache row
+  static constexpr int kRowBytes = kExpand ? 320 : (kFp8 ? 640 : D * 2);
+  static constexpr int kBufs = kStaged ? 3 : 4;
+  // a wave's staged rows: FP4 8 x 320 B (+ pad); FP8-KR 8 x 512 B of codes, then
+  // 256 B whose first 32 hold the rows' scales
+  static constexpr int kStageWave = kFp8 ? 4096 + 256 : 3072;
   static constexpr int kStageBytes = 4 * kStageWave;
+  static constexpr int kSlots = kFp8 ? 2 : 3;
   static constexpr int kRawCopies = 3;
   static constexpr int kTiles = kBufs * kTileBytes;
-  static constexpr int kLds = kTiles + 2 * kPBytes + (kExpand ? 3 * kStageBytes : 0);
+  static constexpr int kLds = kTiles + 2 * kPBytes + (kStaged ? kSlots * kStageBytes : 0);
   static_assert(kLds <= 160 * 1024, "LDS");
   static_assert(4 * kTileBytes <= kLds, "query staging");
 };
@@ -365,6 +382,7 @@ struct PipeGeo {
   [cb] "s"(cb), [cd] "s"(cd), [cl] "s"(cl), [k1152] "s"(G::D * 2), [c0] "v"(cpk[0]),          \
       [c1] "v"(cpk[1]), [c2] "v"(cpk[2]), [c3] "v"(cpk[3]), [c4] "v"(cpk[4])
 #define MLA_ASM_EXPAND [xs] "s"(xs), [xt] "s"(xt), [xw] "s"(xw), [xtl0] "v"(xtl0), [xtl1] "v"(xtl1)
+#define MLA_ASM_EXPAND8 [xs] "s"(xs), [xt] "s"(xt), [xw] "s"(xw)
 #define MLA_ASM_SCRATCH MLA_BF16_ASM_SCRATCH, "memory", "m0", "scc", "vcc"
 
 #include "decode_bf16_asm.inc"
@@ -518,6 +536,62 @@ decode_pipe_kernel(DecodeParams p) {
     const uint32_t e = *reinterpret_cast<const MLA_LDS uint8_t*>(sw + 320 * r + 288 + (c >> 2));
     *reinterpret_cast<MLA_LDS bf16x8_t*>(tw + r * 1152 + 16 * (c ^ swz(8 * wave + r))) = fp4_word_to_bf16(w, e);
   };
+  // FP8-KR: first cache slot of tile k given its block-table entry
+  auto slot_from = [&](int blk, int k) -> int64_t {
+    const int tok0 = j0 + k * kTileT;
+    blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+    return static_cast<int64_t>(blk) * p.block_size + tok0 % p.block_size;
+  };
+  // FP8-KR: the codes of the wave's rows 8w..8w+7 of tile k (4 KB: copy i
+  // moves rows 2i, 2i+1) and their scales (lanes 0-7; the rest repeat them)
+  // into its part of staging slot k % 2
+  auto issue_stage8 = [&](int64_t slot0, int k) {
+    const int last = last_row(k);
+    const char* base = reinterpret_cast<const char*>(p.cache) + slot0 * G::kRowBytes;
+    const uint32_t dst = stage_addr + (k & 1) * G::kStageBytes + wave * G::kStageWave;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = min(8 * wave + 2 * i + (lane >> 5), last);
+      dma16_sv(base, static_cast<uint32_t>(t * G::kRowBytes + ((16 * lane) & 511)), dst + 1024 * i);
+    }
+    const int ts = min(8 * wave + (lane & 7), last);
+    dma4_sv(p.cache_scale + slot0, static_cast<uint32_t>(4 * ts), dst + 4096);
+  };
+  // FP8-KR: the RoPE keys of the wave's rows of tile k (128 B each, already
+  // bf16) straight into chunks 64..71 of their rows in bf16 tile k, one
+  // eight-lane copy per row (position c holds chunk c ^ swz(row))
+  auto issue_rope8 = [&](int64_t slot0, int k) {
+    const int last = last_row(k);
+    const char* base = reinterpret_cast<const char*>(p.cache) + slot0 * G::kRowBytes;
+    const uint32_t dst = buf_addr(k);
+    if (lane < 8) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int t = 8 * wave + jj;
+        const int ts = min(t, last);
+        dma16_sv(base, static_cast<uint32_t>(ts * G::kRowBytes + kDc + 16 * (lane ^ swz(t))),
+                 dst + t * (G::D * 2) + 2 * kDc);
+      }
+    }
+  };
+  // FP8-KR: expand the wave's staged rows of tile k into bf16 tile k (C++
+  // form, for the first two tiles of a pass; the step stream does the rest).
+  // The conversion applies the row's power-of-two scale exactly.
+  auto expand8_cpp = [&](int k) {
+    MLA_LDS const char* sw = tiles + (stage_addr - tiles_addr) + (k & 1) * G::kStageBytes + wave * G::kStageWave;
+    MLA_LDS char* tw = tiles + (static_cast<uint32_t>(k) % G::kBufs) * G::kTileBytes + 8 * wave * G::kChunks * 16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const i32x2_t c = *reinterpret_cast<MLA_LDS const i32x2_t*>(sw + 512 * j + 8 * lane);
+      const float sc = *reinterpret_cast<MLA_LDS const float*>(sw + 4096 + 4 * j);
+      const bf16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, false);
+      const bf16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, true);
+      const bf16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, false);
+      const bf16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, true);
+      *reinterpret_cast<MLA_LDS bf16x8_t*>(tw + j * 1152 + 16 * (lane ^ swz(8 * wave + j))) =
+          bf16x8_t{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+    }
+  };
   // FP4 stream inputs: the rows' last eight chunks (code word | scale byte <<
   // 16 in the staged rows; destination in the bf16 tile) and the swizzle term
   // 64 * (wave & 1) that the wave's rows share
@@ -567,7 +641,17 @@ decode_pipe_kernel(DecodeParams p) {
     __builtin_amdgcn_s_barrier();        // every wave done with the buffers
   }
   auto issue_first = [&]() {  // the first tiles of a pass
-    if constexpr (G::kExpand) {
+    if constexpr (G::kFp8) {
+      // copy order: RoPE 0, staged 0, RoPE 1, staged 1, RoPE 2 (the waits
+      // below count on it)
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if (k < n_tiles) {
+          const int64_t s0 = slot_from(block_of(k), k);
+          issue_rope8(s0, k);
+          if (k < 2) issue_stage8(s0, k);
+        }
+    } else if constexpr (G::kExpand) {
 #pragma unroll
       for (int k = 0; k < 3; ++k)
         if (k < n_tiles) issue_raw_at(tile_base(k), k);
@@ -587,7 +671,24 @@ decode_pipe_kernel(DecodeParams p) {
     l_run = 0.f;
     excess = -INFINITY;
     if (n_tiles == 0) return false;
-    if constexpr (G::kExpand) {
+    if constexpr (G::kFp8) {
+      // each copy group: RoPE 8 copies, staged rows 5 copies
+      if (n_tiles >= 3) wait_vmcnt<21>();  // staged 0 landed (RoPE 1, staged 1, RoPE 2 may not have)
+      else if (n_tiles == 2) wait_vmcnt<13>();
+      else wait_vmcnt<0>();
+      expand8_cpp(0);
+      if (n_tiles > 1) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging slot 0 read
+        if (n_tiles > 2) {
+          issue_stage8(slot_from(block_of(2), 2), 2);
+          wait_vmcnt<13>();  // staged 1 landed (RoPE 2, staged 2 may not have)
+        } else {
+          wait_vmcnt<0>();
+        }
+        expand8_cpp(1);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    } else if constexpr (G::kExpand) {
       // staged tiles 0..2 are in flight; tiles 0 and 1 into bf16 buffers 0, 1
       if (n_tiles >= 3) wait_vmcnt<2 * G::kRawCopies>();
       else if (n_tiles == 2) wait_vmcnt<G::kRawCopies>();
@@ -620,7 +721,37 @@ decode_pipe_kernel(DecodeParams p) {
                      : MLA_ASM_SCRATCH);
     }
     int k = 0;
-    if constexpr (G::kExpand) {
+    if constexpr (G::kFp8) {
+      // Step k expands tile k+2 (staged in step k-1, slot k % 2) and copies
+      // the RoPE keys and staged rows of tile k+3.  Its scored tile k+1 is
+      // not the chunk's last, so the stream skips the mask.  Copy sources
+      // are looked up a step ahead.
+      int64_t s_next = n_tiles > 3 ? slot_from(block_of(3), 3) : 0;
+      int blk_next = n_tiles > 4 ? block_of(4) : 0;
+      for (; k + 2 < n_tiles; ++k) {
+        wait_vmcnt<18>();  // this wave's RoPE keys of tile k+1 (staged k+1, RoPE k+2, staged k+2 after them)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): tile k+1 rows and P^T of tile k written
+        __builtin_amdgcn_s_barrier();  // tile k+1 and P^T of tile k visible; tile k-1 released
+        if (k + 3 < n_tiles) {
+          issue_rope8(s_next, k + 3);
+          issue_stage8(s_next, k + 3);
+        } else {
+          wait_vmcnt<0>();  // no copies behind tile k+2's staged rows for the stream's count
+        }
+        const uint32_t bk = buf_addr(k + 1), bv = buf_addr(k), bp = pbuf_addr_of(k);
+        const uint32_t bpw = pbuf_addr_of(k + 1) + wave * 2048;
+        const uint32_t xs = stage_addr + (k & 1) * G::kStageBytes + wave * G::kStageWave;
+        const uint32_t xt = buf_addr(k + 2) + 8 * wave * G::kChunks * 16;
+        const uint32_t xw = 64 * (wave & 1);
+        const int tok = 32 * (k + 1);
+        asm volatile(MLA_FP8KR_STEP_EXPAND
+                     : MLA_ASM_ACC, MLA_ASM_SOFTMAX_STATE
+                     : MLA_ASM_Q, MLA_ASM_KEYS, MLA_ASM_VALUES, MLA_ASM_SOFTMAX_IN, MLA_ASM_EXPAND8
+                     : MLA_ASM_SCRATCH);
+        if (k + 4 < n_tiles) s_next = slot_from(blk_next, k + 4);
+        if (k + 5 < n_tiles) blk_next = block_of(k + 5);
+      }
+    } else if constexpr (G::kExpand) {
       // Step k expands tile k+2 and copies the stored rows of tile k+4 (into
       // the staging slot that tile k+1 left in step k-1).  Its scored tile
       // k+1 is not the chunk's last, so with q_len <= 32 all of it is
@@ -680,7 +811,7 @@ decode_pipe_kernel(DecodeParams p) {
       }
     }
     for (; k + 1 < n_tiles; ++k) {
-      if (!G::kExpand && k + 2 < n_tiles) wait_vmcnt<G::kCopies>();
+      if (!G::kStaged && k + 2 < n_tiles) wait_vmcnt<G::kCopies>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __builtin_amdgcn_s_barrier();
@@ -890,6 +1021,7 @@ DecodeParams decode_params(const DecodeArgs& a) {
   p.num_splits = a.num_splits;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.items = a.items;
+  p.cache_scale = a.cache_scale;
   const int waves = decode_waves_per_group(a.n_h, a.q_len);
   p.row_groups = a.q_len * a.n_h / (32 * waves);
   p.xcd_group = 0;
@@ -926,6 +1058,8 @@ hipError_t launch_decode_pipe(const DecodeArgs& a, int fmt, hipStream_t st) {
   if (a.items != nullptr && a.num_slots == 0) return hipSuccess;
   if (fmt == kDqFp4Mx)
     hipLaunchKernelGGL(decode_pipe_kernel<kPipeFp4>, grid, dim3(256), 0, st, p);
+  else if (fmt == kDqFp8Kr)
+    hipLaunchKernelGGL(decode_pipe_kernel<kPipeFp8Kr>, grid, dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL(decode_pipe_kernel<kPipeNope>, grid, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();

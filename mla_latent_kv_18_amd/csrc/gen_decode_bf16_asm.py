@@ -285,6 +285,7 @@ def first(geo=G576):
 XS, XSS, XW = KADDR[1], KADDR[2], KADDR[3]    # code, scale and store bases
 XSLOT = [(188, 192), (194, 198)]              # (4 output VGPRs, scale/address)
 XTAIL = 193                                   # second address of the tail chunk
+FP8KR_STEP_VMEM = 13     # copies a step issues after the staged rows it expands: 8 RoPE, 4 code, 1 scale
 FP4_ROW = 320                                 # bytes per stored row
 FP4_CODES = 288                               # code bytes per stored row
 
@@ -341,6 +342,58 @@ def fp4_expand_ops():
     return ops
 
 
+# FP8-KR expansion registers (free in the step's second part: the key
+# fragment slots, and the copy temporaries, since expanding steps issue no
+# copies)
+XC, XSC = KADDR[1], KADDR[2]                  # code and scale read addresses
+XCODE = [(CT, CO, 190), (188, 189, 191)]      # (code pair, scale) per read slot
+XOUT = [192, 196]                             # four bf16 pairs per row, by row parity
+FP8_CODES = 512                               # staged code bytes per row
+FP8_SCALES = 4096                             # offset of the staged row scales
+
+
+def fp8kr_expand_ops(vm_wait):
+    """Op groups expanding this wave's eight staged rows of an e4m3 latent
+    tile (512 codes per row, one power-of-two scale per row) into the bf16
+    tile: four conversions of two codes each, which apply the scale exactly
+    (e4m3 times a power of two is exact in bf16).  Lane l converts codes
+    8l..8l+7 of each row (chunk l of the row); reads run one row ahead.  The
+    RoPE part of the tile arrives by direct copies, not here.
+    vm_wait: vmcnt that leaves this wave's staged rows landed."""
+    rows = 8
+    ops = [[f"s_waitcnt vmcnt({vm_wait})",
+            f"v_lshrrev_b32 v{XC}, 1, %[pa]", f"v_add_u32 v{XC}, %[xs], v{XC}",
+            f"v_mov_b32 v{XSC}, %[xs]",
+            f"v_xor_b32 v{XW}, %[xw], %[pa]", f"v_add_u32 v{XW}, %[xt], v{XW}"]]
+
+    def reads(j):
+        c0, c1, sc = XCODE[j % 2]
+        return [("lds", ("xr", j), f"ds_read_b64 v[{c0}:{c1}], v{XC} offset:{FP8_CODES * j}"),
+                ("lds", ("xr", j), f"ds_read_b32 v{sc}, v{XSC} offset:{FP8_SCALES + 4 * j}")]
+
+    def convert(j):
+        c0, c1, sc = XCODE[j % 2]
+        o = XOUT[j % 2]
+        return [("wait", ("xr", j)),
+                f"v_cvt_scalef32_pk_bf16_fp8 v{o}, v{c0}, v{sc}",
+                f"v_cvt_scalef32_pk_bf16_fp8 v{o + 1}, v{c0}, v{sc} op_sel:[1,0,0]",
+                f"v_cvt_scalef32_pk_bf16_fp8 v{o + 2}, v{c1}, v{sc}",
+                f"v_cvt_scalef32_pk_bf16_fp8 v{o + 3}, v{c1}, v{sc} op_sel:[1,0,0]"]
+
+    def store(j):
+        c0, c1, sc = XCODE[j % 2]
+        return [f"v_xor_b32 v{sc}, {16 * swz_even(j)}, v{XW}",
+                ("lds", ("xw", j), f"ds_write_b128 v{sc}, {vr(XOUT[j % 2])} offset:{1152 * j}")]
+
+    ops.append(reads(0))
+    for j in range(rows):
+        if j + 1 < rows:
+            ops.append(reads(j + 1))
+        ops.append(convert(j))
+        ops.append(store(j))
+    return ops
+
+
 def merge(a, b):
     """Alternate two op lists, spreading the shorter one evenly."""
     if len(a) < len(b):
@@ -355,7 +408,7 @@ def merge(a, b):
     return out
 
 
-def step(copies, masked, geo=G576, expand=False):
+def step(copies, masked, geo=G576, expand=False, fp8_wait=None):
     st = Stream(geo)
     st.emit("s_nop 4")
     addresses(st, True, True)
@@ -376,6 +429,8 @@ def step(copies, masked, geo=G576, expand=False):
     ops = softmax_ops(masked)
     if expand:
         ops = merge(ops, fp4_expand_ops())
+    if fp8_wait is not None:
+        ops = merge(ops, fp8kr_expand_ops(fp8_wait))
     rest = list(range(geo.half, 32))
     per = -(-len(ops) // (len(rest) + 1))
     for n, i in enumerate(rest):
@@ -422,6 +477,7 @@ def main():
     out.append(as_c_string("MLA_NOPE_FIRST", first(G512)))
     out.append(as_c_string("MLA_NOPE_PV_ONLY", pv_only(G512)))
     out.append(as_c_string("MLA_FP4_STEP_EXPAND", step(False, False, G576, expand=True)))
+    out.append(as_c_string("MLA_FP8KR_STEP_EXPAND", step(False, False, G576, fp8_wait=FP8KR_STEP_VMEM)))
     sys.stdout.write("\n".join(out))
 
 

@@ -28,15 +28,28 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
+// A uniform 64-bit address kept in scalar registers (inside divergent code
+// the compiler may otherwise hold it in vector registers).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>(static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+}
 // The same 16-byte copy addressed as a uniform 64-bit base plus a per-lane
 // 32-bit byte offset (one VGPR per copy instead of a 64-bit address pair).
 __device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(uniform_ptr(sbase)),
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }

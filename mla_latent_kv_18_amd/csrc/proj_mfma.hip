@@ -176,8 +176,9 @@ constexpr int kMaxChunks = 16;  // contraction slices of the append GEMM
 //             and E2M1 codes of x / scale (nearest, ties to even, saturating
 //             at 6), two per byte (element 2i in the low nibble), then the
 //             D/32 scale bytes and zero padding to 16 bytes
-//   kOutFp8Kr e4m3 codes of the latent / s, s = max|latent| / 448 in
-//             cache_scale[slot], then the RoPE key in bf16
+//   kOutFp8Kr e4m3 codes of the latent / s, s the smallest power of two with
+//             max|latent| / s <= 448, in cache_scale[slot], then the RoPE
+//             key in bf16 (a power-of-two s keeps code * s exact in bf16)
 enum { kOutBf16 = 0, kOutFp8 = 1, kOutFp4 = 2, kOutFp8Kr = 3 };
 
 template <int D, int OUT>
@@ -289,7 +290,12 @@ __global__ void __launch_bounds__(256) append_finish_kernel(
     if (lane == 0) red[1][wave] = am;
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    float scale = amax > 0.f ? amax / 448.f : 1.f;
+    if (kLatentOnly && amax > 0.f) {
+      int ex;
+      const float f = frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1): amax / 2^(ex-9) <= 448 iff f <= 7/8
+      scale = ldexpf(1.f, f <= 0.875f ? ex - 9 : ex - 8);
+    }
     if (own) {
       if (!kLatentOnly || q < kDc / 4) {
         uint32_t packed = 0;

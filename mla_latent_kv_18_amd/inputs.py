@@ -147,9 +147,14 @@ def to_fp4_rows(x):
 
 def to_fp8kr_rows(x, d_c):
     """float32 rows [n, d_c + d_R] -> (uint8 rows [n, d_c + 2 d_R], float32
-    scale per row): the latent as e4m3 codes with one scale max|latent|/448,
-    the RoPE key as bf16 (little-endian bytes)."""
-    codes, scale = to_fp8_rows(np.asarray(x, dtype=np.float32)[:, :d_c])
+    scale per row): the latent as e4m3 codes of latent / s, s the smallest
+    power of two with max|latent| / s <= 448 (1 for an all-zero latent), the
+    RoPE key as bf16 (little-endian bytes)."""
+    lat = np.asarray(x, dtype=np.float32)[:, :d_c]
+    amax = np.abs(lat).max(axis=-1)
+    f, e = np.frexp(np.where(amax > 0, amax, 1.0).astype(np.float64))
+    scale = np.where(amax > 0, np.ldexp(1.0, np.where(f <= 0.875, e - 9, e - 8)), 1.0).astype(np.float32)
+    codes = torch.from_numpy(lat / scale[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     kr = to_bf16_bits(np.asarray(x, dtype=np.float32)[:, d_c:])
     return np.concatenate([codes, np.ascontiguousarray(kr).view(np.uint8)], axis=1), scale
 

@@ -257,6 +257,8 @@ SMALL_VARIANTS = {
     "nope_q2": ("nope_bs64_ctx4k", dict(batch=2, lens=(3, 300), q_len=2)),
     "fp4_batch8": ("v3_fp4_bs64_ctx4k", dict(batch=8, lens=(0, 2, 63, 64, 65, 97, 161, 2048))),
     "fp4_q2": ("v3_fp4_bs64_ctx4k", dict(batch=2, lens=(3, 300), q_len=2)),
+    "fp8kr_batch8": ("v3_fp8kr_bs64_ctx4k", dict(batch=8, lens=(0, 2, 63, 64, 65, 97, 161, 2048))),
+    "fp8kr_q2": ("v3_fp8kr_bs64_ctx4k", dict(batch=2, lens=(3, 300), q_len=2)),
 }
 
 
@@ -395,6 +397,7 @@ def check_decode_call(step, gen, b, tol, lse_tol=2e-2):
 PEAK_CASES = {   # base workload, overrides: the four decode kernels and the cache-variant kernels
     "fp4_h128": ("v3_fp4_bs64_ctx4k", dict(batch=2, lens=(400, 700))),
     "fp8kr_h64_q2": ("v3_fp8kr_bs64_ctx4k", dict(n_h=64, batch=2, lens=(400, 700), q_len=2)),
+    "fp8kr_h128": ("v3_fp8kr_bs64_ctx4k", dict(batch=2, lens=(400, 700))),
     "nope_h64": ("nope_bs64_ctx4k", dict(n_h=64, batch=2, lens=(400, 700))),
     "bf16_pipelined_h128": ("v3_bs64_ctx4k", dict(batch=2, lens=(400, 700))),
     "bf16_pipelined_h128_q2": ("v3_bs64_ctx4k", dict(batch=2, lens=(400, 700), q_len=2)),
