@@ -12,7 +12,9 @@ Prints one JSON line.  `value` is latent-cache GB/s of the whole step
 `roofline` object covers the decode call (its algorithmic cache bytes, or
 flops when MFMA bound, per launch / its average launch time from HIP events
 on the launch stream, with the last-level caches flushed before each
-launch; the unflushed rate is beside it as achieved_warm);
+launch; the unflushed rate is beside it as achieved_warm; beside the
+published 8 TB/s, hbm_read_ceiling is this GPU's measured streaming read
+rate over the same bytes, flushed the same way, from mla_hbm_read_probe);
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the
 same workload.  `block` (skipped with --no-block) times the whole attention
 block around the step: the query path W^DQ, W^UQ, W^QR and the output
@@ -294,6 +296,7 @@ def main():
 
     import torch
 
+    import mla_latent_kv_18_amd as mla
     from mla_latent_kv_18_amd.inputs import WORKLOADS, generate
     from mla_latent_kv_18_amd.step import DeviceStep
 
@@ -354,6 +357,25 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b))
+    # The achievable read rate of this GPU over the same number of bytes,
+    # flushed the same way: two plain streaming readers (16-byte loads into
+    # registers, and the decode's own copy structure without its arithmetic).
+    ceiling = {}
+    probe_bytes = cache_bytes // 36864 * 36864
+    probe_buf = torch.ones(probe_bytes // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros(mla.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda:0")
+    for mode, key in ((0, "registers_gbs"), (1, "lds_copies_gbs")):
+        t = []
+        for _ in range(min(args.steps, 50)):
+            scratch.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            mla.hbm_read_probe(probe_buf, mode, sink)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        ceiling[key] = round(probe_bytes / (sum(t) / len(t) * 1e-3) / 1e9, 2)
+    del probe_buf, sink
     del scratch
     cold_ms = sum(cold) / len(cold)
     cold_median_ms = sorted(cold)[len(cold) // 2]
@@ -373,6 +395,12 @@ def main():
                 "frac": round(tflops / mfma_peak, 4), "traffic": None, "flops_per_launch": flops,
                 "achieved_warm": round(warm_tflops, 2), "frac_warm": round(warm_tflops / mfma_peak, 4)}
     roof["kernel"] = "mla_decode (chunk partials + combine), caches flushed before each launch"
+    best = max(ceiling.values())
+    roof["hbm_read_ceiling"] = {"bytes": probe_bytes, "unit": "GB/s", **ceiling,
+                                "frac_of_peak": round(best / HBM_PEAK_GBS, 4),
+                                "kernel": "mla_hbm_read_probe, caches flushed before each launch"}
+    if bound == "hbm":
+        roof["frac_of_measured_ceiling"] = round(gbs / best, 4)
     roof["launch_us"] = round(cold_ms * 1e3, 2)
     out = {
         "metric": METRIC if args.workload == WORKLOAD else f"MLA decode latent-cache GB/s ({args.workload})",

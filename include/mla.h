@@ -469,6 +469,22 @@ mla_status_t mla_absorb_output_weights(const mla_dims_t* dims, const void* w_o, 
 mla_status_t mla_absorb_query_weights(const mla_dims_t* dims, int32_t d_cq, const void* w_uq,
                                       const void* w_uk, void* a, mla_stream_t stream);
 
+/* ------------------------------------------------------------ measurement
+ * The achievable HBM read rate, measured beside the published peak: decode
+ * time is set by reading the latent cache from HBM [MLA explainer, why the
+ * KV cache is the bottleneck of inference: arithmetic intensity], so its
+ * rate is read against both.  Reads the `bytes` at device pointer `buf` once
+ * and computes nothing from them that the path uses.
+ *   mode 0: 16-byte loads into registers from 2048 workgroups; bytes a
+ *           multiple of 16; sink: device array of at least 2048 uint32
+ *           (one XOR of the words read per workgroup, so no load is elided)
+ *   mode 1: the decode kernels' copy structure (36 KB tiles by direct
+ *           global->LDS copies, one workgroup per CU, three tiles in flight);
+ *           bytes a multiple of 36864; sink unused (may be NULL)
+ * Asynchronous on `stream`; errors as for the other calls. */
+mla_status_t mla_hbm_read_probe(const void* buf, size_t bytes, int32_t mode, uint32_t* sink, size_t sink_words,
+                                mla_stream_t stream);
+
 /* ------------------------------------------------------------ diagnostics */
 const char* mla_status_string(mla_status_t status);
 const char* mla_last_error_message(void); /* thread-local, never NULL */

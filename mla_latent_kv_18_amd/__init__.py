@@ -28,7 +28,7 @@ EXPORTS = ("mla_cache_row_bytes", "mla_cache_bytes_per_token", "mla_q_lat_row_by
            "mla_decode_uniform_workspace_size", "mla_decode_uniform", "mla_decode_uniform_noalloc",
            "mla_decode_default_split",
            "mla_out_proj", "mla_linear_workspace_size", "mla_linear", "mla_linear_pair", "mla_prefill_attention", "mla_prefill_attention_varlen",
-           "mla_absorb_output_weights", "mla_absorb_query_weights",
+           "mla_absorb_output_weights", "mla_absorb_query_weights", "mla_hbm_read_probe",
            "mla_status_string", "mla_last_error_message", "mla_version")
 
 
@@ -102,6 +102,7 @@ def lib():
         "mla_prefill_attention": (I32, [DP, P, P, P, P, I32, P, I32, P, P, P]),
         "mla_prefill_attention_varlen": (I32, [DP, P, P, P, P, I32, P, P, P, I32, I32, I32, P, P, P]),
         "mla_linear": (I32, [P, I32, P, I32, I32, I32, P, P, SZ, P]),
+        "mla_hbm_read_probe": (I32, [P, SZ, I32, P, SZ, P]),
         "mla_status_string": (ctypes.c_char_p, [I32]),
         "mla_last_error_message": (ctypes.c_char_p, []),
         "mla_version": (I32, []),
@@ -374,6 +375,21 @@ def prefill_attention_varlen(dims, q_nope, q_pe, k_nope, k_rope, v, cu_q, cu_k, 
     _check(lib().mla_prefill_attention_varlen(ctypes.byref(dims), _ptr(q_nope), _ptr(q_pe), _ptr(k_nope),
                                               k_rope.data_ptr(), k_rope.stride(0), _ptr(v), _ptr(cu_q), _ptr(cu_k),
                                               S, max_q, Tq, _ptr(out), _ptr(lse), _stream(out.device)))
+
+
+PROBE_SINK_WORDS = 2048
+
+
+def hbm_read_probe(buf, mode, sink=None):
+    """mla_hbm_read_probe: read the bytes of device tensor `buf` once (mode 0:
+    loads into registers, XOR words into sink, an int32 device tensor of at
+    least PROBE_SINK_WORDS; mode 1: the decode kernels' direct global->LDS
+    tile copies, no sink)."""
+    nbytes = buf.numel() * buf.element_size()
+    if mode == 0 and (sink is None or sink.numel() < PROBE_SINK_WORDS or sink.element_size() != 4):
+        raise ValueError(f"hbm_read_probe: mode 0 needs a 4-byte sink of at least {PROBE_SINK_WORDS} words")
+    _check(lib().mla_hbm_read_probe(_ptr(buf), nbytes, mode, _ptr(sink), 0 if sink is None else sink.numel(),
+                                    _stream(buf.device)))
 
 
 def version():

@@ -680,6 +680,23 @@ mla_status_t mla_absorb_query_weights(const mla_dims_t* dims, int32_t d_cq, cons
                     "mla_absorb_query_weights");
 }
 
+mla_status_t mla_hbm_read_probe(const void* buf, size_t bytes, int32_t mode, uint32_t* sink, size_t sink_words,
+                                mla_stream_t stream) {
+  if (!buf) return fail(MLA_ERR_INVALID_ARGUMENT, "NULL buffer");
+  if (mode == 0) {
+    if (bytes % 16 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes must be a multiple of 16 (mode 0)");
+    if (!sink || sink_words < static_cast<size_t>(mla::kProbeRegsGrid))
+      return fail(MLA_ERR_INVALID_ARGUMENT, "mode 0 needs a sink of at least %d words", mla::kProbeRegsGrid);
+  } else if (mode == 1) {
+    if (bytes % 36864 != 0) return fail(MLA_ERR_INVALID_ARGUMENT, "bytes must be a multiple of 36864 (mode 1)");
+  } else {
+    return fail(MLA_ERR_INVALID_ARGUMENT, "mode must be 0 or 1");
+  }
+  if (bytes == 0) return hip_status(hipSuccess, "");
+  return hip_status(mla::launch_hbm_read_probe(buf, bytes, mode, sink, static_cast<hipStream_t>(stream)),
+                    "mla_hbm_read_probe");
+}
+
 const char* mla_status_string(mla_status_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

@@ -111,6 +111,11 @@ hipError_t launch_decode_dq(const DecodeArgs&, int fmt, hipStream_t);
 // the pipelined decode stream (workgroups of 128 rows, q_len <= 32) over
 // bf16 576-wide rows (launch_decode_mfma), NoPE rows and FP4 rows
 bool decode_pipe_supported(int n_h, int q_len);
+// streaming read of a buffer (achievable HBM read rate); mode 0: loads into
+// registers, grid kProbeRegsGrid, one XOR word per workgroup into sink;
+// mode 1: direct global->LDS copies of 36 KB tiles, 256 workgroups
+constexpr int kProbeRegsGrid = 2048;
+hipError_t launch_hbm_read_probe(const void* buf, size_t bytes, int mode, uint32_t* sink, hipStream_t st);
 hipError_t launch_decode_pipe(const DecodeArgs&, int fmt, hipStream_t);
 // causal prefill attention of one sequence with per-head keys and values
 // (q, k: [d_h content ; d_R RoPE part] = 192 wide, v: 128 wide)

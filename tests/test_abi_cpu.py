@@ -338,3 +338,17 @@ def test_fold_weights_host_checks():
     assert lib.mla_absorb_output_weights(ctypes.byref(d), None, P(1), P(1), None) == 1
     assert lib.mla_absorb_query_weights(ctypes.byref(d), 0, P(1), P(1), P(1), None) == 1
     assert lib.mla_absorb_query_weights(ctypes.byref(d), 1536, P(1), None, P(1), None) == 1
+
+
+def test_hbm_read_probe_host_checks():
+    """mla_hbm_read_probe rejects a bad mode, a misaligned size and a short
+    sink before any launch; zero bytes launch nothing."""
+    lib = mla.lib()
+    assert lib.mla_hbm_read_probe(None, 16, 0, 1, 4096, None) == 1          # NULL buffer
+    assert lib.mla_hbm_read_probe(1, 17, 0, 1, 4096, None) == 1             # not a multiple of 16
+    assert lib.mla_hbm_read_probe(1, 16, 0, 1, 2047, None) == 1             # sink too short
+    assert lib.mla_hbm_read_probe(1, 16, 0, None, 4096, None) == 1          # no sink
+    assert lib.mla_hbm_read_probe(1, 36864 + 16, 1, None, 0, None) == 1     # not whole 36 KB tiles
+    assert lib.mla_hbm_read_probe(1, 36864, 2, None, 0, None) == 1          # no such mode
+    assert b"mode" in lib.mla_last_error_message()
+    assert lib.mla_hbm_read_probe(1, 0, 1, None, 0, None) == 0

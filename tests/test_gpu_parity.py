@@ -458,3 +458,23 @@ def test_fused_append_absorb_equals_the_two_calls(base, over):
         assert torch.equal(a.cache_scale, b.cache_scale)
     assert torch.equal(a.out, b.out)
     check_request(a, gen, 0, list(range(w.n_h)), ov.TOL[w.dtype], 2e-2)
+
+
+@pytest.mark.parametrize("nbytes", [36864 * 3, 36864 * 8192 + 16 * 5])
+def test_hbm_read_probe_reads_every_word_once(nbytes):
+    """The register form of the read probe XOR-folds every 32-bit word it
+    loads: folded over the workgroups, it equals the XOR of the buffer
+    (a word read twice or skipped would change it); the copy form runs on
+    whole tiles."""
+    import mla_latent_kv_18_amd as mla
+    rng = np.random.default_rng(nbytes % 1000)
+    words = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(mla.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    mla.hbm_read_probe(buf, 0, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
+    tiles = buf[: (nbytes // 36864) * 36864 // 4]
+    mla.hbm_read_probe(tiles, 1)
+    torch.cuda.synchronize()
