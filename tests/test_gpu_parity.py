@@ -478,3 +478,25 @@ def test_hbm_read_probe_reads_every_word_once(nbytes):
     tiles = buf[: (nbytes // 36864) * 36864 // 4]
     mla.hbm_read_probe(tiles, 1)
     torch.cuda.synchronize()
+
+
+BLOCK_CASES = {   # 128- and 256-token cache blocks, shuffled tables: tiles sit at offsets 0..224 of a block
+    "bf16_h128": ("v3_bs64_ctx4k", dict(batch=3, lens=(1, 300, 1000))),
+    "bf16_h64": ("v3_bs64_ctx4k", dict(n_h=64, batch=2, lens=(130, 700))),
+    "fp8_h128_q2": ("v3_fp8_bs4_ctx128k_q2", dict(batch=2, lens=(130, 700))),
+    "fp4_h128": ("v3_fp4_bs64_ctx4k", dict(batch=2, lens=(97, 700))),
+    "fp8kr_h128": ("v3_fp8kr_bs64_ctx4k", dict(batch=3, lens=(2, 333, 1000))),
+    "fp8kr_h64": ("v3_fp8kr_bs64_ctx4k", dict(n_h=64, batch=2, lens=(65, 500))),
+    "nope_h128": ("nope_bs64_ctx4k", dict(batch=2, lens=(64, 545))),
+}
+
+
+@pytest.mark.parametrize("block_size", [128, 256])
+@pytest.mark.parametrize("split_tokens", [0, 128])
+@pytest.mark.parametrize("case", sorted(BLOCK_CASES))
+def test_larger_cache_blocks(case, split_tokens, block_size):
+    base, over = BLOCK_CASES[case]
+    w = WORKLOADS[base].scaled(name="blocks", seed=23, block_size=block_size, shuffle=True, **over)
+    gen, step = _run(w, split_tokens, "planned")
+    for b in range(w.batch):
+        check_request(step, gen, b, list(range(w.n_h)), ov.TOL[w.dtype], 2e-2)
