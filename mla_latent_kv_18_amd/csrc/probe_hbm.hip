@@ -4,8 +4,9 @@
 // roofline fraction is read against both.  Two plain streaming readers of a
 // buffer, each touching every byte once:
 //   registers  16-byte loads, eight in flight per lane, 2048 workgroups of
-//              256 threads (eight per CU), grid-strided; the words are
-//              XOR-folded into one word per workgroup so no load is dropped
+//              256 threads (eight per CU), each reading one contiguous
+//              range; the words are XOR-folded into one word per workgroup
+//              so no load is dropped
 //   lds copies the decode kernels' structure without their arithmetic: one
 //              workgroup of four waves per CU, 36 KB tiles (nine 1 KB direct
 //              global->LDS copies per wave), three tiles in flight, each
@@ -21,17 +22,20 @@ constexpr int kProbeTile = 36864;
 __global__ void __launch_bounds__(256) hbm_read_regs_kernel(const uint4* __restrict__ buf, int64_t n16,
                                                             uint32_t* __restrict__ sink) {
   __shared__ uint32_t part[4];
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  // workgroup b reads the contiguous 16-byte words [b * per, (b + 1) * per)
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
+  int64_t i = lo + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
     uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = buf[i + u * stride];
+    for (int u = 0; u < 8; ++u) v[u] = buf[i + u * 256];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < hi; i += 256) {
     const uint4 v = buf[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
