@@ -42,12 +42,16 @@ SPIN_CYCLES = 400_000               # GPU-side wait queued before each timed dec
 WORKLOAD = "v3_bs64_ctx4k"
 METRIC = "MLA decode latent-cache GB/s + TFLOP/s, % roofline (V3 shape, bs64, ctx 4k)"
 COUNTERS = os.path.join(ROOT, "profiles", "decode_v3_bs64_ctx4k_counters.json")
-DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_18_amd", "csrc", "decode_mfma.hip")
+# the headline decode's kernel source: the kernel and its generated step streams
+DECODE_SRC = [os.path.join(ROOT, "mla_latent_kv_18_amd", "csrc", f) for f in ("decode_mfma.hip", "decode_bf16_asm.inc")]
 
 
 def decode_source_hash():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
