@@ -11,9 +11,14 @@
 //   FP4-MX   d_c + d_R = 576 E2M1 codes, two per byte (element 2i in the
 //            low nibble), then 18 E8M0 scales (one per 32 elements, value
 //            2^(b - 127)), then 14 bytes of padding: 320 B.
-//   FP8-KR   512 e4m3 latent codes (one fp32 scale per token, in the scale
-//            array beside the pool) and the 64-wide RoPE key in bf16: 640 B.
+//   FP8-KR   512 e4m3 latent codes (one power-of-two scale per token, fp32,
+//            in the scale array beside the pool) and the 64-wide RoPE key in
+//            bf16: 640 B.
 //   NoPE     d_R = 0: 512 bf16 latent values: 1024 B.
+//
+// This kernel serves the shapes the pipelined stream of decode_mfma.hip does
+// not (64-row workgroups: 64 heads, or more than 32 query positions); the
+// 128-row shapes of all three formats go there.
 //
 // Per 32-token tile: the stored rows arrive by direct global->LDS copies
 // into a staging buffer (three slots), are expanded into a bf16 tile
