@@ -152,3 +152,27 @@ def test_unpack_nibbles_order():
     packed = np.array([[0x21, 0x43, 0xF5]], dtype=np.uint8)
     assert codecs.unpack_nibbles(packed, 6).tolist() == [[1, 2, 3, 4, 5, 15]]
     assert codecs.unpack_nibbles(packed, 5).tolist() == [[1, 2, 3, 4, 5]]
+
+
+def test_fp8kr_generator_rows_use_power_of_two_scales():
+    """The input generator's rows for the e4m3-latent cache: the scale is the
+    smallest power of two s with max|latent| / s <= 448, the codes are the
+    e4m3 rounding of latent / s, and the RoPE key is the bf16 rounding."""
+    import numpy as np
+    from mla_latent_kv_18_amd.inputs import to_fp8kr_rows
+    from oracle import codecs
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((50, 576)) * np.exp(rng.uniform(-8, 8, size=(50, 1)))).astype(np.float32)
+    x[3] = 0.0
+    rows, scale = to_fp8kr_rows(x, 512)
+    s = scale.astype(np.float64)
+    assert np.all(np.frexp(s)[0] == 0.5)
+    amax = np.abs(x[:, :512].astype(np.float64)).max(axis=1)
+    nz = amax > 0
+    assert np.all(amax[nz] / s[nz] <= 448.0) and np.all(amax[nz] / s[nz] > 224.0)
+    assert s[3] == 1.0
+    lat = codecs.e4m3_decode(rows[:, :512]) * s[:, None]
+    want = codecs.e4m3_round(x[:, :512].astype(np.float64) / s[:, None]) * s[:, None]
+    assert np.array_equal(lat, want)
+    kr = codecs.bf16_decode(rows[:, 512:].copy().view(np.uint16))
+    assert np.array_equal(kr, codecs.bf16_round(x[:, 512:].astype(np.float64)))

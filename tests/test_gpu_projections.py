@@ -224,6 +224,12 @@ def test_append_rows_cache_variants(n, fmt):
         got = rows[slots64[keep]]
         assert _rel_err(got[:, :D_C], want[keep, :D_C]) <= TOL["fp8"], "e4m3 latent"
         assert _rel_err(got[:, D_C:], want[keep, D_C:]) <= TOL["bf16"], "bf16 rope key"
+        # the row scale is the smallest power of two s with max|latent| / s <= 448
+        sc = scale.cpu().numpy().astype(np.float64)[slots64[keep]]
+        mant, _ = np.frexp(sc)
+        assert np.all(mant == 0.5), "row scale is not a power of two"
+        amax = np.abs(got[:, :D_C]).max(axis=1)
+        assert np.all(amax / sc <= 448.0) and np.all(amax / sc > 448.0 / 2 * 0.99), "row scale is not the smallest"
     untouched = np.setdiff1d(np.arange(rows.shape[0]), slots64[keep])
     assert not np.any(rows[untouched]), "rows outside the slot mapping were written"
 
