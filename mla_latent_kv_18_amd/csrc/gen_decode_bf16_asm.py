@@ -8,9 +8,8 @@ One step of a workgroup (four waves, 128 heads of one query) consumes two
 latent query and turns the scores into softmax numerators, and it adds tile
 k's numerator-weighted value rows into the output accumulators.
 
-  scores   S^T[t, h] = sum_d K[t, d] Q[h, d]: 36 MFMAs (32x32x16 bf16), in two
-           independent chains (query fragments 0-17 and 18-35) that are added
-           at the end, so that consecutive chain MFMAs never wait on each other
+  scores   S^T[t, h] = sum_d K[t, d] Q[h, d]: 36 MFMAs (32x32x16 bf16) in one
+           accumulator chain (dependent MFMAs issue back to back here)
   softmax  p = 2^(S*scale*log2(e) - m_ref) against a per-head reference fixed
            at the first visible tile; the numerators of this wave's 32 heads
            go to LDS as bf16 (the B operand of the weighted sum)
@@ -19,8 +18,8 @@ k's numerator-weighted value rows into the output accumulators.
            head groups), so each transposed value fragment is read once and
            used for four head groups
 
-The MFMA stream is the 36 score MFMAs (chains A and B alternating) with 12
-sum MFMAs spread evenly among them, then the remaining 20 sum MFMAs with the
+The MFMA stream is the 36 score MFMAs with 12 sum MFMAs spread evenly
+among them, then the remaining 20 sum MFMAs with the
 softmax's VALU work placed between them.  LDS reads are
 issued ahead and waited for with lgkmcnt counts computed here from the issue
 order; the nine tile copies of the wave are spread over the first part.
@@ -44,8 +43,8 @@ Operands (named in the kernel):
 The streams use v177-v255, vcc, m0 and scc as scratch.
 
 The same streams serve two more row formats of the latent cache:
-  NoPE  rows of 512 bf16 values (no RoPE part): 32 query fragments in two
-        chains of 16, eight copies per wave, 64 chunks per tile row
+  NoPE  rows of 512 bf16 values (no RoPE part): 32 query fragments, eight
+        copies per wave, 64 chunks per tile row
   FP4   rows of 576 E2M1 codes with an E8M0 scale per 32 values (320 bytes):
         the stored rows are staged in LDS by copies the kernel issues, and
         the step stream expands tile k+2 into the bf16 tile layout between
@@ -69,11 +68,18 @@ CT, CO = 186, 187                     # copy temporaries
 KF = [188, 192, 196]                  # key fragment slots (4 VGPRs each)
 PF = [200, 204, 208, 212]             # P^T fragments, one per head group
 VF = [216, 220]                       # value fragment slots (lo pair, hi pair)
-SA = 224                              # score chain A, then scores / numerators
+SA = 224                              # score accumulator, then scores / numerators
 SB = 240                              # score chain B, then bf16 numerators + temps
 PW = KADDR[0]                         # P^T write address (keys are done by then)
 NEG_INF = "0xff800000"
 WRITE_TAGS = ("pw", "xw")                     # LDS ops that write no register
+
+
+# One accumulator chain for the scores (dependent MFMAs issue back to back on
+# this GPU at no cost), so the softmax needs no chain sum; the softmax scale
+# is applied inside the exponent's fma, after the row maximum of the raw
+# scores (scale > 0, so the maximum commutes with it).
+SINGLE_CHAIN = True
 
 
 class Geo:
@@ -85,7 +91,10 @@ class Geo:
         self.half = self.nk // 2          # fragments per score chain
         self.chunks = d // 8              # 16-byte chunks per tile row
         self.copies = d * 2 * 32 // 1024 // 4   # 1 KB copies per wave and tile
-        self.kseq = [f for i in range(self.half) for f in (i, self.half + i)]
+        if SINGLE_CHAIN:
+            self.kseq = list(range(self.nk))
+        else:
+            self.kseq = [f for i in range(self.half) for f in (i, self.half + i)]
 
 
 G576 = Geo(576)
@@ -187,16 +196,17 @@ class Stream:
 
 
 def softmax_ops(masked):
-    """VALU work turning the two score chains into bf16 numerators in LDS.
+    """VALU work turning the scores into bf16 numerators in LDS.
     Each entry is a list of instructions kept together."""
     a = [SA + r for r in range(16)]
     b = [SB + r for r in range(16)]
     mx, t1, t2, mu, ps, lim, neg = b[8], b[9], b[10], b[11], b[12], b[13], b[14]
     ops = []
-    for r in range(16):
-        ops.append([f"v_add_f32 v{a[r]}, v{a[r]}, v{b[r]}"])
-    for r in range(16):
-        ops.append([f"v_mul_f32 v{a[r]}, %[scale], v{a[r]}"])
+    if not SINGLE_CHAIN:
+        for r in range(16):
+            ops.append([f"v_add_f32 v{a[r]}, v{a[r]}, v{b[r]}"])
+        for r in range(16):
+            ops.append([f"v_mul_f32 v{a[r]}, %[scale], v{a[r]}"])
     if masked:
         # (-inf goes through a VGPR: v_cndmask reads vcc over the constant bus)
         ops.append([f"v_subrev_u32 v{lim}, %[tok], %[vlim]", f"v_mov_b32 v{neg}, {NEG_INF}"])
@@ -216,6 +226,8 @@ def softmax_ops(masked):
     ops.append([f"v_max_f32 v{mx}, v{m[5]}, v{m[6]}"])
     ops.append([f"v_mov_b32 v{t1}, v{mx}", f"v_mov_b32 v{t2}, v{mx}", "s_nop 1",
                 f"v_permlane32_swap_b32 v{t1}, v{t2}", f"v_max_f32 v{mx}, v{t1}, v{t2}"])
+    if SINGLE_CHAIN:
+        ops.append([f"v_mul_f32 v{mx}, %[scale], v{mx}"])
     # running maximum; reference fixed at the first tile with a visible key;
     # largest excess of a tile maximum over the reference
     ops.append([f"v_max_f32 %[mseen], %[mseen], v{mx}"])
@@ -223,7 +235,10 @@ def softmax_ops(masked):
     ops.append([f"v_sub_f32 v{t1}, v{mx}, %[mref]", f"v_max_f32 %[exc], %[exc], v{t1}"])
     ops.append([f"v_cmp_eq_f32 vcc, {NEG_INF}, %[mref]", f"v_cndmask_b32_e64 v{mu}, %[mref], 0, vcc"])
     for r in range(16):
-        ops.append([f"v_sub_f32 v{a[r]}, v{a[r]}, v{mu}", f"v_exp_f32 v{a[r]}, v{a[r]}"])
+        if SINGLE_CHAIN:
+            ops.append([f"v_fma_f32 v{a[r]}, v{a[r]}, %[scale], -v{mu}", f"v_exp_f32 v{a[r]}, v{a[r]}"])
+        else:
+            ops.append([f"v_sub_f32 v{a[r]}, v{a[r]}, v{mu}", f"v_exp_f32 v{a[r]}, v{a[r]}"])
     ops.append([f"v_add_f32 v{ps}, v{a[0]}, v{a[1]}"])
     for r in range(2, 16):
         ops.append([f"v_add_f32 v{ps}, v{ps}, v{a[r]}"])
@@ -254,13 +269,17 @@ def mfma_results_ready(st):
 
 
 def scores(st, kseq, p):
-    """Score MFMA at position p of kseq (chain A takes fragment i, chain B
-    fragment half + i), with the key read KF slots ahead."""
+    """Score MFMA at position p of kseq, with the key read KF slots ahead
+    (two chains, A over fragments 0..half-1 and B over the rest, when
+    SINGLE_CHAIN is off)."""
     f = kseq[p]
     h = st.geo.half
     st.wait_for(("k", f))
-    chain = SA if f < h else SB
-    acc = "0" if f in (0, h) else vr(chain, 16)
+    if SINGLE_CHAIN:
+        chain, acc = SA, ("0" if f == 0 else vr(SA, 16))
+    else:
+        chain = SA if f < h else SB
+        acc = "0" if f in (0, h) else vr(chain, 16)
     st.emit(f"v_mfma_f32_32x32x16_bf16 {vr(chain, 16)}, {vr(KF[p % len(KF)])}, %[q{f}], {acc}")
     if p + len(KF) < len(kseq):
         st.kread(kseq[p + len(KF)], p % len(KF))
